@@ -1,0 +1,455 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+closed form, an invariant, a special case, a library routine (torch's SDPA and
+rms_norm, transformers' LlamaForCausalLM built offline from a config) or a
+brute-force evaluation. They call the oracle through its module so that
+tests/test_oracle_pins.py can plant mistakes into it and check that some pin
+catches each one.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.smol as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _tiny_cfg(**kw):
+    base = dict(hidden=24, n_heads=6, n_kv_heads=2, intermediate=20, n_layers=2, vocab=37, max_pos=64,
+                rms_eps=1e-5, rope_theta=100000.0)
+    base.update(kw)
+    return O.Config(**base)
+
+
+def _rand_layer(cfg, rng, std=0.2, norm_jitter=0.0):
+    H, I, d = cfg.hidden, cfg.intermediate, cfg.head_dim
+    n = lambda *s: rng.standard_normal(s) * std  # noqa: E731
+    nw = lambda: 1.0 + norm_jitter * rng.standard_normal(H)  # noqa: E731
+    return O.LayerWeights(
+        attn_norm=nw(), wq=n(cfg.n_heads * d, H), wk=n(cfg.n_kv_heads * d, H), wv=n(cfg.n_kv_heads * d, H),
+        wo=n(H, cfg.n_heads * d), mlp_norm=nw(), w_gate=n(I, H), w_up=n(I, H), w_down=n(H, I))
+
+
+def _rand_model(cfg, rng, std=0.2, norm_jitter=0.0):
+    return O.ModelWeights(
+        embed=rng.standard_normal((cfg.vocab, cfg.hidden)) * std,
+        layers=[_rand_layer(cfg, rng, std, norm_jitter) for _ in range(cfg.n_layers)],
+        final_norm=1.0 + norm_jitter * rng.standard_normal(cfg.hidden))
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+
+def pin_rmsnorm_closed_forms():
+    """Constant row c*1 -> c / sqrt(c^2 + eps) * w; one-hot s*e_k -> s / sqrt(s^2/H + eps)."""
+    H, eps = 576, 1e-5
+    w = _rng(1).standard_normal(H)
+    for c in (0.0, 1e-3, 0.5, -3.0, 40.0):
+        got = O.rms_norm(np.full((2, H), c), w, eps)
+        want = c / math.sqrt(c * c + eps) * w
+        assert np.allclose(got, want[None], rtol=1e-13, atol=1e-15), c
+    for s in (1e-2, 2.0, -7.5):
+        x = np.zeros(H)
+        x[17] = s
+        got = O.rms_norm(x, np.ones(H), eps)
+        want = np.zeros(H)
+        want[17] = s / math.sqrt(s * s / H + eps)
+        assert np.allclose(got, want, rtol=1e-13, atol=1e-15), s
+
+
+def pin_rmsnorm_vs_torch():
+    """torch.nn.functional.rms_norm (a library routine) in float64."""
+    import torch
+
+    x = _rng(2).standard_normal((5, 96)) * 3
+    w = _rng(3).standard_normal(96)
+    want = torch.nn.functional.rms_norm(torch.from_numpy(x), (96,), torch.from_numpy(w), eps=1e-5).numpy()
+    assert _rel(O.rms_norm(x, w, 1e-5), want) < 1e-13
+
+
+# ------------------------------------------------------------------ RoPE
+
+
+def pin_inv_freq_closed_form():
+    """omega_0 = 1, omega_{d/4} = theta^(-1/2), constant ratio omega_{i+1}/omega_i = theta^(-2/d)."""
+    for d, theta in ((64, 1e5), (128, 1e5), (64, 1e4)):
+        w = O.rope_inv_freq(d, theta)
+        assert w.shape == (d // 2,)
+        assert w[0] == 1.0
+        assert abs(w[d // 4] - 1.0 / math.sqrt(theta)) < 1e-15
+        ratio = w[1:] / w[:-1]
+        assert np.allclose(ratio, theta ** (-2.0 / d), rtol=1e-12)
+    # printed-by-hand values for theta = 1e5, d = 64: omega_1 = 10^(-5/32)
+    w = O.rope_inv_freq(64, 1e5)
+    assert abs(w[1] - 10 ** (-5.0 / 32.0)) < 1e-15
+
+
+def pin_rope_complex_form():
+    """(z_i + i z_{i+d/2}) * exp(i p omega_i) is the same rotation (a distinct formulation)."""
+    d, theta = 64, 1e5
+    z = _rng(4).standard_normal((3, 7, d))
+    pos = np.array([0, 1, 5, 100, 2047, 4096, 8191])
+    got = O.rope_rotate(z, pos, theta)
+    zc = z[..., : d // 2] + 1j * z[..., d // 2:]
+    omega = theta ** (-np.arange(d // 2) * 2.0 / d)
+    rc = zc * np.exp(1j * pos[:, None] * omega[None, :])
+    want = np.concatenate([rc.real, rc.imag], axis=-1)
+    assert _rel(got, want) < 1e-12
+
+
+def pin_rope_invariants():
+    """Norm preservation, R_0 = I, <R_m q, R_n k> = <R_{m-n} q, k>, and the pairing e_0 -> e_{d/2}."""
+    d, theta = 64, 1e5
+    rng = _rng(5)
+    z = rng.standard_normal((9, d))
+    pos = np.array([0, 3, 17, 255, 256, 1000, 4095, 8190, 8191])
+    r = O.rope_rotate(z, pos, theta)
+    assert np.allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(z, axis=-1), rtol=1e-13)
+    assert np.array_equal(O.rope_rotate(z, np.zeros(9, int), theta), z)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n in ((5, 2), (8191, 0), (8191, 8000), (300, 299), (7, 7)):
+        lhs = O.rope_rotate(q[None], [m], theta)[0] @ O.rope_rotate(k[None], [n], theta)[0]
+        rhs = O.rope_rotate(q[None], [m - n], theta)[0] @ k
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(rhs)), (m, n)
+    e0 = np.zeros(d)
+    e0[0] = 1.0
+    p = 3
+    r0 = O.rope_rotate(e0[None], [p], theta)[0]
+    want = np.zeros(d)
+    want[0], want[d // 2] = math.cos(p), math.sin(p)
+    assert np.allclose(r0, want, atol=1e-15)
+
+
+# ------------------------------------------------------------------ attention
+
+
+def pin_attention_vs_sdpa():
+    """GQA with kv head h // group equals torch SDPA on repeat_interleave-expanded K/V (float64)."""
+    import torch
+
+    rng = _rng(6)
+    B, nq, nkv, T, d = 2, 9, 3, 23, 16
+    q = rng.standard_normal((B, nq, T, d))
+    k = rng.standard_normal((B, nkv, T, d))
+    v = rng.standard_normal((B, nkv, T, d))
+    got = O.gqa_attention(q, k, v, np.arange(T), np.arange(T))
+    kt = torch.from_numpy(k).repeat_interleave(nq // nkv, dim=1)
+    vt = torch.from_numpy(v).repeat_interleave(nq // nkv, dim=1)
+    want = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kt, vt, is_causal=True).numpy()
+    assert _rel(got, want) < 1e-12
+
+
+def pin_attention_special_cases():
+    """Position 0 returns v_0 exactly; equal keys give the running mean of the visible v;
+    a single query at position P over keys 0..P is an unmasked softmax."""
+    rng = _rng(7)
+    B, nq, nkv, T, d = 1, 6, 2, 11, 8
+    q = rng.standard_normal((B, nq, T, d))
+    k = rng.standard_normal((B, nkv, T, d))
+    v = rng.standard_normal((B, nkv, T, d))
+    o = O.gqa_attention(q, k, v, np.arange(T), np.arange(T))
+    for h in range(nq):
+        assert np.array_equal(o[0, h, 0], v[0, h // 3, 0])
+    keq = np.broadcast_to(k[:, :, :1], k.shape)
+    o2 = O.gqa_attention(q, keq, v, np.arange(T), np.arange(T))
+    run_mean = np.cumsum(v, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    for h in range(nq):
+        assert np.allclose(o2[0, h], run_mean[0, h // 3], rtol=1e-12, atol=1e-14)
+    P = T - 1
+    o3 = O.gqa_attention(q[:, :, P:], k, v, np.array([P]), np.arange(T))
+    for h in range(nq):
+        s = k[0, h // 3] @ q[0, h, P] / math.sqrt(d)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        assert np.allclose(o3[0, h, 0], p @ v[0, h // 3], rtol=1e-12)
+
+
+def pin_causality():
+    """Perturbing tokens after t leaves the logits at positions <= t bit-identical."""
+    cfg = _tiny_cfg()
+    rng = _rng(8)
+    mw = _rand_model(cfg, rng)
+    ids = rng.integers(0, cfg.vocab, size=(2, 13))
+    base = O.model_prefill(ids, mw, cfg)
+    t = 6
+    ids2 = ids.copy()
+    ids2[:, t + 1:] = (ids2[:, t + 1:] + 5) % cfg.vocab
+    pert = O.model_prefill(ids2, mw, cfg)
+    assert np.array_equal(base[:, : t + 1], pert[:, : t + 1])
+    assert not np.allclose(base[:, t + 1:], pert[:, t + 1:])
+
+
+# ------------------------------------------------------------------ MLP
+
+
+def pin_silu_values():
+    """silu(0) = 0, silu(1) = 1/(1+e^-1), silu(-1) = -1/(1+e); silu(z) -> z for large z."""
+    got = O.silu(np.array([0.0, 1.0, -1.0, 40.0, -40.0]))
+    assert got[0] == 0.0
+    assert abs(got[1] - 0.7310585786300049) < 1e-15
+    assert abs(got[2] + 0.2689414213699951) < 1e-15
+    assert abs(got[3] - 40.0) < 1e-12 and abs(got[4]) < 1e-15
+
+
+def pin_swiglu_special_case():
+    """With one-hot gate/up rows the MLP reduces to scalars: down[:, j] * silu(u_a) * u_b."""
+    H, I = 8, 3
+    u = _rng(9).standard_normal((4, H))
+    wg = np.zeros((I, H))
+    wu = np.zeros((I, H))
+    wg[1, 2] = 1.0
+    wu[1, 5] = 1.0
+    wd = _rng(10).standard_normal((H, I))
+    got = O.swiglu_mlp(u, wg, wu, wd)
+    want = np.outer(u[:, 2] / (1 + np.exp(-u[:, 2])) * u[:, 5], wd[:, 1])
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------ whole model
+
+
+def _hf_model(cfg, mw):
+    """transformers' LlamaForCausalLM from an in-memory config with our weights, float64, eager attention."""
+    import torch
+    from transformers import LlamaConfig, LlamaForCausalLM
+
+    hc = LlamaConfig(vocab_size=cfg.vocab, hidden_size=cfg.hidden, intermediate_size=cfg.intermediate,
+                     num_hidden_layers=cfg.n_layers, num_attention_heads=cfg.n_heads,
+                     num_key_value_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, rms_norm_eps=cfg.rms_eps,
+                     rope_theta=cfg.rope_theta, max_position_embeddings=cfg.max_pos, tie_word_embeddings=True,
+                     attention_bias=False, mlp_bias=False, hidden_act="silu")
+    hc._attn_implementation = "eager"
+    torch.manual_seed(0)
+    m = LlamaForCausalLM(hc).double().eval()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float64))  # noqa: E731
+    with torch.no_grad():
+        m.model.embed_tokens.weight.copy_(t(mw.embed))
+        m.model.norm.weight.copy_(t(mw.final_norm))
+        for lw, L in zip(mw.layers, m.model.layers):
+            L.input_layernorm.weight.copy_(t(lw.attn_norm))
+            L.post_attention_layernorm.weight.copy_(t(lw.mlp_norm))
+            L.self_attn.q_proj.weight.copy_(t(lw.wq))
+            L.self_attn.k_proj.weight.copy_(t(lw.wk))
+            L.self_attn.v_proj.weight.copy_(t(lw.wv))
+            L.self_attn.o_proj.weight.copy_(t(lw.wo))
+            L.mlp.gate_proj.weight.copy_(t(lw.w_gate))
+            L.mlp.up_proj.weight.copy_(t(lw.w_up))
+            L.mlp.down_proj.weight.copy_(t(lw.w_down))
+    assert m.lm_head.weight.data_ptr() == m.model.embed_tokens.weight.data_ptr()
+    inv = m.model.rotary_emb.inv_freq.double().numpy()
+    assert np.allclose(inv, cfg.rope_theta ** (-np.arange(cfg.head_dim // 2) * 2.0 / cfg.head_dim), rtol=1e-6)
+    return m
+
+
+def pin_model_vs_transformers():
+    """Logits of the oracle equal transformers' Llama on the same weights (rotate_half RoPE,
+    GQA by repeat, causal mask, pre-norm residuals, tied head). transformers builds the RoPE
+    angles in float32, so agreement is to ~1e-6 relative, far below any structural mistake."""
+    import torch
+
+    cfg = _tiny_cfg(hidden=48, n_heads=6, n_kv_heads=2, intermediate=40, n_layers=2, vocab=53)
+    rng = _rng(11)
+    mw = _rand_model(cfg, rng, std=0.3, norm_jitter=0.2)
+    ids = rng.integers(0, cfg.vocab, size=(2, 29))
+    want = _hf_model(cfg, mw)(torch.from_numpy(ids)).logits.detach().numpy()
+    got = O.model_prefill(ids, mw, cfg)
+    assert got.shape == want.shape
+    assert _rel(got, want) < 2e-6, _rel(got, want)
+
+
+def pin_block_vs_transformers_smollm2_shape():
+    """One SmolLM2-135M-shaped block (H 576, 9/3 heads, d 64, I 1536) at seq 128 equals
+    transformers' decoder layer (taken as the model minus embedding and head)."""
+    import torch
+
+    cfg = O.Config(n_layers=1, vocab=64)
+    rng = _rng(12)
+    lw = _rand_layer(cfg, rng, std=1.0 / 24.0, norm_jitter=0.1)
+    mw = O.ModelWeights(embed=rng.standard_normal((cfg.vocab, cfg.hidden)), layers=[lw],
+                        final_norm=np.ones(cfg.hidden))
+    m = _hf_model(cfg, mw)
+    x = rng.standard_normal((1, 128, cfg.hidden))
+    pos = torch.arange(128)[None]
+    xt = torch.from_numpy(x)
+    cos_sin = m.model.rotary_emb(xt, pos)
+    mask = torch.full((128, 128), -torch.inf, dtype=torch.float64).triu(1)[None, None]
+    out = m.model.layers[0](xt, attention_mask=mask, position_ids=pos, position_embeddings=cos_sin)
+    want = (out[0] if isinstance(out, tuple) else out).detach().numpy()
+    got = O.block_forward(x, lw, cfg)
+    assert _rel(got, want) < 2e-6, _rel(got, want)
+
+
+def pin_param_count():
+    """134,515,008 parameters for the SmolLM2-135M shape with tied embeddings, as printed
+    in abi96062 model.py; the fixture also carries the config the count is for."""
+    with open(os.path.join(GOLDEN, "smollm2_135m.json")) as f:
+        g = json.load(f)
+    cfg = O.Config(hidden=g["hidden_size"], n_heads=g["num_attention_heads"], n_kv_heads=g["num_key_value_heads"],
+                   intermediate=g["intermediate_size"], n_layers=g["num_hidden_layers"], vocab=g["vocab_size"],
+                   max_pos=g["max_position_embeddings"], rms_eps=g["rms_norm_eps"], rope_theta=g["rope_theta"])
+    assert cfg.head_dim == g["head_dim"]
+    assert O.param_count(cfg, tied=True) == g["param_count"]
+    assert O.param_count(cfg, tied=False) == g["param_count"] + g["vocab_size"] * g["hidden_size"]
+
+
+def pin_logits_shape():
+    """Input (1, 10) gives logits (1, 10, vocab) (abi96062 model.py __main__), here on a narrow model."""
+    with open(os.path.join(GOLDEN, "smollm2_135m.json")) as f:
+        g = json.load(f)
+    cfg = _tiny_cfg(vocab=g["vocab_size"], n_layers=1)
+    rng = _rng(13)
+    mw = _rand_model(cfg, rng)
+    ids = rng.integers(0, cfg.vocab, size=tuple(g["example_input_shape"]))
+    out = O.model_prefill(ids, mw, cfg)
+    assert list(out.shape) == g["example_logits_shape"][:2] + [cfg.vocab]
+    assert cfg.vocab == g["example_logits_shape"][2]
+
+
+def pin_gqa_mapping_smollm3():
+    """The SmolLM3 page's mapping (query head h reads kv head h // 4) holds for 16/4 heads:
+    editing kv head j changes exactly query heads 4j .. 4j+3."""
+    with open(os.path.join(GOLDEN, "smollm3_3b_shape.json")) as f:
+        g = json.load(f)
+    nq, nkv = g["num_attention_heads"], g["num_key_value_heads"]
+    rng = _rng(14)
+    T, d = 5, 8
+    q = rng.standard_normal((1, nq, T, d))
+    k = rng.standard_normal((1, nkv, T, d))
+    v = rng.standard_normal((1, nkv, T, d))
+    base = O.gqa_attention(q, k, v, np.arange(T), np.arange(T))
+    for j in range(nkv):
+        v2 = v.copy()
+        v2[0, j] += 1.0
+        out = O.gqa_attention(q, k, v2, np.arange(T), np.arange(T))
+        changed = [h for h in range(nq) if not np.array_equal(out[0, h], base[0, h])]
+        assert changed == [h for h in range(nq) if g["gqa_head_to_kv"][h] == j]
+
+
+def pin_decode_equals_prefill():
+    """Decode at position P over a cache from prefill(ids[:P]) equals prefill(ids[:P+1]) at P."""
+    cfg = _tiny_cfg()
+    rng = _rng(15)
+    mw = _rand_model(cfg, rng)
+    B, P = 3, 9
+    ids = rng.integers(0, cfg.vocab, size=(B, P + 1))
+    full = O.model_prefill(ids, mw, cfg)
+    _, cache = O.model_prefill(ids[:, :P], mw, cfg, keep_cache=True)
+    kc = [c[0] for c in cache]
+    vc = [c[1] for c in cache]
+    logits, nk, nv = O.decode_step(ids[:, P], P, mw, cfg, kc, vc)
+    assert _rel(logits, full[:, P]) < 1e-12
+    _, cache_full = O.model_prefill(ids, mw, cfg, keep_cache=True)
+    for li in range(cfg.n_layers):
+        assert np.allclose(nk[li], cache_full[li][0][:, :, P], rtol=1e-12)
+        assert np.allclose(nv[li], cache_full[li][1][:, :, P], rtol=1e-12)
+
+
+def _brute_force_logits(cfg, mw, ids):
+    """Scalar pure-Python evaluation of the whole forward (for tiny sizes only)."""
+    H, d, nq, nkv = cfg.hidden, cfg.head_dim, cfg.n_heads, cfg.n_kv_heads
+    G = nq // nkv
+    B, T = len(ids), len(ids[0])
+
+    def norm(row, w):
+        ms = sum(v * v for v in row) / H
+        r = 1.0 / math.sqrt(ms + cfg.rms_eps)
+        return [w[i] * row[i] * r for i in range(H)]
+
+    def lin(row, W):
+        return [sum(W[o][i] * row[i] for i in range(len(row))) for o in range(len(W))]
+
+    def rot(vec, p):
+        out = list(vec)
+        for i in range(d // 2):
+            a = p * cfg.rope_theta ** (-2.0 * i / d)
+            c, s = math.cos(a), math.sin(a)
+            out[i] = vec[i] * c - vec[i + d // 2] * s
+            out[i + d // 2] = vec[i + d // 2] * c + vec[i] * s
+        return out
+
+    E = mw.embed.tolist()
+    logits = []
+    for b in range(B):
+        xs = [list(E[ids[b][t]]) for t in range(T)]
+        for lw in mw.layers:
+            W = {n: getattr(lw, n).tolist() for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")}
+            us = [norm(x, lw.attn_norm.tolist()) for x in xs]
+            qs = [lin(u, W["wq"]) for u in us]
+            ks = [lin(u, W["wk"]) for u in us]
+            vs = [lin(u, W["wv"]) for u in us]
+            for t in range(T):
+                att = [0.0] * (nq * d)
+                for h in range(nq):
+                    g = h // G
+                    qh = rot(qs[t][h * d:(h + 1) * d], t)
+                    sc = []
+                    for j in range(t + 1):
+                        kj = rot(ks[j][g * d:(g + 1) * d], j)
+                        sc.append(sum(qh[e] * kj[e] for e in range(d)) / math.sqrt(d))
+                    mx = max(sc)
+                    ex = [math.exp(s - mx) for s in sc]
+                    z = sum(ex)
+                    for e in range(d):
+                        att[h * d + e] = sum(ex[j] / z * vs[j][g * d + e] for j in range(t + 1))
+                xs[t] = [xs[t][i] + o for i, o in enumerate(lin(att, W["wo"]))]
+            for t in range(T):
+                w = norm(xs[t], lw.mlp_norm.tolist())
+                gt = lin(w, W["w_gate"])
+                up = lin(w, W["w_up"])
+                y = [gt[i] / (1.0 + math.exp(-gt[i])) * up[i] for i in range(len(gt))]
+                xs[t] = [xs[t][i] + o for i, o in enumerate(lin(y, W["w_down"]))]
+        for t in range(T):
+            z = norm(xs[t], mw.final_norm.tolist())
+            logits.append([sum(E[v][i] * z[i] for i in range(H)) for v in range(cfg.vocab)])
+    return np.array(logits).reshape(B, T, cfg.vocab)
+
+
+def pin_brute_force_tiny():
+    """numpy oracle vs a scalar pure-Python evaluation: H 12, 3 q heads / 1 kv head, d 4,
+    I 8, 2 layers, vocab 16, T 5."""
+    cfg = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=2, vocab=16, max_pos=32,
+                   rms_eps=1e-5, rope_theta=1e5)
+    rng = _rng(16)
+    mw = _rand_model(cfg, rng, std=0.5, norm_jitter=0.3)
+    ids = rng.integers(0, cfg.vocab, size=(2, 5))
+    want = _brute_force_logits(cfg, mw, ids.tolist())
+    got = O.model_prefill(ids, mw, cfg)
+    assert _rel(got, want) < 1e-12
+
+
+ALL_PINS = [
+    pin_rmsnorm_closed_forms,
+    pin_rmsnorm_vs_torch,
+    pin_inv_freq_closed_form,
+    pin_rope_complex_form,
+    pin_rope_invariants,
+    pin_attention_vs_sdpa,
+    pin_attention_special_cases,
+    pin_causality,
+    pin_silu_values,
+    pin_swiglu_special_case,
+    pin_model_vs_transformers,
+    pin_block_vs_transformers_smollm2_shape,
+    pin_param_count,
+    pin_logits_shape,
+    pin_gqa_mapping_smollm3,
+    pin_decode_equals_prefill,
+    pin_brute_force_tiny,
+]

@@ -1,0 +1,171 @@
+"""The CPU oracle against its pins, and planted mistakes that the pins must catch."""
+
+import numpy as np
+import pytest
+
+import oracle.smol as O
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", P.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------- planted mistakes
+# Each entry replaces one oracle function with a plausibly wrong variant; at least one
+# pin must fail on it. The mistakes are planted in the oracle, on the CPU.
+
+F64 = np.float64
+
+
+def _rms_eps_outside(x, w, eps):
+    x = np.asarray(x, F64)
+    return np.asarray(w, F64) * x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)
+
+
+def _rms_sum_not_mean(x, w, eps):
+    x = np.asarray(x, F64)
+    return np.asarray(w, F64) * x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _rms_weight_dropped(x, w, eps):
+    x = np.asarray(x, F64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _inv_freq_half_exponent(d, theta):
+    return float(theta) ** (-np.arange(d // 2, dtype=F64) / d)
+
+
+def _rope_interleaved(z, positions, theta):
+    z = np.asarray(z, F64)
+    d = z.shape[-1]
+    ang = np.asarray(positions, F64)[..., None] * O.rope_inv_freq(d, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = z[..., 0::2], z[..., 1::2]
+    out = np.empty_like(z)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = b * c + a * s
+    return out
+
+
+def _rope_sign_flipped(z, positions, theta):
+    z = np.asarray(z, F64)
+    d = z.shape[-1]
+    ang = np.asarray(positions, F64)[..., None] * O.rope_inv_freq(d, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = z[..., : d // 2], z[..., d // 2:]
+    return np.concatenate([a * c + b * s, b * c - a * s], axis=-1)
+
+
+def _make_attention(mapping="div", scale="sqrt", strict=False):
+    def attn(q, k, v, q_pos, k_pos):
+        q, k, v = (np.asarray(a, F64) for a in (q, k, v))
+        B, nq, T, d = q.shape
+        nkv = k.shape[1]
+        G = nq // nkv
+        qp, kp = np.asarray(q_pos), np.asarray(k_pos)
+        vis = (kp[None, :] < qp[:, None]) if strict else (kp[None, :] <= qp[:, None])
+        sc = 1.0 / np.sqrt(d) if scale == "sqrt" else 1.0 / d
+        out = np.empty((B, nq, T, d))
+        for b in range(B):
+            for h in range(nq):
+                g = h // G if mapping == "div" else h % nkv
+                s = np.where(vis, (q[b, h] @ k[b, g].T) * sc, -np.inf)
+                out[b, h] = O.softmax(s) @ v[b, g]
+        return out
+    return attn
+
+
+def _swiglu_swapped(u, wg, wu, wd):
+    g = u @ np.asarray(wg, F64).T
+    up = u @ np.asarray(wu, F64).T
+    return (O.silu(up) * g) @ np.asarray(wd, F64).T
+
+
+def _silu_sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, F64)))
+
+
+def _block_no_mlp_residual(x, lw, cfg, pos0=0, return_parts=False):
+    x = np.asarray(x, F64)
+    positions = np.arange(pos0, pos0 + x.shape[1])
+    attn, k, v = O.attention_sublayer(x, lw, cfg, positions)
+    h = x + attn
+    mlp = O.mlp_sublayer(h, lw, cfg)
+    out = mlp + attn  # the first residual's x is dropped
+    if return_parts:
+        return out, {"attn": attn, "mlp": mlp, "k": k, "v": v}
+    return out
+
+
+def _mlp_reads_stream_not_norm(h, lw, cfg):
+    return O.swiglu_mlp(np.asarray(h, F64), lw.w_gate, lw.w_up, lw.w_down)
+
+
+_orig_attention_sublayer = O.attention_sublayer
+
+
+def _attention_rotates_v(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None):
+    out, k, v = _orig_attention_sublayer(x, lw, cfg, positions, past_k, past_v, past_pos)
+    vr = O.rope_rotate(v, np.asarray(positions), cfg.rope_theta)
+    # recompute the output with rotated values
+    B, T, H = np.asarray(x).shape
+    d = cfg.head_dim
+    u = O.rms_norm(x, lw.attn_norm, cfg.rms_eps)
+    q = (u @ np.asarray(lw.wq, F64).T).reshape(B, T, cfg.n_heads, d).transpose(0, 2, 1, 3)
+    q = O.rope_rotate(q, np.asarray(positions), cfg.rope_theta)
+    if past_k is not None:
+        k_all = np.concatenate([past_k, k], 2)
+        v_all = np.concatenate([past_v, vr], 2)
+        kp = np.concatenate([past_pos, positions])
+    else:
+        k_all, v_all, kp = k, vr, positions
+    o = O.gqa_attention(q, k_all, v_all, positions, kp).transpose(0, 2, 1, 3).reshape(B, T, -1)
+    return o @ np.asarray(lw.wo, F64).T, k, vr
+
+
+def _attention_wo_transposed(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None):
+    import copy
+    lw2 = copy.copy(lw)
+    lw2.wo = np.asarray(lw.wo).T
+    return _orig_attention_sublayer(x, lw2, cfg, positions, past_k, past_v, past_pos)
+
+
+def _lm_head_no_final_norm(x, final_norm, E, cfg):
+    return np.asarray(x, F64) @ np.asarray(E, F64).T
+
+
+MISTAKES = {
+    "rmsnorm eps outside the root": ("rms_norm", _rms_eps_outside),
+    "rmsnorm sum instead of mean": ("rms_norm", _rms_sum_not_mean),
+    "rmsnorm weight dropped": ("rms_norm", _rms_weight_dropped),
+    "inv_freq exponent halved": ("rope_inv_freq", _inv_freq_half_exponent),
+    "rope interleaved pairs": ("rope_rotate", _rope_interleaved),
+    "rope sign flipped": ("rope_rotate", _rope_sign_flipped),
+    "gqa head h % n_kv": ("gqa_attention", _make_attention(mapping="mod")),
+    "attention scale 1/d": ("gqa_attention", _make_attention(scale="d")),
+    "causal mask excludes the diagonal": ("gqa_attention", _make_attention(strict=True)),
+    "swiglu gate and up swapped": ("swiglu_mlp", _swiglu_swapped),
+    "silu is the sigmoid": ("silu", _silu_sigmoid),
+    "block drops the residual x": ("block_forward", _block_no_mlp_residual),
+    "mlp reads the stream, not its norm": ("mlp_sublayer", _mlp_reads_stream_not_norm),
+    "rope applied to v": ("attention_sublayer", _attention_rotates_v),
+    "o_proj transposed": ("attention_sublayer", _attention_wo_transposed),
+    "final norm dropped": ("lm_head", _lm_head_no_final_norm),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MISTAKES))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, bad = MISTAKES[name]
+    monkeypatch.setattr(O, attr, bad)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught: {name}"
