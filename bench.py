@@ -1,0 +1,280 @@
+"""Benchmark: SmolLM2-135M-shaped prefill (bf16, 30 layers, batch 4 x seq 512) on one
+MI355X through the C ABI, plus the decode step (batch 64 over 2047 cached positions).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-graph] [--no-cpu]
+                    [--profile-kernel NAME]
+
+A step is one smol_model_prefill call: embedding, 30 blocks (RMSNorm, QKV+RoPE,
+causal GQA attention, o_proj+residual, RMSNorm, gate/up+SwiGLU, down+residual),
+final RMSNorm and the tied lm_head writing bf16 logits [4, 512, 49152]. Inputs and
+weights are resident in HBM before the timed region. By default the step is
+captured once into a HIP graph and replayed (every kernel still runs each step);
+--no-graph times plain launches. Rank 0 prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+
+
+def prefill_flops(s) -> dict:
+    """Algorithmic FLOPs of one prefill (causal attention counts the visible triangle only)."""
+    M, L, H, d = s.batch * s.seq, s.n_layers, s.hidden, s.head_dim
+    per_layer = {
+        "qkv_rope": 2 * M * H * (s.n_heads + 2 * s.n_kv_heads) * d,
+        "o_proj": 2 * M * s.n_heads * d * H,
+        "gate_up": 2 * M * H * 2 * s.intermediate,
+        "down": 2 * M * s.intermediate * H,
+        "attention": 2 * d * s.n_heads * s.seq * (s.seq + 1) * s.batch,
+    }
+    out = {k: v * L for k, v in per_layer.items()}
+    out["lm_head"] = 2 * M * H * s.vocab
+    out["per_launch"] = dict(per_layer, lm_head=out["lm_head"])
+    out["total"] = sum(v for k, v in out.items() if k not in ("per_launch",))
+    return out
+
+
+def decode_bytes(s, P: int) -> dict:
+    """Algorithmic HBM bytes of one decode step (bf16): every cached key/value read once,
+    every weight read once, the new k/v written, logits written."""
+    L, B, H, d, I, V = s.n_layers, s.batch, s.hidden, s.head_dim, s.intermediate, s.vocab
+    layer_w = 2 * (H * (s.n_heads + 2 * s.n_kv_heads) * d + s.n_heads * d * H + 3 * H * I + 2 * H)
+    kv_read = 2 * 2 * s.n_kv_heads * d * (P + 1) * B  # per layer: keys 0..P incl. the new one
+    out = {
+        "kv_read": kv_read * L,
+        "weights": layer_w * L + 2 * V * H + 2 * H,
+        "kv_append": 2 * 2 * s.n_kv_heads * d * B * L,
+        "logits": 2 * B * V,
+        "decode_attention_per_launch": kv_read,
+    }
+    out["total"] = out["kv_read"] + out["weights"] + out["kv_append"] + out["logits"]
+    return out
+
+
+def _time_steps(fn, steps, torch):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
+    """Average duration (ms) of one kernel class over one eager step, from HIP events the
+    library records around each of its launches on the launch stream."""
+    torch.cuda.synchronize()
+    B.smol_timing_begin(kernel, max_launches)
+    run_once()
+    ms, n = B.smol_timing_end()
+    return ms, n
+
+
+def cpu_baseline(s, model, ids_np, budget_s=12.0):
+    """The CPU oracle (numpy float64, as it stands) on whole sequences of the same prefill,
+    one after another until about budget_s seconds have passed."""
+    import oracle.smol as O
+    from threadpoolctl import threadpool_info
+
+    cfg = O.Config(hidden=s.hidden, n_heads=s.n_heads, n_kv_heads=s.n_kv_heads, intermediate=s.intermediate,
+                   n_layers=s.n_layers, vocab=s.vocab, max_pos=s.max_pos, rms_eps=s.rms_eps, rope_theta=s.rope_theta)
+    om = O.ModelWeights(embed=model.embed.f64,
+                        layers=[O.LayerWeights(**{n: getattr(l, n).f64 for n in l.NAMES}) for l in model.layers],
+                        final_norm=model.final_norm.f64)
+    t0 = time.perf_counter()
+    done = 0
+    while done < ids_np.shape[0]:
+        O.model_prefill(ids_np[done:done + 1], om, cfg)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": done * s.seq / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {ids_np.shape[0]} sequences x {s.seq} tokens, full 30-layer forward and all "
+                      f"logits, numpy float64, {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the whole forward on a single MI355X "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from llama_decoder_only_amd import binding as B
+    from llama_decoder_only_amd import synthetic as S
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+
+    s = S.workload("prefill_bf16")
+    cfg = B.Config.from_shape(s)
+    model = S.model_weights(s, 0)
+    md = B.upload_model(model, dev)
+    ids_np = S.token_ids(s, 0)
+    ids = torch.from_numpy(ids_np).to(dev)
+    logits = torch.empty(s.batch, s.seq, s.vocab, dtype=torch.bfloat16, device=dev)
+    ws = B.workspace(cfg, B.SMOL_OP_PREFILL, s.batch, s.seq, dev)
+    stream = torch.cuda.Stream()
+
+    def step():
+        B.smol_model_prefill(cfg, md, ids, logits, ws=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step()
+    torch.cuda.synchronize()
+    eager_ref = logits.clone()
+
+    eager_s = _time_steps(lambda: step(), args.steps, torch)
+    graph_s = None
+    mode = "eager"
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        for _ in range(3):  # every replay reproduces the eager result
+            logits.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(logits, eager_ref):
+                raise RuntimeError("graph replay differs from the eager result")
+        graph_s = _time_steps(lambda: g.replay(), args.steps, torch)
+        mode = "hip_graph"
+    step_s = graph_s if graph_s is not None else eager_s
+
+    flops = prefill_flops(s)
+    tokens = s.batch * s.seq
+    value = tokens / step_s
+
+    # per-kernel-class durations from HIP events (eager step on the same stream)
+    kern = {}
+    with torch.cuda.stream(stream):
+        for name in ("qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head", "rmsnorm", "embed"):
+            ms, n = _kernel_time(B, name, step, torch)
+            kern[name] = {"total_ms": ms, "launches": n, "avg_us": 1e3 * ms / max(n, 1)}
+    dominant = max((k for k in kern if k in flops["per_launch"]), key=lambda k: kern[k]["total_ms"])
+    avg_s = kern[dominant]["avg_us"] * 1e-6
+    ach = flops["per_launch"][dominant] / avg_s / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flop_per_launch": flops["per_launch"][dominant],
+                "avg_launch_us": round(kern[dominant]["avg_us"], 2)}
+
+    out = {
+        "metric": "prefill tokens/s (SmolLM2-135M fwd, bf16, 1 GPU) + % MFMA peak; decode HBM GB/s",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0, (1/24)^2) weights, unit RMSNorm weights, uniform token ids",
+        "config": {"workload": "SmolLM2-135M-shaped prefill: 30 layers, hidden 576, 9/3 heads x 64, "
+                               "intermediate 1536, vocab 49152 tied head; batch 4 x seq 512, bf16 logits",
+                   "global_batch": s.batch, "seq_len": s.seq, "parallelism": "single GPU", "timing": mode},
+        "mfma_frac": round(flops["total"] / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "algorithmic_gflop_per_step": round(flops["total"] / 1e9, 2),
+        "eager_ms_per_step": round(eager_s * 1e3, 4),
+        "roofline": roofline,
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+    }
+
+    if not args.no_decode:
+        sd = S.workload("decode_bf16")
+        P, cap = sd.cache_len, sd.cache_len + 1
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        kc = torch.randn(sd.n_layers, sd.batch, sd.n_kv_heads, cap, sd.head_dim, generator=gen, device=dev,
+                         dtype=torch.float32).to(torch.bfloat16)
+        vc = torch.randn(kc.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        dids = torch.from_numpy(S.token_ids(sd, 0, S.T_DECODE_IDS)[:, 0].copy()).to(dev)
+        cl = torch.full((sd.batch,), P, dtype=torch.int32, device=dev)
+        dlog = torch.empty(sd.batch, sd.vocab, dtype=torch.bfloat16, device=dev)
+        dws = B.workspace(cfg, B.SMOL_OP_DECODE, sd.batch, cap, dev)
+
+        def dstep():
+            B.smol_decode_step(cfg, md, dids, cl, kc, vc, dlog, ws=dws, stream=stream)
+
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dstep()
+        torch.cuda.synchronize()
+        dref = dlog.clone()
+        dmode = "eager"
+        dfn = dstep
+        if not args.no_graph:
+            dg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(dg, stream=stream):
+                dstep()
+            for _ in range(3):
+                dlog.zero_()
+                dg.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(dlog, dref):
+                    raise RuntimeError("decode graph replay differs from the eager result")
+            dfn = dg.replay
+            dmode = "hip_graph"
+        d_s = _time_steps(dfn, args.decode_steps, torch)
+        db = decode_bytes(sd, P)
+        with torch.cuda.stream(stream):
+            ms, n = _kernel_time(B, "decode_attention", dstep, torch)
+        att_s = ms / max(n, 1) * 1e-3
+        att_gbps = db["decode_attention_per_launch"] / att_s / 1e9
+        out["decode"] = {
+            "workload": "decode step: batch 64, 2047 cached positions (+1 new), 30 layers, bf16",
+            "timing": dmode,
+            "ms_per_step": round(d_s * 1e3, 4),
+            "tokens_per_s": round(sd.batch / d_s, 1),
+            "algorithmic_gb_per_step": round(db["total"] / 1e9, 4),
+            "hbm_gbps": round(db["total"] / d_s / 1e9, 1),
+            "hbm_frac": round(db["total"] / d_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "roofline": {"bound": "hbm", "kernel": "decode_attention", "achieved": round(att_gbps, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": None, "algorithmic_bytes_per_launch": db["decode_attention_per_launch"],
+                         "avg_launch_us": round(att_s * 1e6, 2)},
+        }
+        del kc, vc
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(s, model, ids_np)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

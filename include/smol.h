@@ -1,0 +1,152 @@
+/*
+ * smol.h -- C ABI of libsmol: the forward pass of a LLaMA-style pre-norm decoder
+ * stack (SmolLM2-135M shape and relatives) on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are the pages on SmolLM2-135M / SmolLM3):
+ *   embedding gather   -> abi96062 model.py, SmolLM2Model.forward
+ *   per block          -> h = x + attn(RMSNorm_a(x)); out = h + mlp(RMSNorm_m(h))
+ *                         (nnterp "SmolLM3", "The block, in order"; tohio block.py)
+ *   RMSNorm            -> w * x / sqrt(mean(x^2) + eps) (abi96062 components.py, RMSNorm)
+ *   RoPE               -> pairs (i, i + d/2) rotated by p * theta^(-2i/d), on q and k only
+ *                         (Sualeh77 model.py, "3. RoPE"; rope_interleaved false in "1. Config")
+ *   attention          -> causal softmax(q k^T / sqrt(d)) v, query head h reads kv head
+ *                         h / (n_heads / n_kv_heads) (Sualeh77 model.py, "4. Attention";
+ *                         abi96062 components.py, GroupedQueryAttention)
+ *   MLP                -> down(silu(gate(x)) * up(x)) (abi96062 components.py, SwiGLU_FFN)
+ *   head               -> logits = RMSNorm_f(x) E^T, lm_head tied to the embedding E
+ *                         (abi96062 model.py, weight tying)
+ *   decode             -> one new token per sequence at position cache_len[b]; its k (after
+ *                         RoPE) and v are appended to the cache and it attends over keys
+ *                         0 .. cache_len[b] (Sualeh77 model.py, "7. Top-level", forward with
+ *                         past_key_values; the cache holds keys after RoPE)
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked "host". The caller owns every buffer
+ *     (weights, ids, caches, logits, workspace); the library keeps no pointer after it
+ *     returns, never allocates or frees device memory and never synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = default
+ *     stream) and is asynchronous. No memset nodes are recorded, so the calls may be
+ *     captured into a HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued. A failed check
+ *     returns a status and enqueues nothing; smol_last_error() then names the
+ *     argument. SMOL_ERR_HIP reports a launch error (hipGetLastError after enqueue);
+ *     faults during execution surface at the caller's next synchronisation.
+ *   - Element types follow config.dtype: SMOL_F32 -> float, SMOL_BF16 -> bfloat16
+ *     (weights, embedding, norm weights, caches, logits). The residual stream inside
+ *     the library and the hidden states at the block interface are float32 for both.
+ *   - Matrices are row-major. Linear weights are [out, in] (as nn.Linear stores them):
+ *     wq [n_heads*d, H], wk/wv [n_kv*d, H], wo [H, n_heads*d], w_gate/w_up [I, H],
+ *     w_down [H, I]; norm weights [H]; embedding [vocab, H].
+ *   - Supported shapes: head_dim 64 or 128; hidden, intermediate and vocab multiples
+ *     of 64; hidden == n_heads*head_dim; n_heads divisible by n_kv_heads with 1 to 4
+ *     query heads per kv head. Anything else returns SMOL_ERR_UNSUPPORTED or
+ *     SMOL_ERR_INVALID_ARG. Batch and sequence length are arbitrary (>= 1).
+ *   - Calls that share a workspace or a cache must not overlap.
+ */
+#ifndef SMOL_H
+#define SMOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMOL_OK = 0,
+  SMOL_ERR_INVALID_ARG = 1, /* null pointer, size out of range, inconsistent config */
+  SMOL_ERR_UNSUPPORTED = 2, /* a valid shape this library does not implement */
+  SMOL_ERR_WORKSPACE = 3,   /* ws_bytes smaller than smol_workspace_size() */
+  SMOL_ERR_HIP = 4          /* the HIP runtime reported an error while enqueuing */
+} smol_status;
+
+typedef enum { SMOL_F32 = 0, SMOL_BF16 = 1 } smol_dtype;
+
+typedef enum { SMOL_OP_BLOCK = 0, SMOL_OP_PREFILL = 1, SMOL_OP_DECODE = 2 } smol_op;
+
+/* Model shape (host struct). SmolLM2-135M: hidden 576, n_heads 9, n_kv_heads 3,
+ * head_dim 64, intermediate 1536, n_layers 30, vocab 49152, max_pos 8192,
+ * rms_eps 1e-5, rope_theta 100000 (Sualeh77 model.py, "1. Config"). */
+typedef struct {
+  int32_t hidden, n_heads, n_kv_heads, head_dim, intermediate, n_layers, vocab, max_pos;
+  float rms_eps, rope_theta;
+  int32_t dtype; /* smol_dtype */
+} smol_config;
+
+/* One block's weights (host struct of device pointers), element type config.dtype. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} smol_layer_weights;
+
+/* The model (host struct): embed [vocab, H] is also the lm_head (tied); layers is a
+ * HOST array of n_layers entries; final_norm [H]. */
+typedef struct {
+  const void *embed;
+  const smol_layer_weights *layers;
+  const void *final_norm;
+} smol_model_weights;
+
+/* Bytes of scratch device memory that `op` needs for this config, batch and seq;
+ * for SMOL_OP_DECODE pass the cache capacity (cache_cap) as seq. Host-only;
+ * writes *bytes. The workspace must be 256-byte aligned. */
+smol_status smol_workspace_size(const smol_config *cfg, int op, int batch, int seq, size_t *bytes);
+
+/* One decoder block on hidden states x_in [batch, seq, H] float32 -> x_out (same
+ * shape, float32; may equal x_in). Token t sits at absolute position pos0 + t.
+ * k_cache / v_cache: NULL, or [batch, n_kv, cache_cap, head_dim] caches that receive
+ * the block's k (after RoPE) and v at indices pos0 .. pos0+seq-1; with a cache the
+ * queries also attend to the cached keys 0 .. pos0-1. Without a cache they attend
+ * only to the seq new tokens. Requires pos0 + seq <= max_pos (and <= cache_cap). */
+smol_status smol_block_forward(const smol_config *cfg, const smol_layer_weights *w,
+                               const float *x_in, float *x_out, int batch, int seq, int pos0,
+                               void *k_cache, void *v_cache, int cache_cap,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* Whole-model prefill: ids [batch, seq] int32 at positions 0 .. seq-1 -> logits
+ * [batch, seq, vocab]. k_cache / v_cache: NULL, or [n_layers, batch, n_kv, cache_cap,
+ * head_dim] caches filled at indices 0 .. seq-1 for a later smol_decode_step.
+ * Requires seq <= max_pos (and <= cache_cap). Ids must lie in [0, vocab): an id
+ * outside it makes its sequence's logits NaN from that position on (earlier
+ * positions of that sequence may turn NaN too; other sequences are unaffected). */
+smol_status smol_model_prefill(const smol_config *cfg, const smol_model_weights *w,
+                               const int32_t *ids, int batch, int seq, void *logits,
+                               void *k_cache, void *v_cache, int cache_cap,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* One decode step: ids [batch] int32; cache_len [batch] int32 (device) = positions
+ * already in the cache for each sequence. Sequence b's token sits at position
+ * cache_len[b]: its k (after RoPE) and v are written to index cache_len[b] of every
+ * layer's cache [n_layers, batch, n_kv, cache_cap, head_dim] and it attends to
+ * indices 0 .. cache_len[b]. logits [batch, vocab]. cache_len is not advanced. A
+ * sequence whose cache_len[b] is negative or leaves no room (cache_len[b] >=
+ * min(cache_cap, max_pos)) writes nothing to the cache and gets NaN logits. */
+smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w,
+                             const int32_t *ids, const int32_t *cache_len, int batch,
+                             void *k_cache, void *v_cache, int cache_cap, void *logits,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *smol_status_string(smol_status s);
+
+/* Text of the last failed check on this thread ("" if none). */
+const char *smol_last_error(void);
+
+/* Kernel-duration measurement (diagnostic, not for captured streams). After
+ * smol_timing_begin(kernel, max_launches) the next launches of that kernel class
+ * (smol_kernel) are bracketed by HIP events on their stream, up to max_launches.
+ * smol_timing_end() waits for those events and returns the summed duration in
+ * milliseconds and the number of launches timed (host pointers). */
+typedef enum {
+  SMOL_K_EMBED = 0, SMOL_K_RMSNORM = 1, SMOL_K_QKV_ROPE = 2, SMOL_K_ATTENTION = 3,
+  SMOL_K_O_PROJ = 4, SMOL_K_GATE_UP = 5, SMOL_K_DOWN = 6, SMOL_K_LM_HEAD = 7,
+  SMOL_K_DECODE_ATTENTION = 8, SMOL_K_DECODE_COMBINE = 9, SMOL_K_COUNT = 10
+} smol_kernel;
+smol_status smol_timing_begin(int kernel, int max_launches);
+smol_status smol_timing_end(float *total_ms, int *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOL_H */

@@ -1,0 +1,440 @@
+// The C ABI (include/smol.h): host-side argument checks, workspace layout and
+// the sequence of kernel launches for a block, a prefill and a decode step.
+//
+// Order of one block (nnterp "SmolLM3", "The block, in order"; tohio block.py):
+//   u = RMSNorm(x; attn_norm)            rmsnorm
+//   q, k, v = u W^T, RoPE on q, k        gemm_qkv_rope (k, v land in the cache)
+//   o = causal GQA attention             attention_prefill / attention_decode
+//   x += o W_o^T                         gemm_residual
+//   u = RMSNorm(x; mlp_norm)             rmsnorm
+//   y = silu(u W_g^T) * (u W_u^T)        gemm_swiglu
+//   x += y W_d^T                         gemm_residual
+// The model adds the embedding gather before and RMSNorm + the tied head after
+// (abi96062 model.py, SmolLM2Model.forward).
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+#include "smol.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+smol_status fail(smol_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+struct Dims {
+  int H, nq, nkv, d, I, L, V, max_pos, G;
+  float eps, theta;
+  bool bf16;
+  size_t esz;
+};
+
+smol_status check_config(const smol_config *c, Dims *o) {
+  if (!c) return fail(SMOL_ERR_INVALID_ARG, "cfg is NULL");
+  if (c->dtype != SMOL_F32 && c->dtype != SMOL_BF16) return fail(SMOL_ERR_INVALID_ARG, "dtype %d unknown", c->dtype);
+  if (c->hidden < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 || c->intermediate < 1 ||
+      c->n_layers < 1 || c->vocab < 1 || c->max_pos < 1)
+    return fail(SMOL_ERR_INVALID_ARG, "config sizes must be >= 1");
+  if (c->hidden != c->n_heads * c->head_dim)
+    return fail(SMOL_ERR_INVALID_ARG, "hidden %d != n_heads %d * head_dim %d", c->hidden, c->n_heads, c->head_dim);
+  if (c->n_heads % c->n_kv_heads != 0)
+    return fail(SMOL_ERR_INVALID_ARG, "n_heads %d not divisible by n_kv_heads %d", c->n_heads, c->n_kv_heads);
+  if (!(std::isfinite(c->rms_eps) && c->rms_eps >= 0.f)) return fail(SMOL_ERR_INVALID_ARG, "rms_eps must be finite, >= 0");
+  if (!(std::isfinite(c->rope_theta) && c->rope_theta > 0.f)) return fail(SMOL_ERR_INVALID_ARG, "rope_theta must be > 0");
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G > 4) return fail(SMOL_ERR_UNSUPPORTED, "%d query heads per kv head (supported: 1..4)", G);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(SMOL_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
+  if (c->hidden % 64 || c->intermediate % 64 || c->vocab % 64)
+    return fail(SMOL_ERR_UNSUPPORTED, "hidden, intermediate and vocab must be multiples of 64");
+  o->H = c->hidden;
+  o->nq = c->n_heads;
+  o->nkv = c->n_kv_heads;
+  o->d = c->head_dim;
+  o->I = c->intermediate;
+  o->L = c->n_layers;
+  o->V = c->vocab;
+  o->max_pos = c->max_pos;
+  o->G = G;
+  o->eps = c->rms_eps;
+  o->theta = c->rope_theta;
+  o->bf16 = c->dtype == SMOL_BF16;
+  o->esz = o->bf16 ? 2 : 4;
+  return SMOL_OK;
+}
+
+smol_status check_layer(const smol_layer_weights *w, int idx) {
+  if (!w) return fail(SMOL_ERR_INVALID_ARG, "layer weights %d: NULL", idx);
+  const void *p[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
+  static const char *names[9] = {"attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"};
+  for (int i = 0; i < 9; ++i)
+    if (!p[i]) return fail(SMOL_ERR_INVALID_ARG, "layer %d: %s is NULL", idx, names[i]);
+  return SMOL_OK;
+}
+
+constexpr size_t ALIGN = 256;
+size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Workspace carve-up. Offsets in bytes from ws.
+struct Ws {
+  size_t x, u, q, k, v, o, y, part, total;
+};
+
+Ws layout(const Dims &D, int op, int B, int T) {
+  Ws w{};
+  const size_t M = (op == SMOL_OP_DECODE) ? (size_t)B : (size_t)B * T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += up(bytes); return at; };
+  w.x = take(M * D.H * 4);
+  w.u = take(M * D.H * D.esz);
+  w.q = take(M * D.nq * D.d * D.esz);
+  w.o = take(M * D.nq * D.d * D.esz);
+  w.y = take(M * D.I * D.esz);
+  if (op == SMOL_OP_DECODE) {
+    int chunk;
+    const int cap = std::min(T, D.max_pos);
+    const int splits = smol::decode_splits(cap, &chunk);
+    w.part = take((size_t)B * D.nq * splits * (D.d + 2) * 4);
+  } else {
+    w.k = take((size_t)B * D.nkv * T * D.d * D.esz);
+    w.v = take((size_t)B * D.nkv * T * D.d * D.esz);
+  }
+  w.total = off;
+  return w;
+}
+
+// ------------------------------------------------------------------ timing
+
+struct Timing {
+  std::mutex mu;
+  int kernel = -1, max = 0, count = 0;
+  std::vector<hipEvent_t> ev;  // start/stop pairs
+} g_timing;
+
+}  // namespace
+
+namespace smol {
+
+void timing_before(int kernel, hipStream_t s) {
+  if (g_timing.kernel != kernel || g_timing.count >= g_timing.max) return;
+  (void)hipEventRecord(g_timing.ev[2 * g_timing.count], s);
+}
+
+void timing_after(int kernel, hipStream_t s) {
+  if (g_timing.kernel != kernel || g_timing.count >= g_timing.max) return;
+  (void)hipEventRecord(g_timing.ev[2 * g_timing.count + 1], s);
+  ++g_timing.count;
+}
+
+}  // namespace smol
+
+namespace {
+
+#define SMOL_LAUNCH(kind, call)                                                                        \
+  do {                                                                                                 \
+    smol::timing_before(kind, s);                                                                      \
+    hipError_t e_ = (call);                                                                            \
+    smol::timing_after(kind, s);                                                                       \
+    if (e_ != hipSuccess) return fail(SMOL_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));         \
+  } while (0)
+
+struct LayerCtx {
+  const Dims *D;
+  char *ws;
+  Ws lay;
+  int B, T, pos0;
+  void *kc, *vc;
+  int cap, kv_off, q_key_off;
+  const int *cache_len;  // decode only
+  float inv_freq[64];
+  hipStream_t s;
+};
+
+template <typename T>
+smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x) {
+  const Dims &D = *c.D;
+  const hipStream_t s = c.s;
+  const bool decode = c.cache_len != nullptr;
+  const int M = decode ? c.B : c.B * c.T;
+  using A = Act<T>;  // activations: MFMA operand type
+  A *u = (A *)(c.ws + c.lay.u);
+  A *q = (A *)(c.ws + c.lay.q);
+  A *o = (A *)(c.ws + c.lay.o);
+  A *y = (A *)(c.ws + c.lay.y);
+
+  SMOL_LAUNCH(SMOL_K_RMSNORM, smol::rmsnorm<T>(x, (const T *)w->attn_norm, u, M, D.H, D.eps, s));
+  smol::QkvOut qo{M, D.H, D.nq * D.d, D.nkv * D.d, D.d, q, c.kc, c.vc,
+                  decode ? 1 : c.T, c.cap, D.nkv, c.pos0, c.kv_off, D.max_pos, c.cache_len, c.inv_freq};
+  SMOL_LAUNCH(SMOL_K_QKV_ROPE, smol::gemm_qkv_rope<T>(u, (const T *)w->wq, (const T *)w->wk, (const T *)w->wv, qo, s));
+  if (decode) {
+    int chunk;
+    const int splits = smol::decode_splits(std::min(c.cap, D.max_pos), &chunk);
+    smol::DecodeAttnArgs da{q, c.kc, c.vc, o, c.cache_len, c.B, D.nq, D.nkv, D.d, c.cap, D.max_pos, splits, chunk,
+                            (float *)(c.ws + c.lay.part)};
+    hipError_t e = smol::attention_decode<T>(da, s);
+    if (e != hipSuccess) return fail(SMOL_ERR_HIP, "attention_decode: %s", hipGetErrorString(e));
+  } else {
+    smol::AttnArgs aa{q, c.kc, c.vc, o, c.B, c.T, D.nq, D.nkv, D.d, c.cap, c.q_key_off};
+    SMOL_LAUNCH(SMOL_K_ATTENTION, smol::attention_prefill<T>(aa, s));
+  }
+  SMOL_LAUNCH(SMOL_K_O_PROJ, smol::gemm_residual<T>(o, (const T *)w->wo, M, D.H, D.nq * D.d, x, s));
+  SMOL_LAUNCH(SMOL_K_RMSNORM, smol::rmsnorm<T>(x, (const T *)w->mlp_norm, u, M, D.H, D.eps, s));
+  SMOL_LAUNCH(SMOL_K_GATE_UP, smol::gemm_swiglu<T>(u, (const T *)w->w_gate, (const T *)w->w_up, M, D.I, D.H, y, s));
+  SMOL_LAUNCH(SMOL_K_DOWN, smol::gemm_residual<T>(y, (const T *)w->w_down, M, D.H, D.I, x, s));
+  return SMOL_OK;
+}
+
+void fill_inv_freq(const Dims &D, float *f) {
+  // omega_i = theta^(-2i/d) (abi96062 components.py, RotaryEmbedding), in double, rounded once
+  for (int i = 0; i < D.d / 2; ++i) f[i] = (float)std::pow((double)D.theta, -2.0 * i / D.d);
+}
+
+smol_status check_ws(const Dims &D, int op, int B, int T, void *ws, size_t ws_bytes, Ws *lay) {
+  *lay = layout(D, op, B, T);
+  if (!ws) return fail(SMOL_ERR_INVALID_ARG, "ws is NULL");
+  if (ws_bytes < lay->total)
+    return fail(SMOL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, lay->total);
+  if ((uintptr_t)ws % ALIGN) return fail(SMOL_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  return SMOL_OK;
+}
+
+template <typename T>
+smol_status head(const Dims &D, const smol_model_weights *w, float *x, int M, void *logits, char *ws, const Ws &lay,
+                 hipStream_t s) {
+  Act<T> *u = (Act<T> *)(ws + lay.u);
+  SMOL_LAUNCH(SMOL_K_RMSNORM, smol::rmsnorm<T>(x, (const T *)w->final_norm, u, M, D.H, D.eps, s));
+  SMOL_LAUNCH(SMOL_K_LM_HEAD, smol::gemm_store<T>(u, (const T *)w->embed, M, D.V, D.H, logits, 0, s));
+  return SMOL_OK;
+}
+
+template <typename T>
+smol_status block_impl(const Dims &D, const smol_layer_weights *w, const float *x_in, float *x_out, int B, int T_,
+                       int pos0, void *kc, void *vc, int cap, char *ws, const Ws &lay, hipStream_t s) {
+  LayerCtx c{};
+  c.D = &D;
+  c.ws = ws;
+  c.lay = lay;
+  c.B = B;
+  c.T = T_;
+  c.pos0 = pos0;
+  c.s = s;
+  if (kc) {
+    c.kc = kc; c.vc = vc; c.cap = cap; c.kv_off = 0; c.q_key_off = pos0;
+  } else {
+    c.kc = ws + lay.k; c.vc = ws + lay.v; c.cap = T_; c.kv_off = pos0; c.q_key_off = 0;
+  }
+  fill_inv_freq(D, c.inv_freq);
+  if (x_out != x_in) SMOL_LAUNCH(-1, smol::copy_f32(x_in, x_out, (size_t)B * T_ * D.H, s));
+  return run_layer<T>(c, w, x_out);
+}
+
+template <typename T>
+smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32_t *ids, int B, int T_, void *logits,
+                         void *kc, void *vc, int cap, char *ws, const Ws &lay, hipStream_t s) {
+  float *x = (float *)(ws + lay.x);
+  const int M = B * T_;
+  SMOL_LAUNCH(SMOL_K_EMBED, smol::embed_rows<T>(ids, (const T *)w->embed, x, M, D.H, D.V, s));
+  LayerCtx c{};
+  c.D = &D;
+  c.ws = ws;
+  c.lay = lay;
+  c.B = B;
+  c.T = T_;
+  c.pos0 = 0;
+  c.s = s;
+  fill_inv_freq(D, c.inv_freq);
+  const size_t layer_elems = (size_t)B * D.nkv * cap * D.d;
+  for (int l = 0; l < D.L; ++l) {
+    if (kc) {
+      c.kc = (char *)kc + l * layer_elems * D.esz;
+      c.vc = (char *)vc + l * layer_elems * D.esz;
+      c.cap = cap; c.kv_off = 0; c.q_key_off = 0;
+    } else {
+      c.kc = ws + lay.k; c.vc = ws + lay.v; c.cap = T_; c.kv_off = 0; c.q_key_off = 0;
+    }
+    smol_status st = run_layer<T>(c, &w->layers[l], x);
+    if (st != SMOL_OK) return st;
+  }
+  return head<T>(D, w, x, M, logits, ws, lay, s);
+}
+
+template <typename T>
+smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_t *ids, const int32_t *cache_len,
+                        int B, void *kc, void *vc, int cap, void *logits, char *ws, const Ws &lay, hipStream_t s) {
+  float *x = (float *)(ws + lay.x);
+  SMOL_LAUNCH(SMOL_K_EMBED, smol::embed_rows<T>(ids, (const T *)w->embed, x, B, D.H, D.V, s));
+  LayerCtx c{};
+  c.D = &D;
+  c.ws = ws;
+  c.lay = lay;
+  c.B = B;
+  c.T = 1;
+  c.cap = cap;
+  c.cache_len = cache_len;
+  c.s = s;
+  fill_inv_freq(D, c.inv_freq);
+  const size_t layer_elems = (size_t)B * D.nkv * cap * D.d;
+  for (int l = 0; l < D.L; ++l) {
+    c.kc = (char *)kc + l * layer_elems * D.esz;
+    c.vc = (char *)vc + l * layer_elems * D.esz;
+    smol_status st = run_layer<T>(c, &w->layers[l], x);
+    if (st != SMOL_OK) return st;
+  }
+  return head<T>(D, w, x, B, logits, ws, lay, s);
+}
+
+smol_status check_model(const Dims &D, const smol_model_weights *w) {
+  if (!w) return fail(SMOL_ERR_INVALID_ARG, "model weights NULL");
+  if (!w->embed) return fail(SMOL_ERR_INVALID_ARG, "embed is NULL");
+  if (!w->final_norm) return fail(SMOL_ERR_INVALID_ARG, "final_norm is NULL");
+  if (!w->layers) return fail(SMOL_ERR_INVALID_ARG, "layers is NULL");
+  for (int l = 0; l < D.L; ++l) {
+    smol_status st = check_layer(&w->layers[l], l);
+    if (st != SMOL_OK) return st;
+  }
+  return SMOL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+smol_status smol_workspace_size(const smol_config *cfg, int op, int batch, int seq, size_t *bytes) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if (!bytes) return fail(SMOL_ERR_INVALID_ARG, "bytes is NULL");
+  if (op != SMOL_OP_BLOCK && op != SMOL_OP_PREFILL && op != SMOL_OP_DECODE) return fail(SMOL_ERR_INVALID_ARG, "op %d", op);
+  if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch and seq must be >= 1");
+  *bytes = layout(D, op, batch, seq).total;
+  return SMOL_OK;
+}
+
+smol_status smol_block_forward(const smol_config *cfg, const smol_layer_weights *w, const float *x_in, float *x_out,
+                               int batch, int seq, int pos0, void *k_cache, void *v_cache, int cache_cap, void *ws,
+                               size_t ws_bytes, void *stream) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if ((st = check_layer(w, 0)) != SMOL_OK) return st;
+  if (!x_in || !x_out) return fail(SMOL_ERR_INVALID_ARG, "x_in / x_out is NULL");
+  if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d, seq %d must be >= 1", batch, seq);
+  if (pos0 < 0) return fail(SMOL_ERR_INVALID_ARG, "pos0 %d < 0", pos0);
+  if ((long)pos0 + seq > D.max_pos)
+    return fail(SMOL_ERR_INVALID_ARG, "pos0 + seq = %ld exceeds max_pos %d", (long)pos0 + seq, D.max_pos);
+  if (!k_cache != !v_cache) return fail(SMOL_ERR_INVALID_ARG, "k_cache and v_cache must both be set or both NULL");
+  if (k_cache && cache_cap < pos0 + seq)
+    return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d < pos0 + seq = %d", cache_cap, pos0 + seq);
+  Ws lay;
+  if ((st = check_ws(D, SMOL_OP_BLOCK, batch, seq, ws, ws_bytes, &lay)) != SMOL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return D.bf16 ? block_impl<bf16>(D, w, x_in, x_out, batch, seq, pos0, k_cache, v_cache, cache_cap, (char *)ws, lay, s)
+                : block_impl<float>(D, w, x_in, x_out, batch, seq, pos0, k_cache, v_cache, cache_cap, (char *)ws, lay, s);
+}
+
+smol_status smol_model_prefill(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids, int batch,
+                               int seq, void *logits, void *k_cache, void *v_cache, int cache_cap, void *ws,
+                               size_t ws_bytes, void *stream) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if ((st = check_model(D, w)) != SMOL_OK) return st;
+  if (!ids || !logits) return fail(SMOL_ERR_INVALID_ARG, "ids / logits is NULL");
+  if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d, seq %d must be >= 1", batch, seq);
+  if (seq > D.max_pos) return fail(SMOL_ERR_INVALID_ARG, "seq %d exceeds max_pos %d", seq, D.max_pos);
+  if (!k_cache != !v_cache) return fail(SMOL_ERR_INVALID_ARG, "k_cache and v_cache must both be set or both NULL");
+  if (k_cache && cache_cap < seq) return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d < seq %d", cache_cap, seq);
+  Ws lay;
+  if ((st = check_ws(D, SMOL_OP_PREFILL, batch, seq, ws, ws_bytes, &lay)) != SMOL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return D.bf16 ? prefill_impl<bf16>(D, w, ids, batch, seq, logits, k_cache, v_cache, cache_cap, (char *)ws, lay, s)
+                : prefill_impl<float>(D, w, ids, batch, seq, logits, k_cache, v_cache, cache_cap, (char *)ws, lay, s);
+}
+
+smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids,
+                             const int32_t *cache_len, int batch, void *k_cache, void *v_cache, int cache_cap,
+                             void *logits, void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if ((st = check_model(D, w)) != SMOL_OK) return st;
+  if (!ids || !cache_len || !logits) return fail(SMOL_ERR_INVALID_ARG, "ids / cache_len / logits is NULL");
+  if (!k_cache || !v_cache) return fail(SMOL_ERR_INVALID_ARG, "decode needs k_cache and v_cache");
+  if (batch < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d must be >= 1", batch);
+  if (cache_cap < 1) return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d must be >= 1", cache_cap);
+  Ws lay;
+  if ((st = check_ws(D, SMOL_OP_DECODE, batch, cache_cap, ws, ws_bytes, &lay)) != SMOL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return D.bf16 ? decode_impl<bf16>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay, s)
+                : decode_impl<float>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay, s);
+}
+
+const char *smol_status_string(smol_status s) {
+  switch (s) {
+    case SMOL_OK: return "ok";
+    case SMOL_ERR_INVALID_ARG: return "invalid argument";
+    case SMOL_ERR_UNSUPPORTED: return "unsupported shape";
+    case SMOL_ERR_WORKSPACE: return "workspace too small";
+    case SMOL_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *smol_last_error(void) { return g_err.c_str(); }
+
+smol_status smol_timing_begin(int kernel, int max_launches) {
+  g_err.clear();
+  if (kernel < 0 || kernel >= SMOL_K_COUNT) return fail(SMOL_ERR_INVALID_ARG, "kernel class %d", kernel);
+  if (max_launches < 1 || max_launches > 1 << 16) return fail(SMOL_ERR_INVALID_ARG, "max_launches %d", max_launches);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  while ((int)g_timing.ev.size() < 2 * max_launches) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return fail(SMOL_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    g_timing.ev.push_back(e);
+  }
+  g_timing.kernel = kernel;
+  g_timing.max = max_launches;
+  g_timing.count = 0;
+  return SMOL_OK;
+}
+
+smol_status smol_timing_end(float *total_ms, int *launches) {
+  g_err.clear();
+  if (!total_ms || !launches) return fail(SMOL_ERR_INVALID_ARG, "total_ms / launches is NULL");
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  float sum = 0.f;
+  for (int i = 0; i < g_timing.count; ++i) {
+    hipError_t err = hipEventSynchronize(g_timing.ev[2 * i + 1]);
+    if (err != hipSuccess) return fail(SMOL_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(err));
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]);
+    if (err != hipSuccess) return fail(SMOL_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(err));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = g_timing.count;
+  g_timing.kernel = -1;
+  g_timing.count = 0;
+  return SMOL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Shared device helpers for the gfx950 kernels: element types, MFMA wrappers,
+// wavefront reductions. Wave size is 64 on CDNA4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define SMOL_WAVE 64
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }     // RNE
+
+// ---------------------------------------------------------------- element types
+// W: how weights, the embedding, the KV cache and the logits are stored (the
+// model's dtype). Act<W>: the MFMA operand type of the activations. For bfloat16
+// models the activations are float16: every bfloat16 value whose magnitude lies in
+// float16's normal range converts to float16 exactly (8 significant bits fit in
+// 11), and float16 keeps 3 more bits of each activation at the same MFMA rate.
+template <typename W> struct OperandOf { using type = W; };
+template <> struct OperandOf<bf16> { using type = f16; };
+template <typename W> using Act = typename OperandOf<W>::type;
+
+// ---------------------------------------------------------------- fragments
+// A 32x32x16 MFMA step takes, per lane, 8 consecutive K values of one row of A
+// (row = lane % 32, K chunk = lane / 32) and likewise of one column of B. Frag<T>
+// holds those 8 values. The same register layout feeds both element types: for
+// float the step is issued as eight 32x32x2 MFMAs, instruction j taking element j
+// of every lane. A and B are always loaded the same way, so the order in which K
+// is summed inside a step does not change the contraction.
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<f16> { f16x8 v; };
+template <> struct Frag<float> { f32x8 v; };
+
+__device__ __forceinline__ void mma_32x32x16(f32x16 &acc, const Frag<bf16> &a, const Frag<bf16> &b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_32x32x16(f32x16 &acc, const Frag<f16> &a, const Frag<f16> &b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.v, b.v, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mma_32x32x16(f32x16 &acc, const Frag<float> &a, const Frag<float> &b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+// Load 8 consecutive elements (16 B for bf16, 32 B for float).
+__device__ __forceinline__ void load_frag(Frag<bf16> &f, const bf16 *p) {
+  f.v = *reinterpret_cast<const bf16x8 *>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<f16> &f, const f16 *p) {
+  f.v = *reinterpret_cast<const f16x8 *>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float> &f, const float *p) {
+  const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+  f.v = (f32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Row of the 32x32 accumulator held in register r of a lane (column = lane % 32).
+__device__ __forceinline__ int acc_row(int r, int lane) { return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3); }
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, SMOL_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, SMOL_WAVE));
+  return v;
+}
+
+// 16-byte vector (8 two-byte or 4 four-byte elements) for global <-> LDS staging.
+// A native vector type, so that arrays of chunks stay in registers.
+typedef uint32_t Chunk16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Chunk16 ld16(const void *p) { return *reinterpret_cast<const Chunk16 *>(p); }
+__device__ __forceinline__ void st16(void *p, Chunk16 v) { *reinterpret_cast<Chunk16 *>(p) = v; }
+
+// Element e of a chunk viewed as T.
+template <typename T> __device__ __forceinline__ T chunk_elem(const Chunk16 &c, int e);
+template <> __device__ __forceinline__ float chunk_elem<float>(const Chunk16 &c, int e) { return __uint_as_float(c[e]); }
+template <> __device__ __forceinline__ bf16 chunk_elem<bf16>(const Chunk16 &c, int e) {
+  return __builtin_bit_cast(bf16, (uint16_t)(c[e >> 1] >> ((e & 1) * 16)));
+}
+template <> __device__ __forceinline__ f16 chunk_elem<f16>(const Chunk16 &c, int e) {
+  return __builtin_bit_cast(f16, (uint16_t)(c[e >> 1] >> ((e & 1) * 16)));
+}
+
+// Convert a staged chunk from storage type W to operand type Act<W> (same size).
+template <typename W> __device__ __forceinline__ Chunk16 to_operand(const Chunk16 &c) { return c; }
+template <> __device__ __forceinline__ Chunk16 to_operand<bf16>(const Chunk16 &c) {
+  Chunk16 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16 lo = (f16)__uint_as_float(c[i] << 16);
+    const f16 hi = (f16)__uint_as_float(c[i] & 0xffff0000u);
+    r[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return r;
+}

@@ -1,0 +1,231 @@
+// Decode attention: one new query per (sequence, head) against the KV cache,
+// split along the keys so that the whole cache streams through every CU.
+//
+// The new token of sequence b sits at position P = cache_len[b] and sees keys
+// 0 .. P with no mask (Sualeh77 model.py, "4. Attention": with a cache the single
+// new token attends to all past keys and itself). This step is bound by HBM:
+// every cached key and value is read once.
+//
+// Kernel 1, grid (splits, n_kv, B), 256 threads: a workgroup takes `chunk`
+// consecutive keys of kv head g and serves all G query heads of the group.
+// D/EPC lanes cooperate on one key row (16-byte loads, fully coalesced rows);
+// phase 1 writes scaled scores to LDS, phase 2 takes the chunk's max and exp-sum
+// per head, phase 3 accumulates p * v. The partial (max, sum, o[D]) goes to ws.
+// Kernel 2, grid (B * n_heads), D threads: merges the partials of one head
+// (rescaling by exp(m_s - m)) and writes the attention output.
+#include "common.h"
+#include "kernels.h"
+
+namespace smol {
+
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_CHUNK = 256;
+
+int decode_splits(int cap, int *chunk) {
+  *chunk = DEC_CHUNK;
+  return (cap + DEC_CHUNK - 1) / DEC_CHUNK;
+}
+
+__device__ __forceinline__ bool decode_pos_ok(int P, int cap, int max_pos) { return P >= 0 && P < cap && P < max_pos; }
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(DEC_THREADS)
+decode_attn_kernel(const DecodeAttnArgs a) {
+  using A = Act<T>;  // q arrives in the operand type; the cache is in the storage type T
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int LPK = D / EPC;             // lanes per key row
+  constexpr int KPP = DEC_THREADS / LPK;   // keys per pass
+  constexpr int CHUNK = DEC_CHUNK;
+  static_assert(64 % LPK == 0, "a key row must stay inside one wavefront");
+
+  __shared__ float S[G][CHUNK];
+  __shared__ float red[KPP][G][D];
+  __shared__ float stat[G][2];
+
+  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int kk = tid / LPK, dl = tid % LPK, d0 = dl * EPC;
+  const int P = a.cache_len[b];
+  float *part = a.part + (((size_t)b * a.n_heads + g * G) * a.splits + sp) * (D + 2);
+  const size_t head_stride = (size_t)a.splits * (D + 2);
+
+  const int k_begin = sp * CHUNK;
+  const int k_end = decode_pos_ok(P, a.cap, a.max_pos) ? min(k_begin + CHUNK, P + 1) : 0;
+  const int n = k_end - k_begin;
+  if (n <= 0) {  // empty split: neutral partial
+    if (tid < G) {
+      part[tid * head_stride + 0] = -INFINITY;
+      part[tid * head_stride + 1] = 0.f;
+    }
+    return;
+  }
+
+  float q[G][EPC];
+  const A *qp = (const A *)a.q + (size_t)b * a.n_heads * D + g * G * D + d0;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const Chunk16 c = ld16(qp + hh * D);
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) q[hh][j] = to_f32(chunk_elem<A>(c, j));
+  }
+
+  const T *kb = (const T *)a.k + ((size_t)(b * a.n_kv + g) * a.cap + k_begin) * D + d0;
+  const T *vb = (const T *)a.v + ((size_t)(b * a.n_kv + g) * a.cap + k_begin) * D + d0;
+  const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
+
+  // phase 1: scores
+  constexpr int PASSES = CHUNK / KPP;
+  {
+    Chunk16 kc[PASSES];
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int j = min(kk + it * KPP, n - 1);  // rows past the chunk re-read its last key
+      kc[it] = ld16(kb + (size_t)j * D);
+    }
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int j = kk + it * KPP;
+      float dot[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < EPC; ++x) acc += q[hh][x] * to_f32(chunk_elem<T>(kc[it], x));
+        dot[hh] = acc;
+      }
+#pragma unroll
+      for (int o = LPK / 2; o > 0; o >>= 1)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) dot[hh] += __shfl_xor(dot[hh], o, 64);
+      if (dl == 0 && j < n)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) S[hh][j] = dot[hh] * c_log2;
+    }
+  }
+  __syncthreads();
+
+  // phase 2: per-head max and exp-sum over the chunk (wave w serves head w)
+  const int w = tid >> 6, lane = tid & 63;
+  for (int hh = w; hh < G; hh += DEC_THREADS / 64) {
+    float m = -INFINITY;
+    for (int j = lane; j < n; j += 64) m = fmaxf(m, S[hh][j]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int j = lane; j < n; j += 64) {
+      const float p = exp2f(S[hh][j] - m);
+      S[hh][j] = p;
+      l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0) {
+      stat[hh][0] = m;
+      stat[hh][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // phase 3: o = sum_j p_j v_j
+  {
+    float acc[G][EPC];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int x = 0; x < EPC; ++x) acc[hh][x] = 0.f;
+    Chunk16 vc[PASSES];
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int j = min(kk + it * KPP, n - 1);
+      vc[it] = ld16(vb + (size_t)j * D);
+    }
+#pragma unroll
+    for (int it = 0; it < PASSES; ++it) {
+      const int j = kk + it * KPP;
+      if (j < n) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float p = S[hh][j];
+#pragma unroll
+          for (int x = 0; x < EPC; ++x) acc[hh][x] += p * to_f32(chunk_elem<T>(vc[it], x));
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int x = 0; x < EPC; ++x) red[kk][hh][d0 + x] = acc[hh][x];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += DEC_THREADS) {
+    const int hh = i / D, d = i % D;
+    float s = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < KPP; ++r) s += red[r][hh][d];
+    part[hh * head_stride + 2 + d] = s;
+  }
+  if (tid < G) {
+    part[tid * head_stride + 0] = stat[tid][0];
+    part[tid * head_stride + 1] = stat[tid][1];
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(D)
+decode_combine_kernel(const DecodeAttnArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.n_heads, h = bh % a.n_heads;
+  const int d = threadIdx.x;
+  const int P = a.cache_len[b];
+  using A = Act<T>;
+  A *out = (A *)a.o + (size_t)b * a.n_heads * D + h * D + d;
+  if (!decode_pos_ok(P, a.cap, a.max_pos)) {
+    *out = from_f32<A>(__builtin_nanf(""));
+    return;
+  }
+  const float *part = a.part + ((size_t)b * a.n_heads + h) * a.splits * (D + 2);
+  const int used = (P + a.chunk) / a.chunk;  // splits that hold keys 0 .. P
+  float m = -INFINITY;
+  for (int s = 0; s < used; ++s) m = fmaxf(m, part[s * (D + 2)]);
+  float l = 0.f, acc = 0.f;
+  for (int s = 0; s < used; ++s) {
+    const float f = exp2f(part[s * (D + 2)] - m);
+    l += f * part[s * (D + 2) + 1];
+    acc += f * part[s * (D + 2) + 2 + d];
+  }
+  *out = from_f32<A>(acc / l);
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_dec(const DecodeAttnArgs &a, hipStream_t s) {
+  timing_before(8, s);
+  hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3(a.splits, a.n_kv, a.B), dim3(DEC_THREADS), 0, s, a);
+  timing_after(8, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  timing_before(9, s);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.n_heads), dim3(D), 0, s, a);
+  timing_after(9, s);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_dec_d(const DecodeAttnArgs &a, hipStream_t s) {
+  switch (a.n_heads / a.n_kv) {
+    case 1: return launch_dec<T, D, 1>(a, s);
+    case 2: return launch_dec<T, D, 2>(a, s);
+    case 3: return launch_dec<T, D, 3>(a, s);
+    case 4: return launch_dec<T, D, 4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t attention_decode(const DecodeAttnArgs &a, hipStream_t s) {
+  if (a.head_dim == 64) return launch_dec_d<T, 64>(a, s);
+  if (a.head_dim == 128) return launch_dec_d<T, 128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template hipError_t attention_decode<float>(const DecodeAttnArgs &, hipStream_t);
+template hipError_t attention_decode<bf16>(const DecodeAttnArgs &, hipStream_t);
+
+}  // namespace smol

@@ -1,0 +1,97 @@
+// RMSNorm (one wavefront per row, reduction by cross-lane shuffles), the
+// embedding gather and a float copy.
+//   RMSNorm: out = w * (x / sqrt(mean(x^2) + eps)) -- abi96062 components.py, RMSNorm;
+//            statistics in float32, one rounding to the operand type at the output.
+//   Embedding: x[m, :] = E[ids[m], :] -- abi96062 model.py, SmolLM2Model.forward.
+#include "common.h"
+#include "kernels.h"
+
+namespace smol {
+
+constexpr int NORM_ROWS = 4;  // rows (waves) per workgroup
+
+template <typename T, typename O, int VEC>
+__global__ void __launch_bounds__(64 * NORM_ROWS)
+rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ w, O *__restrict__ out, int M, int H, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * NORM_ROWS + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float *xr = x + (size_t)row * H;
+  O *orow = out + (size_t)row * H;
+  float ss = 0.f;
+  if constexpr (VEC == 4) {
+    for (int i = lane * 4; i < H; i += 256) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + i);
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+  } else {
+    for (int i = lane; i < H; i += 64) {
+      const float v = xr[i];
+      ss += v * v;
+    }
+  }
+  ss = wave_sum(ss);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+  if constexpr (VEC == 4) {
+    for (int i = lane * 4; i < H; i += 256) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) orow[i + j] = from_f32<O>(to_f32(w[i + j]) * (v[j] * r));
+    }
+  } else {
+    for (int i = lane; i < H; i += 64) orow[i] = from_f32<O>(to_f32(w[i]) * (xr[i] * r));
+  }
+}
+
+template <typename T>
+hipError_t rmsnorm(const float *x, const T *w, Act<T> *out, int M, int H, float eps, hipStream_t s) {
+  const dim3 grid((M + NORM_ROWS - 1) / NORM_ROWS), block(64 * NORM_ROWS);
+  if (H % 256 == 0)
+    hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 4>), grid, block, 0, s, x, w, out, M, H, eps);
+  else
+    hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 1>), grid, block, 0, s, x, w, out, M, H, eps);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+embed_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, float *__restrict__ x, int M, int H, int V) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int id = ids[row];
+  float *xr = x + (size_t)row * H;
+  if (id < 0 || id >= V) {
+    for (int i = lane; i < H; i += 64) xr[i] = __builtin_nanf("");
+    return;
+  }
+  const T *er = E + (size_t)id * H;
+  for (int i = lane; i < H; i += 64) xr[i] = to_f32(er[i]);
+}
+
+template <typename T>
+hipError_t embed_rows(const int32_t *ids, const T *E, float *x, int M, int H, int V, hipStream_t s) {
+  hipLaunchKernelGGL((embed_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, s, ids, E, x, M, H, V);
+  return hipGetLastError();
+}
+
+__global__ void copy_f32_kernel(const float *__restrict__ src, float *__restrict__ dst, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+hipError_t copy_f32(const float *src, float *dst, size_t n, hipStream_t s) {
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
+template hipError_t rmsnorm<float>(const float *, const float *, float *, int, int, float, hipStream_t);
+template hipError_t rmsnorm<bf16>(const float *, const bf16 *, f16 *, int, int, float, hipStream_t);
+template hipError_t embed_rows<float>(const int32_t *, const float *, float *, int, int, int, hipStream_t);
+template hipError_t embed_rows<bf16>(const int32_t *, const bf16 *, float *, int, int, int, hipStream_t);
+
+}  // namespace smol

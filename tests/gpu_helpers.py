@@ -1,0 +1,78 @@
+"""Shared helpers for the GPU parity tests: upload seeded inputs, run the C ABI,
+and feed the same inputs (exact stored values, float64) to the CPU oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle.smol as O
+from llama_decoder_only_amd import synthetic as S
+
+# fp32 and bf16 tolerances: rel = max|gpu - oracle| / max|oracle| over the compared tensor
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def say(msg: str):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rel(g, o) -> float:
+    g = np.asarray(g, np.float64)
+    o = np.asarray(o, np.float64)
+    return float(np.max(np.abs(g - o)) / max(float(np.max(np.abs(o))), 1e-300))
+
+
+def ocfg(s: S.Shape) -> O.Config:
+    return O.Config(hidden=s.hidden, n_heads=s.n_heads, n_kv_heads=s.n_kv_heads, intermediate=s.intermediate,
+                    n_layers=s.n_layers, vocab=s.vocab, max_pos=s.max_pos, rms_eps=s.rms_eps,
+                    rope_theta=s.rope_theta)
+
+
+def olayer(l: S.Layer) -> O.LayerWeights:
+    return O.LayerWeights(**{n: getattr(l, n).f64 for n in S.Layer.NAMES})
+
+
+def omodel(m: S.Model) -> O.ModelWeights:
+    return O.ModelWeights(embed=m.embed.f64, layers=[olayer(l) for l in m.layers], final_norm=m.final_norm.f64)
+
+
+def to_np(t) -> np.ndarray:
+    import torch
+
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype != torch.float64 else t.cpu().numpy()
+
+
+def block_rows_oracle(x, lw: O.LayerWeights, cfg: O.Config, rows, pos0=0):
+    """The block's output at the given token rows of one sequence x [T, H], composed from the
+    oracle's own steps: k and v over every position, q only at the rows asked for."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    d = cfg.head_dim
+    rows = np.asarray(rows)
+    u = O.rms_norm(x, lw.attn_norm, cfg.rms_eps)
+    pos = np.arange(pos0, pos0 + T)
+    k = (u @ lw.wk.T).reshape(T, cfg.n_kv_heads, d).transpose(1, 0, 2)[None]
+    v = (u @ lw.wv.T).reshape(T, cfg.n_kv_heads, d).transpose(1, 0, 2)[None]
+    k = O.rope_rotate(k, pos, cfg.rope_theta)
+    q = (u[rows] @ lw.wq.T).reshape(len(rows), cfg.n_heads, d).transpose(1, 0, 2)[None]
+    q = O.rope_rotate(q, pos[rows], cfg.rope_theta)
+    o = O.gqa_attention(q, k, v, pos[rows], pos)[0].transpose(1, 0, 2).reshape(len(rows), -1)
+    h = x[rows] + o @ lw.wo.T
+    return h + O.mlp_sublayer(h, lw, cfg)
+
+
+class LazyCache:
+    """Per-layer cache values for the oracle, converted to float64 on access."""
+
+    def __init__(self, tensors, P):
+        self.tensors, self.P = tensors, P
+
+    def __getitem__(self, i):
+        return self.tensors[i].f64[:, :, : self.P]
+
+    def __len__(self):
+        return len(self.tensors)

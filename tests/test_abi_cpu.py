@@ -1,0 +1,174 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/smol.h
+declares, sizes workspaces, and rejects bad arguments before touching the GPU.
+
+No call here reaches a kernel: each one fails a host-side check first (fake,
+never-dereferenced pointers stand in for device buffers)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from llama_decoder_only_amd import binding as B  # noqa: E402
+from llama_decoder_only_amd import synthetic as S  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "smol.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smol_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    declared = _declared_symbols()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(B.EXPORTED) == declared
+
+
+def test_status_strings():
+    assert B.smol_status_string(0) == "ok"
+    assert "workspace" in B.smol_status_string(3)
+    assert B.smol_status_string(99) == "unknown status"
+
+
+def _cfg(**kw):
+    c = B.Config.from_shape(S.workload("prefill_bf16"))
+    d = {k: getattr(c, k) for k in c.__dataclass_fields__}
+    d.update(kw)
+    return B.Config(**d)
+
+
+def _ws(cfg, op, b, t):
+    n = ctypes.c_size_t(0)
+    st = B.lib().smol_workspace_size(ctypes.byref(cfg.c()), op, b, t, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes():
+    cfg = _cfg()
+    st, n1 = _ws(cfg, B.SMOL_OP_PREFILL, 4, 512)
+    assert st == 0 and n1 > 4 * 512 * 576 * 4
+    st, n2 = _ws(cfg, B.SMOL_OP_PREFILL, 8, 512)
+    assert st == 0 and n2 > n1
+    st, n3 = _ws(cfg, B.SMOL_OP_DECODE, 64, 2048)
+    assert st == 0 and n3 > 0
+    st, _ = _ws(cfg, 7, 1, 1)
+    assert st == B.SMOL_ERR_INVALID_ARG
+    st, _ = _ws(cfg, B.SMOL_OP_BLOCK, 0, 1)
+    assert st == B.SMOL_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=577), B.SMOL_ERR_INVALID_ARG),              # hidden != heads * head_dim
+    (dict(n_kv_heads=2), B.SMOL_ERR_INVALID_ARG),            # 9 % 2 != 0
+    (dict(n_kv_heads=1), B.SMOL_ERR_UNSUPPORTED),            # 9 q heads per kv head
+    (dict(head_dim=32, n_heads=18, n_kv_heads=6), B.SMOL_ERR_UNSUPPORTED),
+    (dict(intermediate=1500), B.SMOL_ERR_UNSUPPORTED),
+    (dict(vocab=49153), B.SMOL_ERR_UNSUPPORTED),
+    (dict(rms_eps=-1.0), B.SMOL_ERR_INVALID_ARG),
+    (dict(rope_theta=0.0), B.SMOL_ERR_INVALID_ARG),
+    (dict(n_layers=0), B.SMOL_ERR_INVALID_ARG),
+])
+def test_config_checks(kw, status):
+    st, _ = _ws(_cfg(**kw), B.SMOL_OP_PREFILL, 1, 8)
+    assert st == status, B.smol_last_error()
+    assert B.smol_last_error() != ""
+
+
+def _layer_struct(null=None):
+    return B.smol_layer_weights(*[None if n == null else FAKE for n in B.LAYER_FIELDS])
+
+
+def _block(cfg, w, x_in=FAKE, x_out=FAKE, batch=1, seq=8, pos0=0, kc=None, vc=None, cap=0, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = _ws(cfg, B.SMOL_OP_BLOCK, max(batch, 1), max(seq, 1))[1]
+    return B.lib().smol_block_forward(ctypes.byref(cfg.c()), ctypes.byref(w), x_in, x_out, batch, seq, pos0, kc, vc,
+                                      cap, ws, ws_bytes, None)
+
+
+def test_block_forward_rejects():
+    cfg = _cfg()
+    w = _layer_struct()
+    assert _block(cfg, _layer_struct(null="wk")) == B.SMOL_ERR_INVALID_ARG and "wk" in B.smol_last_error()
+    assert _block(cfg, w, x_in=None) == B.SMOL_ERR_INVALID_ARG
+    assert _block(cfg, w, batch=0) == B.SMOL_ERR_INVALID_ARG
+    assert _block(cfg, w, seq=8193) == B.SMOL_ERR_INVALID_ARG and "max_pos" in B.smol_last_error()
+    assert _block(cfg, w, pos0=8190, seq=8) == B.SMOL_ERR_INVALID_ARG
+    assert _block(cfg, w, pos0=-1) == B.SMOL_ERR_INVALID_ARG
+    assert _block(cfg, w, kc=FAKE, vc=None, cap=16) == B.SMOL_ERR_INVALID_ARG
+    assert _block(cfg, w, kc=FAKE, vc=FAKE, cap=4, seq=8) == B.SMOL_ERR_INVALID_ARG and "cache_cap" in B.smol_last_error()
+    need = _ws(cfg, B.SMOL_OP_BLOCK, 1, 8)[1]
+    assert _block(cfg, w, ws_bytes=need - 1) == B.SMOL_ERR_WORKSPACE
+    assert _block(cfg, w, ws=FAKE + 8) == B.SMOL_ERR_INVALID_ARG and "aligned" in B.smol_last_error()
+    assert _block(cfg, w, ws=None) == B.SMOL_ERR_INVALID_ARG
+    assert B.lib().smol_block_forward(None, ctypes.byref(w), FAKE, FAKE, 1, 8, 0, None, None, 0, FAKE, need,
+                                      None) == B.SMOL_ERR_INVALID_ARG
+
+
+def _model_struct(cfg, null_layer=None):
+    layers = (B.smol_layer_weights * cfg.n_layers)(
+        *[_layer_struct(null="w_down" if i == null_layer else None) for i in range(cfg.n_layers)])
+    m = B.smol_model_weights(FAKE, layers, FAKE)
+    return m, layers
+
+
+def test_model_prefill_rejects():
+    cfg = _cfg()
+    m, keep = _model_struct(cfg)
+    need = _ws(cfg, B.SMOL_OP_PREFILL, 2, 16)[1]
+    call = lambda **k: B.lib().smol_model_prefill(  # noqa: E731
+        ctypes.byref(cfg.c()), ctypes.byref(k.get("m", m)), k.get("ids", FAKE), k.get("b", 2), k.get("t", 16),
+        k.get("logits", FAKE), k.get("kc"), k.get("vc"), k.get("cap", 0), FAKE, k.get("ws_bytes", need), None)
+    assert call(ids=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(logits=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(t=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(t=9000) == B.SMOL_ERR_INVALID_ARG
+    assert call(kc=FAKE, vc=FAKE, cap=8) == B.SMOL_ERR_INVALID_ARG
+    assert call(ws_bytes=need // 2) == B.SMOL_ERR_WORKSPACE
+    m2, keep2 = _model_struct(cfg, null_layer=17)
+    assert call(m=m2) == B.SMOL_ERR_INVALID_ARG and "layer 17" in B.smol_last_error()
+    m3 = B.smol_model_weights(None, keep, FAKE)
+    assert call(m=m3) == B.SMOL_ERR_INVALID_ARG and "embed" in B.smol_last_error()
+
+
+def test_decode_step_rejects():
+    cfg = _cfg()
+    m, keep = _model_struct(cfg)
+    need = _ws(cfg, B.SMOL_OP_DECODE, 64, 2048)[1]
+    call = lambda **k: B.lib().smol_decode_step(  # noqa: E731
+        ctypes.byref(cfg.c()), ctypes.byref(m), k.get("ids", FAKE), k.get("cl", FAKE), k.get("b", 64),
+        k.get("kc", FAKE), k.get("vc", FAKE), k.get("cap", 2048), FAKE, FAKE, k.get("ws_bytes", need), None)
+    assert call(cl=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(kc=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(b=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(cap=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 256) == B.SMOL_ERR_WORKSPACE
+
+
+def test_timing_rejects():
+    L = B.lib()
+    assert L.smol_timing_begin(-1, 4) == B.SMOL_ERR_INVALID_ARG
+    assert L.smol_timing_begin(3, 0) == B.SMOL_ERR_INVALID_ARG
+    assert L.smol_timing_end(None, None) == B.SMOL_ERR_INVALID_ARG
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The binding and the package never reach oracle/ (it is test infrastructure)."""
+    pkg = os.path.join(ROOT, "llama_decoder_only_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                with open(os.path.join(dirpath, f)) as fh:
+                    text = fh.read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "oracle/" not in text and "#include \"oracle" not in text, f

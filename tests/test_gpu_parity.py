@@ -1,0 +1,312 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle on the
+same seeded inputs. fp32: rel <= 1e-4 and bit-exact argmax; bf16: rel <= 2e-2,
+where rel = max|gpu - oracle| / max|oracle| over the compared tensor."""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle.smol as O  # noqa: E402
+from llama_decoder_only_amd import binding as B  # noqa: E402
+from llama_decoder_only_amd import synthetic as S  # noqa: E402
+from tests.gpu_helpers import (TOL_BF16, TOL_F32, LazyCache, block_rows_oracle, ocfg, olayer,  # noqa: E402
+                               omodel, rel, say, to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _ids(s, seed=0):
+    return torch.from_numpy(S.token_ids(s, seed)).to(DEV)
+
+
+def _run_block(s, layer_dev, x_np, pos0=0, kc=None, vc=None):
+    cfg = B.Config.from_shape(s)
+    x = torch.from_numpy(np.ascontiguousarray(x_np, np.float32)).to(DEV)
+    out = torch.empty_like(x)
+    B.smol_block_forward(cfg, layer_dev, x, out, pos0=pos0, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    return out
+
+
+# ------------------------------------------------------------------ one block
+
+
+@pytest.mark.parametrize("name,batch,seq,jitter", [
+    ("block_f32", 1, 128, 0.0),     # the single-block fp32 workload
+    ("block_f32", 2, 100, 0.1),     # ragged tail (M = 200), non-unit norm weights
+    ("block_f32", 3, 1, 0.1),       # one token
+    ("block_f32", 1, 333, 0.0),     # several key tiles plus a ragged one
+])
+def test_block_f32(name, batch, seq, jitter):
+    s = S.workload(name, batch=batch, seq=seq, norm_jitter=jitter)
+    say(f"block f32 B={batch} T={seq}")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.data))
+    want = O.block_forward(x.f64, olayer(layer), ocfg(s))
+    r = rel(got, want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_F32
+
+
+@pytest.mark.parametrize("batch,seq,jitter", [(2, 77, 0.1), (4, 512, 0.0)])
+def test_block_bf16(batch, seq, jitter):
+    s = S.workload("prefill_bf16", n_layers=1, batch=batch, seq=seq, norm_jitter=jitter)
+    say(f"block bf16 B={batch} T={seq}")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.f64))
+    want = O.block_forward(x.f64, olayer(layer), ocfg(s))
+    r = rel(got, want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_BF16
+
+
+def test_block_f32_with_cache_and_offset():
+    """Chunked prefill: positions pos0.. with keys 0..pos0-1 already in the cache."""
+    s = S.workload("block_f32", batch=2, seq=40, norm_jitter=0.1)
+    pos0, cap = 70, 128
+    say("block f32 with cache, pos0=70")
+    layer = S.layer_weights(s, 0, 0)
+    ld = B.upload_layer(layer)
+    x = S.hidden_states(s, 0)
+    past_k = np.random.default_rng(5).standard_normal((2, s.n_kv_heads, pos0, s.head_dim)).astype(np.float32)
+    past_v = np.random.default_rng(6).standard_normal((2, s.n_kv_heads, pos0, s.head_dim)).astype(np.float32)
+    kc = torch.zeros(2, s.n_kv_heads, cap, s.head_dim, device=DEV)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :pos0] = torch.from_numpy(past_k).to(DEV)
+    vc[:, :, :pos0] = torch.from_numpy(past_v).to(DEV)
+    got = to_np(_run_block(s, ld, x.data, pos0=pos0, kc=kc, vc=vc))
+    cfg = ocfg(s)
+    lw = olayer(layer)
+    pos = np.arange(pos0, pos0 + s.seq)
+    attn, k, v = O.attention_sublayer(x.f64, lw, cfg, pos, past_k, past_v, np.arange(pos0))
+    h = x.f64 + attn
+    want = h + O.mlp_sublayer(h, lw, cfg)
+    assert rel(got, want) <= TOL_F32
+    assert rel(to_np(kc[:, :, pos0:pos0 + s.seq]), k) <= TOL_F32
+    assert rel(to_np(vc[:, :, pos0:pos0 + s.seq]), v) <= TOL_F32
+    assert torch.all(kc[:, :, pos0 + s.seq:] == 0)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    """9/3 heads equals 9/9 heads whose k/v projections repeat each kv head 3 times."""
+    s = S.workload("block_f32", batch=2, seq=96)
+    s9 = S.workload("block_f32", batch=2, seq=96, n_kv_heads=9)
+    say("GQA vs MHA")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got3 = to_np(_run_block(s, B.upload_layer(layer), x.data))
+    rep = lambda t: S.Tensor(np.repeat(t.data.reshape(3, 64, -1), 3, axis=0).reshape(576, -1).copy(), t.dtype)  # noqa
+    l9 = S.Layer(**{n: getattr(layer, n) for n in S.Layer.NAMES})
+    l9.wk, l9.wv = rep(layer.wk), rep(layer.wv)
+    got9 = to_np(_run_block(s9, B.upload_layer(l9), x.data))
+    assert rel(got3, got9) <= 1e-5
+
+
+# ------------------------------------------------------------------ whole model
+
+
+def _prefill(s, md, ids, kc=None, vc=None):
+    cfg = B.Config.from_shape(s)
+    logits = torch.empty(ids.shape[0], ids.shape[1], s.vocab, dtype=cfg.torch_dtype, device=DEV)
+    B.smol_model_prefill(cfg, md, ids, logits, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    return logits
+
+
+def test_model_f32_argmax_exact():
+    """The 30-layer model in float32 (batch 1, seq 128): logits within 1e-4, argmax bit-exact."""
+    s = S.workload("model_f32")
+    say("model f32 30 layers B=1 T=128")
+    model = S.model_weights(s, 0)
+    ids_np = S.token_ids(s, 0)
+    got = to_np(_prefill(s, B.upload_model(model), torch.from_numpy(ids_np).to(DEV)))
+    want = O.model_prefill(ids_np, omodel(model), ocfg(s))
+    r = rel(got, want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_F32
+    top2 = np.sort(want, axis=-1)[..., -2:]
+    gap = top2[..., 1] - top2[..., 0]
+    err = np.max(np.abs(got - want))
+    close = gap <= 2 * err
+    say(f"argmax near-ties (gap <= 2*max err): {int(close.sum())}")
+    assert np.array_equal(np.argmax(got, -1)[~close], np.argmax(want, -1)[~close])
+    assert np.array_equal(np.argmax(got, -1), np.argmax(want, -1))
+
+
+@pytest.mark.parametrize("layers,batch,seq", [(3, 2, 130), (2, 1, 1)])
+def test_model_bf16_small(layers, batch, seq):
+    s = S.workload("prefill_bf16", n_layers=layers, batch=batch, seq=seq, norm_jitter=0.1)
+    say(f"model bf16 L={layers} B={batch} T={seq}")
+    model = S.model_weights(s, 0)
+    ids_np = S.token_ids(s, 0)
+    got = to_np(_prefill(s, B.upload_model(model), torch.from_numpy(ids_np).to(DEV)))
+    want = O.model_prefill(ids_np, omodel(model), ocfg(s))
+    r = rel(got, want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_BF16
+
+
+def test_prefill_bf16_full_size_sampled():
+    """The benchmarked prefill (30 layers, batch 4 x seq 512, bf16): sequence 0 against the oracle
+    on 48 sampled rows; all four sequences are run in the launch configuration bench.py times."""
+    s = S.workload("prefill_bf16")
+    say("prefill bf16 B=4 T=512 full size")
+    model = S.model_weights(s, 0)
+    ids_np = S.token_ids(s, 0)
+    md = B.upload_model(model)
+    got = _prefill(s, md, torch.from_numpy(ids_np).to(DEV))
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 511], np.random.default_rng(0).integers(0, 512, 42)]))
+    want = O.model_prefill(ids_np[:1], omodel(model), ocfg(s), logit_rows=rows)
+    g = to_np(got[0, torch.from_numpy(rows).to(DEV)])
+    r = rel(g, want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_BF16
+    assert torch.isfinite(got.float()).all()
+
+
+def test_long_prefill_bf16_properties():
+    """The long-context prefill (batch 1 x seq 8192): the first 96 positions equal the oracle's
+    prefill of that prefix (causality makes them independent of later tokens); perturbing
+    tokens after 5000 leaves rows <= 5000 bit-identical; two runs are bit-identical."""
+    s = S.workload("long_prefill_bf16")
+    say("long prefill bf16 B=1 T=8192")
+    model = S.model_weights(s, 0)
+    md = B.upload_model(model)
+    ids_np = S.token_ids(s, 0)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    a = _prefill(s, md, ids)
+    b = _prefill(s, md, ids)
+    assert torch.equal(a, b), "prefill is not deterministic"
+    ids2 = ids.clone()
+    ids2[:, 5001:] = (ids2[:, 5001:] + 7) % s.vocab
+    c = _prefill(s, md, ids2)
+    assert torch.equal(a[:, :5001], c[:, :5001]), "rows before the perturbation changed"
+    assert not torch.equal(a[:, 5001:], c[:, 5001:])
+    P = 96
+    want = O.model_prefill(ids_np[:, :P], omodel(model), ocfg(s))
+    r = rel(to_np(a[:, :P]), want)
+    say(f"prefix rel = {r:.3e}")
+    assert r <= TOL_BF16
+    del a, b, c
+
+
+def test_long_block_bf16_sampled_rows():
+    """One bf16 block at seq 8192: 40 sampled rows (every key tile of the last row) against the oracle."""
+    s = S.workload("long_prefill_bf16", n_layers=1)
+    say("block bf16 B=1 T=8192 sampled rows")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.f64))
+    rows = np.unique(np.concatenate([[0, 63, 64, 4095, 8190, 8191], np.random.default_rng(1).integers(0, 8192, 34)]))
+    want = block_rows_oracle(x.f64[0], olayer(layer), ocfg(s), rows)
+    r = rel(got[0, rows], want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_BF16
+
+
+# ------------------------------------------------------------------ decode
+
+
+def _decode(s, md, ids, cache_len, kc, vc):
+    cfg = B.Config.from_shape(s)
+    logits = torch.empty(ids.shape[0], s.vocab, dtype=cfg.torch_dtype, device=DEV)
+    B.smol_decode_step(cfg, md, ids, cache_len, kc, vc, logits)
+    torch.cuda.synchronize()
+    return logits
+
+
+def test_decode_f32_equals_prefill():
+    """Decode at position P after a prefill of P tokens equals the prefill of P+1 tokens at P."""
+    s = S.workload("model_f32", n_layers=3, batch=3, seq=51, norm_jitter=0.1)
+    say("decode f32 vs prefill")
+    model = S.model_weights(s, 0)
+    md = B.upload_model(model)
+    ids_np = S.token_ids(s, 0)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    P, cap = 50, 64
+    kc = torch.zeros(s.n_layers, 3, s.n_kv_heads, cap, s.head_dim, device=DEV)
+    vc = torch.zeros_like(kc)
+    s_p = S.workload("model_f32", n_layers=3, batch=3, seq=P, norm_jitter=0.1)
+    _prefill(s_p, md, ids[:, :P].contiguous(), kc, vc)
+    cl = torch.full((3,), P, dtype=torch.int32, device=DEV)
+    got = to_np(_decode(s, md, ids[:, P].contiguous(), cl, kc, vc))
+    full = to_np(_prefill(s, md, ids))[:, P]
+    assert rel(got, full) <= TOL_F32
+    want = O.model_prefill(ids_np, omodel(model), ocfg(s))[:, P]
+    assert rel(got, want) <= TOL_F32
+
+
+def test_decode_bf16_full_size():
+    """The benchmarked decode step: batch 64, 2047 cached positions (N(0,1) bf16), 30 layers."""
+    s = S.workload("decode_bf16")
+    say("decode bf16 B=64 P=2047 full size")
+    model = S.model_weights(s, 0)
+    md = B.upload_model(model)
+    P, cap = s.cache_len, 2048
+    ks, vs = [], []
+    kc = torch.empty(s.n_layers, s.batch, s.n_kv_heads, cap, s.head_dim, dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    for l in range(s.n_layers):
+        k, v = S.kv_cache_values(s, 0, l, cap)
+        ks.append(k)
+        vs.append(v)
+        kc[l] = B.to_device(k)
+        vc[l] = B.to_device(v)
+    ids_np = S.token_ids(s, 0, S.T_DECODE_IDS)[:, 0]
+    ids = torch.from_numpy(ids_np.copy()).to(DEV)
+    cl = torch.full((s.batch,), P, dtype=torch.int32, device=DEV)
+    got = to_np(_decode(s, md, ids, cl, kc, vc))
+    say("oracle decode")
+    want, nk, nv = O.decode_step(ids_np, P, omodel(model), ocfg(s), LazyCache(ks, P), LazyCache(vs, P))
+    r = rel(got, want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_BF16
+    for l in (0, 17, 29):
+        assert rel(to_np(kc[l, :, :, P]), nk[l]) <= TOL_BF16
+        assert rel(to_np(vc[l, :, :, P]), nv[l]) <= TOL_BF16
+    assert torch.equal(kc[5, :, :, :P], B.to_device(ks[5])[:, :, :P])
+
+
+def test_decode_invalid_cache_len_gives_nan_and_no_write():
+    s = S.workload("model_f32", n_layers=2, batch=3, seq=1)
+    say("decode invalid cache_len")
+    md = B.upload_model(S.model_weights(s, 0))
+    cap = 16
+    kc = torch.zeros(2, 3, s.n_kv_heads, cap, s.head_dim, device=DEV)
+    vc = torch.zeros_like(kc)
+    cl = torch.tensor([4, cap, -1], dtype=torch.int32, device=DEV)
+    ids = torch.tensor([1, 2, 3], dtype=torch.int32, device=DEV)
+    out = _decode(s, md, ids, cl, kc, vc)
+    assert torch.isfinite(out[0]).all()
+    assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
+    assert torch.all(kc[:, 1:] == 0) and torch.all(vc[:, 1:] == 0)
+    assert torch.any(kc[:, 0, :, 4] != 0)
+
+
+def test_prefill_invalid_id_poisons_only_its_sequence():
+    """An id outside [0, vocab) turns its sequence's logits NaN from that position on;
+    the other sequences are bit-identical to a clean run."""
+    s = S.workload("model_f32", n_layers=2, batch=2, seq=20)
+    say("prefill invalid id")
+    md = B.upload_model(S.model_weights(s, 0))
+    ids = _ids(s)
+    good = _prefill(s, md, ids)
+    bad_ids = ids.clone()
+    bad_ids[1, 5] = -3
+    bad = _prefill(s, md, bad_ids)
+    assert torch.equal(good[0], bad[0])
+    assert torch.isnan(bad[1, 5:]).all()
