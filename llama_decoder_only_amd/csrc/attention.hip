@@ -107,6 +107,7 @@ attn_prefill_kernel(const AttnArgs a) {
   for (int kt = 0; kt < ntiles; ++kt) {
     const int cur = kt & 1;
     fetch(min(kt + 1, ntiles - 1));  // branch-free prefetch (the last one is a harmless re-read)
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before this tile's math
     const int k0 = kt * BKV;
     if (wave_live && k0 <= wave_kmax) {
       f32x16 s[2] = {(f32x16){}, (f32x16){}};
@@ -164,6 +165,7 @@ attn_prefill_kernel(const AttnArgs a) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     stash(cur ^ 1);
     __syncthreads();
   }

@@ -108,6 +108,16 @@ template <> __device__ __forceinline__ f16 chunk_elem<f16>(const Chunk16 &c, int
   return __builtin_bit_cast(f16, (uint16_t)(c[e >> 1] >> ((e & 1) * 16)));
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS byte address lds_base + 16 * l, lds_base wave-uniform.
+// Issued through inline asm so the compiler adds no waits of its own: the caller
+// waits with wait_vmcnt<N>() and a barrier before anyone reads the data.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
+
 // Convert a staged chunk from storage type W to operand type Act<W> (same size).
 template <typename W> __device__ __forceinline__ Chunk16 to_operand(const Chunk16 &c) { return c; }
 template <> __device__ __forceinline__ Chunk16 to_operand<bf16>(const Chunk16 &c) {

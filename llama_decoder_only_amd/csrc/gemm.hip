@@ -3,18 +3,24 @@
 // Both operands are K-contiguous (activations row-major, weights [out, in] as the
 // linear layers store them), so every lane reads 8 consecutive K values of one
 // row for a 32x32x16 MFMA step. Weight rows arrive in the storage type W and are
-// converted to the activations' operand type Act<W> on their way into LDS. A
-// workgroup owns a BM x BN tile; its waves each own (32*TM) x (32*TN). K is staged through LDS 128 bytes per row at a time,
-// double-buffered: the next stage is fetched into registers while the current
-// one feeds the MFMAs.
+// converted to the activations' operand type Act<W> as their fragments leave LDS.
 //
-// Epilogues (what the five projections of a block and the head need):
-//   EPI_STORE     C = acc                       lm_head logits (float or the storage type)
-//   EPI_RESIDUAL  X += acc (float X)            o_proj and down_proj with residual add
-//   EPI_SWIGLU    Y = silu(gate) * up           gate/up projection; B rows interleave
-//                                               32 gate rows then 32 up rows
-//   EPI_QKV_ROPE  q, k rotated at their position, q stored [M, n_heads*d];
-//                 k, v stored into the [B, n_kv, cap, d] cache at their index.
+// A workgroup of four waves (2 x 2) owns a BM x BN tile; K is staged through an
+// S-deep ring of LDS stages, 128 bytes per row each, filled by direct global->LDS
+// copies (no register staging) that run S-1 stages ahead of the MFMAs; one barrier
+// per stage hands a filled slot to all waves and frees the slot just consumed.
+// Weight fragments are converted from W to the operand type as they leave LDS.
+// When the K loop ends, the
+// float accumulators go to LDS (reusing the staging buffers) and the epilogue
+// walks the tile row-major, so every global write is a contiguous 8- or 16-byte
+// vector and each epilogue sees whole rows of the tile:
+//   EPI_STORE     C = acc                          lm_head logits
+//   EPI_RESIDUAL  X += acc (float X)               o_proj / down_proj + residual
+//   EPI_SWIGLU    Y = silu(gate) * up              gate/up projection: tile columns
+//                                                  [0, BN/2) read gate rows and
+//                                                  [BN/2, BN) the matching up rows
+//   EPI_QKV_ROPE  q, k rotated at their position, q stored [M, n_heads*d]; k, v
+//                 stored into the [B, n_kv, cap, d] cache at their index.
 // Projection math: abi96062 components.py (GroupedQueryAttention, SwiGLU_FFN);
 // RoPE pairs (i, i + d/2): Sualeh77 model.py, "3. RoPE".
 #include "common.h"
@@ -38,13 +44,15 @@ struct GemmParams {
   float inv_freq[64];
 };
 
-template <typename W, int EPI>
+// Source row of logical B column n.
+template <typename W, int EPI, int BN>
 __device__ __forceinline__ const W *b_row(const GemmParams &p, int n) {
-  if (EPI == EPI_SWIGLU) {
-    const int c = n & 63;
-    const int r = ((n >> 6) << 5) + (c & 31);
-    return (c < 32 ? (const W *)p.B0 : (const W *)p.B1) + (size_t)r * p.K;
-  } else if (EPI == EPI_QKV_ROPE) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    constexpr int HB = BN / 2;
+    const int c = n % BN;
+    const int r = (n / BN) * HB + (c % HB);
+    return (c < HB ? (const W *)p.B0 : (const W *)p.B1) + (size_t)r * p.K;
+  } else if constexpr (EPI == EPI_QKV_ROPE) {
     if (n < p.nq_cols) return (const W *)p.B0 + (size_t)n * p.K;
     n -= p.nq_cols;
     if (n < p.nkv_cols) return (const W *)p.B1 + (size_t)n * p.K;
@@ -56,70 +64,94 @@ __device__ __forceinline__ const W *b_row(const GemmParams &p, int n) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <typename W, int TM, int TN, int WAVES_M, int WAVES_N, int EPI>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
-gemm_kernel(const GemmParams p) {
-  using T = Act<W>;  // MFMA operand type; B rows are converted from W while staged
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int BM = 32 * TM * WAVES_M;
-  constexpr int BN = 32 * TN * WAVES_N;
-  constexpr int EPC = 16 / sizeof(T);           // elements per 16-byte chunk
-  constexpr int BK = 128 / sizeof(T);           // K elements per stage (128 bytes per row)
-  constexpr int PITCH = BK + EPC;               // padded LDS row (144 bytes)
-  constexpr int KSTEPS = BK / 16;
-  constexpr int A_CH = BM * 8 / NT;             // 16-byte chunks per thread per stage
-  constexpr int B_CH = BN * 8 / NT;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile/thread mismatch");
+// Store N (4 or 8) consecutive floats as type O.
+template <typename O, int N>
+__device__ __forceinline__ void store_vec(O *dst, const float *v) {
+  if constexpr (sizeof(O) == 2 && N == 8) {
+    Chunk16 c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      c[i] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i])) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i + 1])) << 16);
+    st16(dst, c);
+  } else if constexpr (sizeof(O) == 2 && N == 4) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 c;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      c[i] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i])) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i + 1])) << 16);
+    *reinterpret_cast<u32x2 *>(dst) = c;
+  } else {
+    static_assert(sizeof(O) == 4, "float output");
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<f32x4 *>((float *)dst + i) = (f32x4){v[i], v[i + 1], v[i + 2], v[i + 3]};
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) T smem[2][(BM + BN) * PITCH];
+// Fragment of 8 consecutive K values of one row from a swizzled LDS stage row:
+// 16-byte chunk c of row r sits at slot c ^ (r & 7) (see gemm_kernel).
+template <typename T>
+__device__ __forceinline__ Chunk16 lds_chunk(const char *row, int c, int sw) {
+  return *reinterpret_cast<const Chunk16 *>(row + ((c ^ sw) << 4));
+}
+
+template <typename W, int BM, int BN, int EPI, int S>
+__global__ void __launch_bounds__(256)
+gemm_kernel(const GemmParams p) {
+  using T = Act<W>;  // MFMA operand type; weight fragments convert from W as they are read
+  static_assert(sizeof(T) == sizeof(W), "storage and operand types have the same width");
+  constexpr int NT = 256;
+  constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 MFMA tiles per wave (2 x 2 waves)
+  constexpr int ROWS = BM + BN;              // LDS rows per stage: A rows, then B rows
+  constexpr int STAGE_BYTES = ROWS * 128;    // 128 bytes of K per row per stage
+  constexpr int IPW = ROWS / 32;             // DMA instructions per wave per stage (8 rows each)
+  constexpr int KE = 128 / sizeof(T);        // K elements per stage
+  constexpr int KSTEPS = KE / 16;
+  constexpr int CPF = 16 * sizeof(T) / 16 / 2;  // 16-byte chunks per 8-element fragment (1 or 2)
+  constexpr int OP = BN + 4;                 // float pitch of the epilogue tile
+  // The epilogue walks the tile in row chunks of ER rows that fit the staging LDS.
+  constexpr int ER = (BM * OP * 4 <= S * STAGE_BYTES) ? BM : 32 * TM;
+  static_assert(ER * OP * 4 <= S * STAGE_BYTES, "epilogue chunk must fit the staging LDS");
+  static_assert(S >= 2, "at least double buffering");
+
+  __shared__ __attribute__((aligned(16))) char smem[S * STAGE_BYTES];
+  float *tile = reinterpret_cast<float *>(smem);
+  const uint32_t smem_base = lds_addr(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int wm = wave & 1, wn = wave >> 1;
 
-  // XCD-aware tile order: consecutive workgroups land on different XCDs, so give
-  // neighbouring N tiles (which share the A rows) to the same XCD's L2.
+  // XCD-aware tile order: workgroup i runs on XCD i % 8, so hand each XCD a
+  // contiguous range of tiles; consecutive tiles share their B (weight) columns.
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int tiles_n = p.N / BN;
-  const int ntiles = tiles_m * tiles_n;
+  const int ntiles = tiles_m * (p.N / BN);
   int bid = blockIdx.x;
   if (ntiles % 8 == 0) bid = (bid % 8) * (ntiles / 8) + bid / 8;
   const int tm = bid % tiles_m, tn = bid / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // per-thread global source pointers (fixed rows, K advances)
-  const T *a_src[A_CH];
-  const W *b_src[B_CH];
-  int a_dst[A_CH], b_dst[B_CH];
+  // DMA sources. Wave w's instruction j fills rows 8*(w*IPW + j) .. +7 of a stage;
+  // lane l writes slot l % 8 of row 8*(..) + l / 8 and so fetches the row's 16-byte
+  // chunk (l % 8) ^ (row & 7): an XOR swizzle that keeps fragment reads (32 rows,
+  // one chunk each) free of bank conflicts without padding.
+  const char *src[IPW];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT;
-    const int r = c >> 3, k = (c & 7) * EPC;
-    const int gr = min(m0 + r, p.M - 1);
-    a_src[i] = (const T *)p.A + (size_t)gr * p.lda + k;
-    a_dst[i] = r * PITCH + k;
+  for (int j = 0; j < IPW; ++j) {
+    const int r = 8 * (wave * IPW + j) + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    if (r < BM)
+      src[j] = (const char *)((const T *)p.A + (size_t)min(m0 + r, p.M - 1) * p.lda) + c * 16;
+    else
+      src[j] = (const char *)b_row<W, EPI, BN>(p, n0 + r - BM) + c * 16;
   }
+  auto issue = [&](int stage, int slot) {
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * NT;
-    const int r = c >> 3, k = (c & 7) * EPC;
-    b_src[i] = b_row<W, EPI>(p, n0 + r) + k;
-    b_dst[i] = (BM + r) * PITCH + k;
-  }
-
-  Chunk16 ra[A_CH], rb[B_CH];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = ld16(a_src[i] + k0);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = ld16(b_src[i] + k0);
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) st16(&smem[buf][a_dst[i]], ra[i]);
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) st16(&smem[buf][b_dst[i]], to_operand<W>(rb[i]));
+    for (int j = 0; j < IPW; ++j)
+      lds_dma16(src[j] + stage * 128, smem_base + slot * STAGE_BYTES + (8 * (wave * IPW + j)) * 128);
   };
 
   f32x16 acc[TM][TN];
@@ -128,108 +160,139 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
-  const int nk = p.K / BK;
-  fetch(0);
-  stash(0);
-  __syncthreads();
+  const int nk = p.K / KE;
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) issue(st, st);
 
-  const int frag_row = lane & 31;
-  const int frag_k = (lane >> 5) * 8;
+  const int sw = lane & 7;  // row & 7 for every fragment row this lane reads
+  const int half = lane >> 5;
   for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    // Prefetch the next stage (the last iteration re-reads the final stage into the
-    // idle buffer: a branch-free loop keeps the prefetch registers out of scratch).
-    fetch(min(kb + 1, nk - 1) * BK);
-    const T *sa = &smem[cur][(wm * 32 * TM + frag_row) * PITCH + frag_k];
-    const T *sb = &smem[cur][(BM + wn * 32 * TN + frag_row) * PITCH + frag_k];
+    // stage kb has landed (for this wave) once at most S-2 later stages are pending
+    if (kb + S - 2 < nk)
+      wait_vmcnt<(S - 2) * IPW>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // ... and for every wave; also all reads of stage kb-1 are done
+    if (kb + S - 1 < nk) issue(kb + S - 1, (kb + S - 1) % S);  // refill the slot of stage kb-1
+    const char *sa = smem + (kb % S) * STAGE_BYTES + (wm * 32 * TM + (lane & 31)) * 128;
+    const char *sb = smem + (kb % S) * STAGE_BYTES + (BM + wn * 32 * TN + (lane & 31)) * 128;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       Frag<T> fa[TM], fb[TN];
+      const int c0 = (2 * s + half) * CPF;  // first chunk of this lane's 8 K values
 #pragma unroll
-      for (int i = 0; i < TM; ++i) load_frag(fa[i], sa + i * 32 * PITCH + s * 16);
+      for (int i = 0; i < TM; ++i) {
+        const char *row = sa + i * 32 * 128;
+        if constexpr (CPF == 1) {
+          const Chunk16 c = lds_chunk<T>(row, c0, sw);
+          fa[i].v = __builtin_bit_cast(decltype(fa[i].v), c);
+        } else {
+          const Chunk16 lo = lds_chunk<T>(row, c0, sw), hi = lds_chunk<T>(row, c0 + 1, sw);
+          fa[i].v = (f32x8){__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]), __uint_as_float(lo[3]),
+                            __uint_as_float(hi[0]), __uint_as_float(hi[1]), __uint_as_float(hi[2]), __uint_as_float(hi[3])};
+        }
+      }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) load_frag(fb[j], sb + j * 32 * PITCH + s * 16);
+      for (int j = 0; j < TN; ++j) {
+        const char *row = sb + j * 32 * 128;
+        if constexpr (CPF == 1) {
+          const Chunk16 c = to_operand<W>(lds_chunk<W>(row, c0, sw));
+          fb[j].v = __builtin_bit_cast(decltype(fb[j].v), c);
+        } else {
+          const Chunk16 lo = lds_chunk<W>(row, c0, sw), hi = lds_chunk<W>(row, c0 + 1, sw);
+          fb[j].v = (f32x8){__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]), __uint_as_float(lo[3]),
+                            __uint_as_float(hi[0]), __uint_as_float(hi[1]), __uint_as_float(hi[2]), __uint_as_float(hi[3])};
+        }
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) mma_32x32x16(acc[i][j], fa[i], fb[j]);
     }
-    stash(cur ^ 1);
-    __syncthreads();
   }
+  __syncthreads();  // every wave is done reading the stages: the epilogue tile reuses them
 
-  // ------------------------------------------------------------ epilogue
-  const int col_in_tile = lane & 31;
-  const int wrow0 = m0 + wm * 32 * TM;
-  const int wcol0 = n0 + wn * 32 * TN;
-
-  if constexpr (EPI == EPI_STORE) {
+  // ------------------------------------------------------------ accumulators -> LDS
+  // Row chunk ec holds tile rows [ec*ER, ec*ER + ER): the waves whose rows fall in it
+  // write their accumulators, then the epilogue walks those rows.
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int ec = 0; ec < BM / ER; ++ec) {
+    const int r_lo = ec * ER;
+    if (ER == BM || wm == ec) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wrow0 + i * 32 + acc_row(r, lane);
-        if (row >= p.M) continue;
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = wcol0 + j * 32 + col_in_tile;
-          if (p.c_f32)
-            ((float *)p.C)[(size_t)row * p.ldc + col] = acc[i][j][r];
-          else
-            ((W *)p.C)[(size_t)row * p.ldc + col] = from_f32<W>(acc[i][j][r]);
-        }
-      }
-  } else if constexpr (EPI == EPI_RESIDUAL) {
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wrow0 + i * 32 + acc_row(r, lane);
-        if (row >= p.M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          float *x = (float *)p.C + (size_t)row * p.ldc + wcol0 + j * 32 + col_in_tile;
-          *x = *x + acc[i][j][r];
-        }
-      }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    static_assert(TN % 2 == 0, "gate/up pairs");
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wrow0 + i * 32 + acc_row(r, lane);
-        if (row >= p.M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; j += 2) {
-          const int n = wcol0 + j * 32;             // logical column of the gate tile (multiple of 64)
-          const int col = (n >> 1) + col_in_tile;   // output column
-          const float g = acc[i][j][r], u = acc[i][j + 1][r];
-          ((T *)p.C)[(size_t)row * p.ldc + col] = from_f32<T>(silu(g) * u);
-        }
-      }
-  } else if constexpr (EPI == EPI_QKV_ROPE) {
-    // The wave's 32*TN columns are one head (TN*32 == head_dim): column e and e + d/2
-    // sit in tiles j and j + TN/2 of the same lane.
-    constexpr int HALF = TN / 2;
-    const int D = 32 * TN;
-    int kind, head;  // 0 = q, 1 = k, 2 = v
-    if (wcol0 < p.nq_cols) {
-      kind = 0;
-      head = wcol0 / D;
-    } else if (wcol0 < p.nq_cols + p.nkv_cols) {
-      kind = 1;
-      head = (wcol0 - p.nq_cols) / D;
-    } else {
-      kind = 2;
-      head = (wcol0 - p.nq_cols - p.nkv_cols) / D;
+          for (int r = 0; r < 16; ++r)
+            tile[(wm * 32 * TM + i * 32 + acc_row(r, lane) - r_lo) * OP + wn * 32 * TN + j * 32 + (lane & 31)] =
+                acc[i][j][r];
     }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wrow0 + i * 32 + acc_row(r, lane);
+    __syncthreads();
+    const int em0 = m0 + r_lo;  // first global row of this chunk
+
+    // ------------------------------------------------------------ epilogue (row-major walk)
+    if constexpr (EPI == EPI_STORE) {
+      if (p.c_f32 || sizeof(W) == 4) {
+        constexpr int V = 4;
+        for (int it = tid; it < ER * BN / V; it += NT) {
+          const int r = it / (BN / V), c = (it % (BN / V)) * V;
+          if (em0 + r >= p.M) continue;
+          store_vec<float, V>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, &tile[r * OP + c]);
+        }
+      } else {
+        constexpr int V = 8;
+        for (int it = tid; it < ER * BN / V; it += NT) {
+          const int r = it / (BN / V), c = (it % (BN / V)) * V;
+          if (em0 + r >= p.M) continue;
+          if constexpr (sizeof(W) == 2) store_vec<W, V>((W *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, &tile[r * OP + c]);
+        }
+      }
+    } else if constexpr (EPI == EPI_RESIDUAL) {
+      constexpr int V = 4;
+      for (int it = tid; it < ER * BN / V; it += NT) {
+        const int r = it / (BN / V), c = (it % (BN / V)) * V;
+        if (em0 + r >= p.M) continue;
+        f32x4 *x = reinterpret_cast<f32x4 *>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c);
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(&tile[r * OP + c]);
+        *x = *x + t;
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int HB = BN / 2;
+      constexpr int V = 16 / sizeof(T);
+      static_assert(HB % V == 0, "output row segment");
+      for (int it = tid; it < ER * HB / V; it += NT) {
+        const int r = it / (HB / V), c = (it % (HB / V)) * V;
+        if (em0 + r >= p.M) continue;
+        float y[V];
+  #pragma unroll
+        for (int e = 0; e < V; ++e) y[e] = silu(tile[r * OP + c + e]) * tile[r * OP + HB + c + e];
+        store_vec<T, V>((T *)p.C + (size_t)(em0 + r) * p.ldc + n0 / 2 + c, y);
+      }
+    } else if constexpr (EPI == EPI_QKV_ROPE) {
+      // Items: (row, head within the tile, 4 consecutive dims e0.. of the first half);
+      // each item rotates the pairs (e, e + d/2) for its 4 dims.
+      const int D = p.head_dim, HALF = D / 2;
+      const int heads = BN / D;
+      const int per_row = heads * (HALF / 4);
+      for (int it = tid; it < ER * per_row; it += NT) {
+        const int r = it / per_row, rem = it % per_row;
+        const int hi = rem / (HALF / 4), e0 = (rem % (HALF / 4)) * 4;
+        const int row = em0 + r;
         if (row >= p.M) continue;
+        const int ncol = n0 + hi * D;  // first column of this head
+        int kind, head;                // 0 = q, 1 = k, 2 = v
+        if (ncol < p.nq_cols) {
+          kind = 0;
+          head = ncol / D;
+        } else if (ncol < p.nq_cols + p.nkv_cols) {
+          kind = 1;
+          head = (ncol - p.nq_cols) / D;
+        } else {
+          kind = 2;
+          head = (ncol - p.nq_cols - p.nkv_cols) / D;
+        }
         int b, pos, idx;
         bool valid = true;
         if (p.cache_len) {
@@ -242,62 +305,61 @@ gemm_kernel(const GemmParams p) {
           pos = p.pos0 + (row - b * p.seq);
           idx = pos - p.kv_off;
         }
-        float z[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) z[j] = acc[i][j][r];
+        const float *t = &tile[r * OP + hi * D];
+        float lo[4], up[4];
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = t[e0 + e];
+          up[e] = t[HALF + e0 + e];
+        }
         if (kind != 2) {
-#pragma unroll
-          for (int j = 0; j < HALF; ++j) {
-            const int e = j * 32 + col_in_tile;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
             float s, c;
-            sincosf((float)pos * p.inv_freq[e], &s, &c);
-            const float a = z[j], bb = z[j + HALF];
-            z[j] = a * c - bb * s;
-            z[j + HALF] = bb * c + a * s;
+            sincosf((float)pos * p.inv_freq[e0 + e], &s, &c);
+            const float a = lo[e], bb = up[e];
+            lo[e] = a * c - bb * s;
+            up[e] = bb * c + a * s;
           }
         }
         if (kind == 0) {
-          T *q = (T *)p.q_out + (size_t)row * p.nq_cols + head * D + col_in_tile;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) q[j * 32] = from_f32<T>(z[j]);
+          T *q = (T *)p.q_out + (size_t)row * p.nq_cols + head * D;
+          store_vec<T, 4>(q + e0, lo);
+          store_vec<T, 4>(q + HALF + e0, up);
         } else if (valid) {
-          W *dst = (W *)(kind == 1 ? p.k_out : p.v_out) +
-                   (((size_t)b * p.n_kv + head) * p.cap + idx) * D + col_in_tile;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) dst[j * 32] = from_f32<W>(z[j]);
+          W *dst = (W *)(kind == 1 ? p.k_out : p.v_out) + (((size_t)b * p.n_kv + head) * p.cap + idx) * D;
+          store_vec<W, 4>(dst + e0, lo);
+          store_vec<W, 4>(dst + HALF + e0, up);
         }
       }
+    }
+    __syncthreads();  // the next chunk overwrites the tile
   }
 }
 
 // ---------------------------------------------------------------- launchers
 
-template <typename W, int TM, int TN, int WM, int WN, int EPI>
+template <typename W, int BM, int BN, int EPI, int S>
 static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
-  constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-  if (p.N % BN != 0) return hipErrorInvalidValue;
+  if (p.N % BN != 0 || p.K % (128 / (int)sizeof(W)) != 0) return hipErrorInvalidValue;
   const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
-  hipLaunchKernelGGL((gemm_kernel<W, TM, TN, WM, WN, EPI>), dim3(tiles), dim3(64 * WM * WN), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<W, BM, BN, EPI, S>), dim3(tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-// Tile choice: 128x128 when N allows it and the grid still fills the chip, else
-// narrower tiles; the QKV epilogue needs the wave's N extent to equal head_dim.
+// Tile choice (measured on MI355X over the model's shapes: a 2-stage ring was never
+// slower than 3 or 4 stages): 128 x 128 when that still gives >= 2 workgroups per
+// CU (lm_head), else 128 x 64 under the same rule (gate/up), else 64 x 64 for
+// parallelism on small N (o_proj, down, QKV, every decode GEMM); 64 x 128 when a
+// 128-wide head must stay in one tile for RoPE.
 template <typename T, int EPI>
 static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
-  if constexpr (EPI == EPI_QKV_ROPE) {
-    if (p.head_dim == 64) {
-      if (p.M <= 64) return launch_cfg<T, 1, 2, 1, 1, EPI>(p, s);
-      return launch_cfg<T, 2, 2, 2, 1, EPI>(p, s);
-    }
-    if (p.M <= 64) return launch_cfg<T, 1, 4, 1, 1, EPI>(p, s);
-    return launch_cfg<T, 2, 4, 2, 1, EPI>(p, s);
-  } else {
-    const long big_tiles = (long)((p.M + 127) / 128) * (p.N / 128);
-    if (p.N % 128 == 0 && p.M > 64 && big_tiles >= 256) return launch_cfg<T, 2, 2, 2, 2, EPI>(p, s);
-    if (p.M <= 64) return launch_cfg<T, 1, 2, 2, 1, EPI>(p, s);
-    return launch_cfg<T, 2, 2, 2, 1, EPI>(p, s);
-  }
+  const long tm128 = (p.M + 127) / 128;
+  const long t128 = (p.N % 128 == 0) ? tm128 * (p.N / 128) : 0;
+  if (t128 >= 512) return launch_cfg<T, 128, 128, EPI, 2>(p, s);
+  if (EPI == EPI_QKV_ROPE && p.head_dim == 128) return launch_cfg<T, 64, 128, EPI, 2>(p, s);
+  if (tm128 * (p.N / 64) >= 512) return launch_cfg<T, 128, 64, EPI, 2>(p, s);
+  return launch_cfg<T, 64, 64, EPI, 2>(p, s);
 }
 
 template <typename T>

@@ -10,7 +10,9 @@ namespace smol {
 
 constexpr int NORM_ROWS = 4;  // rows (waves) per workgroup
 
-template <typename T, typename O, int VEC>
+// VPL = H / 64 values per lane when known at compile time (the row stays in
+// registers and all its loads are in flight at once); VPL = 0 is the generic path.
+template <typename T, typename O, int VPL>
 __global__ void __launch_bounds__(64 * NORM_ROWS)
 rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ w, O *__restrict__ out, int M, int H, float eps) {
   const int lane = threadIdx.x & 63;
@@ -18,27 +20,28 @@ rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ w, O *__restri
   if (row >= M) return;
   const float *xr = x + (size_t)row * H;
   O *orow = out + (size_t)row * H;
-  float ss = 0.f;
-  if constexpr (VEC == 4) {
-    for (int i = lane * 4; i < H; i += 256) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + i);
-      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  if constexpr (VPL > 0) {
+    float v[VPL], wv[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      v[j] = xr[lane + 64 * j];
+      wv[j] = to_f32(w[lane + 64 * j]);
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) ss += v[j] * v[j];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) orow[lane + 64 * j] = from_f32<O>(wv[j] * (v[j] * r));
   } else {
+    float ss = 0.f;
     for (int i = lane; i < H; i += 64) {
       const float v = xr[i];
       ss += v * v;
     }
-  }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)H + eps);
-  if constexpr (VEC == 4) {
-    for (int i = lane * 4; i < H; i += 256) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) orow[i + j] = from_f32<O>(to_f32(w[i + j]) * (v[j] * r));
-    }
-  } else {
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)H + eps);
     for (int i = lane; i < H; i += 64) orow[i] = from_f32<O>(to_f32(w[i]) * (xr[i] * r));
   }
 }
@@ -46,10 +49,11 @@ rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ w, O *__restri
 template <typename T>
 hipError_t rmsnorm(const float *x, const T *w, Act<T> *out, int M, int H, float eps, hipStream_t s) {
   const dim3 grid((M + NORM_ROWS - 1) / NORM_ROWS), block(64 * NORM_ROWS);
-  if (H % 256 == 0)
-    hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 4>), grid, block, 0, s, x, w, out, M, H, eps);
-  else
-    hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 1>), grid, block, 0, s, x, w, out, M, H, eps);
+  switch (H) {
+    case 576: hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 9>), grid, block, 0, s, x, w, out, M, H, eps); break;
+    case 2048: hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 32>), grid, block, 0, s, x, w, out, M, H, eps); break;
+    default: hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 0>), grid, block, 0, s, x, w, out, M, H, eps); break;
+  }
   return hipGetLastError();
 }
 
@@ -66,6 +70,7 @@ embed_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, float *__
     return;
   }
   const T *er = E + (size_t)id * H;
+#pragma unroll 8
   for (int i = lane; i < H; i += 64) xr[i] = to_f32(er[i]);
 }
 

@@ -74,6 +74,41 @@ def test_block_bf16(batch, seq, jitter):
     assert r <= TOL_BF16
 
 
+@pytest.mark.parametrize("dtype,hidden,heads,kv,inter,tol", [
+    ("f32", 640, 10, 5, 1280, TOL_F32),     # generic hidden size (no unrolled RMSNorm), G = 2
+    ("bf16", 640, 10, 5, 1280, TOL_BF16),
+    ("f32", 512, 4, 1, 1024, TOL_F32),      # head_dim 128, G = 4
+    ("bf16", 512, 4, 1, 1024, TOL_BF16),
+])
+def test_block_other_shapes(dtype, hidden, heads, kv, inter, tol):
+    base = "block_f32" if dtype == "f32" else "prefill_bf16"
+    s = S.workload(base, n_layers=1, batch=2, seq=150, hidden=hidden, n_heads=heads, n_kv_heads=kv,
+                   head_dim=hidden // heads, intermediate=inter, norm_jitter=0.1)
+    say(f"block {dtype} H={hidden} heads={heads}/{kv} d={hidden // heads}")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.f64))
+    want = O.block_forward(x.f64, olayer(layer), ocfg(s))
+    r = rel(got, want)
+    say(f"rel = {r:.3e}")
+    assert r <= tol
+
+
+def test_smollm3_shaped_two_layers_bf16():
+    """The SmolLM3-3B shape (H 2048, 16/4 heads x 128, I 11008, vocab 128256, eps 1e-6) with 2 of its
+    36 layers, batch 1 x seq 200, sampled logit rows against the oracle."""
+    s = S.workload("smollm3_prefill_bf16", n_layers=2, batch=1, seq=200, norm_jitter=0.1)
+    say("SmolLM3-shaped 2 layers bf16 B=1 T=200")
+    model = S.model_weights(s, 0)
+    ids_np = S.token_ids(s, 0)
+    got = _prefill(s, B.upload_model(model), torch.from_numpy(ids_np).to(DEV))
+    rows = np.array([0, 1, 63, 64, 127, 128, 150, 199])
+    want = O.model_prefill(ids_np, omodel(model), ocfg(s), logit_rows=rows)
+    r = rel(to_np(got[0, torch.from_numpy(rows).to(DEV)]), want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_BF16
+
+
 def test_block_f32_with_cache_and_offset():
     """Chunked prefill: positions pos0.. with keys 0..pos0-1 already in the cache."""
     s = S.workload("block_f32", batch=2, seq=40, norm_jitter=0.1)
