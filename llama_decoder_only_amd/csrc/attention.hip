@@ -9,11 +9,13 @@
 // tile of K and V is staged in LDS once and read by all G heads, so the group's
 // K/V are fetched once instead of G times (no repeat_interleave copy).
 //
+// K and V tiles stream through an S-deep LDS ring filled by direct global->LDS
+// copies in their cache layout ([key][d], 16-byte chunks XOR-swizzled per row).
 // A wave computes S^T = K . Q^T with 32x32x16 MFMAs, so its lane holds one query
 // (lane % 32) and half of that query's keys in registers: the row max / sum of
 // the online softmax needs only in-register reductions plus one exchange with
-// lane ^ 32. P then feeds O^T = V^T . P^T straight from those registers; V is
-// written to LDS transposed ([d][key]) so each lane reads 4 consecutive keys.
+// lane ^ 32. P then feeds O^T = V^T . P^T straight from those registers; the V^T
+// fragments come from transposing LDS reads (ds_read_b64_tr_b16).
 // Keys come in tiles in increasing order, so tile 0 (always visible) fixes a
 // finite running max before any fully masked tile can occur.
 #include "common.h"
@@ -21,22 +23,44 @@
 
 namespace smol {
 
-template <typename W, int D, int G, int QW>
+// Byte offset of 16-bit element (row, col) in a swizzled LDS tile with RB-byte rows:
+// 16-byte chunk c of row r sits at slot c ^ (r & 7).
+template <int RB, int ES>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int EPC = 16 / ES;
+  return row * RB + (((col / EPC) ^ (row & 7)) << 4) + (col % EPC) * ES;
+}
+
+typedef __fp16 half4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+// 4 x 16-bit transposed read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane 4r + c receives element c of the 8-byte blocks addressed by lanes
+// 4j + r, j = 0..3 (an in-bounds probe on the hardware fixed this mapping).
+__device__ __forceinline__ u16x4 lds_read_tr16(const char *p) {
+  const half4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) half4 *)p);
+  return __builtin_bit_cast(u16x4, v);
+}
+
+
+template <typename W, int D, int G, int QW, int S>
 __global__ void __launch_bounds__(64 * G * QW)
 attn_prefill_kernel(const AttnArgs a) {
-  using T = Act<W>;  // operand type of q, p and o; cached k, v (type W) convert on staging
-  constexpr int NW = G * QW, NT = 64 * NW, BQ = 32 * QW, BKV = 64;
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int KP = D + EPC;    // K row pitch (elements)
-  constexpr int VP = BKV + EPC;  // V^T row pitch (elements)
-  constexpr int CPR = D / EPC;   // chunks per key row
-  constexpr int CH = BKV * CPR;  // chunks per K (or V) tile
-  constexpr int MAXC = (2 * CH + NT - 1) / NT;
-  constexpr int DS = D / 16;     // MFMA K-steps over the head dim
-  constexpr int DT = D / 32;     // 32-row tiles of O^T
+  using T = Act<W>;  // operand type of q, p and o; cached k, v (type W) convert as they leave LDS
+  constexpr int NW = G * QW, BQ = 32 * QW, BKV = 64;
+  constexpr int ES = sizeof(W);
+  constexpr int RB = D * ES;                 // bytes per key row
+  constexpr int CPR = RB / 16;               // 16-byte chunks per key row
+  constexpr int TILE_BYTES = BKV * RB;       // K (or V) bytes per tile
+  constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  constexpr int NINS = 2 * BKV * CPR / 64;   // DMA wave-instructions per stage
+  constexpr int IPW = (NINS + NW - 1) / NW;  // per wave (surplus waves repeat the last one)
+  constexpr int DS = D / 16;                 // MFMA K-steps over the head dim
+  constexpr int DT = D / 32;                 // 32-row tiles of O^T
+  static_assert(S >= 2, "ring depth");
 
-  __shared__ __attribute__((aligned(16))) T Ks[2][BKV * KP];
-  __shared__ __attribute__((aligned(16))) T Vt[2][D * VP];
+  __shared__ __attribute__((aligned(16))) char smem[S * STAGE_BYTES];
+  const uint32_t smem_base = lds_addr(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
@@ -67,32 +91,53 @@ attn_prefill_kernel(const AttnArgs a) {
   const W *kbase_ptr = (const W *)a.k + (size_t)(b * a.n_kv + g) * a.cap * D;
   const W *vbase_ptr = (const W *)a.v + (size_t)(b * a.n_kv + g) * a.cap * D;
 
-  Chunk16 pre[MAXC];
-  auto fetch = [&](int kt) {
+  // DMA: instruction q of a stage fills LDS bytes [q*1024, q*1024 + 1024) of the stage:
+  // chunk index q*64 + lane -> (tile K or V, key row, slot); the slot receives the
+  // row's chunk slot ^ (row & 7). The per-lane geometry is fixed; only the key moves.
+  const W *dma_base[IPW];
+  int dma_row[IPW];
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = min(tid + i * NT, 2 * CH - 1);  // surplus threads re-read the last chunk
-      const int cc = c < CH ? c : c - CH;
-      const int key = min(kt * BKV + cc / CPR, nkeys - 1);
-      const W *src = (c < CH ? kbase_ptr : vbase_ptr) + (size_t)key * D + (cc % CPR) * EPC;
-      pre[i] = ld16(src);
+  for (int j = 0; j < IPW; ++j) {
+    const int q = min(w * IPW + j, NINS - 1);
+    const int cidx = q * 64 + lane;
+    const int row = (cidx % (BKV * CPR)) / CPR;
+    const int c = (cidx % CPR) ^ (row & 7);
+    dma_base[j] = (cidx / (BKV * CPR) == 0 ? kbase_ptr : vbase_ptr) + c * (16 / ES);
+    dma_row[j] = row;
+  }
+  auto issue = [&](int kt, int slot) {
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int q = min(w * IPW + j, NINS - 1);
+      const int key = min(kt * BKV + dma_row[j], nkeys - 1);
+      lds_dma16(dma_base[j] + (size_t)key * D, smem_base + slot * STAGE_BYTES + q * 1024);
     }
   };
-  auto stash = [&](int buf) {
+
+  // Per-lane LDS offsets of the K fragments (S^T = K Q^T) and of the V^T fragment
+  // sources for the transposed reads, fixed for the whole loop.
+  int koff[2][DS];
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int c = tid + i * NT;
-      const Chunk16 cv = to_operand<W>(pre[i]);
-      if (c < CH) {
-        st16(&Ks[buf][(c / CPR) * KP + (c % CPR) * EPC], cv);
-      } else if (c < 2 * CH) {
-        const int cc = c - CH;
-        const int key = cc / CPR, d0 = (cc % CPR) * EPC;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) Vt[buf][(d0 + j) * VP + key] = chunk_elem<T>(cv, j);
+    for (int st = 0; st < DS; ++st) koff[i][st] = swz<RB, ES>(32 * i + ql, 16 * st + half * 8);
+  int voff[4][DT][2];
+#pragma unroll
+  for (int sg = 0; sg < 4; ++sg)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        if constexpr (ES == 2) {
+          // lane l supplies 4 dims starting at 16*((l/16)%2) + 4*(l%4) of key row
+          // 16 sg + 8 pp + 4*(l/32) + (l%16)/4; the transposed read then returns dim
+          // (l % 32) of the 4 keys 16 sg + 8 pp + 4 half + (0..3).
+          const int sl = lane & 15;
+          voff[sg][dt][pp] = swz<RB, ES>(16 * sg + 8 * pp + 4 * half + (sl >> 2), 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (sl & 3));
+        } else {
+          voff[sg][dt][pp] = 0;
+        }
       }
-    }
-  };
 
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   f32x16 o[DT];
@@ -100,53 +145,74 @@ attn_prefill_kernel(const AttnArgs a) {
   for (int i = 0; i < DT; ++i) o[i] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < ntiles) issue(st, st);
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    fetch(min(kt + 1, ntiles - 1));  // branch-free prefetch (the last one is a harmless re-read)
-    __builtin_amdgcn_sched_barrier(0);  // issue the loads before this tile's math
+    if (kt + S - 2 < ntiles)
+      wait_vmcnt<(S - 2) * IPW>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // tile kt landed for every wave; slot of tile kt-1 is free
+    if (kt + S - 1 < ntiles) issue(kt + S - 1, (kt + S - 1) % S);
+    const char *ks = smem + (kt % S) * STAGE_BYTES;
+    const char *vs = ks + TILE_BYTES;
     const int k0 = kt * BKV;
     if (wave_live && k0 <= wave_kmax) {
+      // ---- S^T = K . Q^T (lane: one query, 32 of its keys in two 32-key tiles)
       f32x16 s[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
+          const int row = 32 * i + ql;
           Frag<T> kf;
-          load_frag(kf, &Ks[cur][(32 * i + ql) * KP + 16 * st + half * 8]);
+          if constexpr (ES == 2) {
+            const Chunk16 c = to_operand<W>(*reinterpret_cast<const Chunk16 *>(ks + koff[i][st]));
+            kf.v = __builtin_bit_cast(decltype(kf.v), c);
+          } else {
+            const Chunk16 lo = *reinterpret_cast<const Chunk16 *>(ks + swz<RB, ES>(row, 16 * st + half * 8));
+            const Chunk16 hi = *reinterpret_cast<const Chunk16 *>(ks + swz<RB, ES>(row, 16 * st + half * 8 + 4));
+            kf.v = (f32x8){__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]), __uint_as_float(lo[3]),
+                           __uint_as_float(hi[0]), __uint_as_float(hi[1]), __uint_as_float(hi[2]), __uint_as_float(hi[3])};
+          }
           mma_32x32x16(s[i], kf, qf[st]);
         }
       }
+      // ---- online softmax. Scores stay unscaled; the running max m_run lives in the
+      // scaled (log2) domain, so p = exp2(s * c - m) is one FMA and one v_exp_f32 (its
+      // argument is <= 0, where the plain hardware exp2 needs no range fix-up).
       const bool need_mask = k0 + BKV - 1 > q0 + a.q_key_off;
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = s[i][r] * c_log2;
-          if (need_mask && k0 + 32 * i + acc_row(r, lane) > my_kmax) v = -INFINITY;
-          s[i][r] = v;
-          mx = fmaxf(mx, v);
+          if (need_mask && k0 + 32 * i + acc_row(r, lane) > my_kmax) s[i][r] = -INFINITY;
+          mx = fmaxf(mx, s[i][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      const float m_new = fmaxf(m_run, mx * c_log2);
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(s[i][r] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[i][r], c_log2, -m_new));
           s[i][r] = p;
           ls += p;
         }
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
+      if (__any(m_new != m_run)) {  // rescale only when some running max moved
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      }
+      l_run += ls;
+      m_run = m_new;
+      // ---- O^T += V^T . P^T. Element e of a lane's 8 values in key step sg is key
+      // 16 sg + 8 (e / 4) + 4 half + e % 4, for P (from the score registers) and V alike.
 #pragma unroll
       for (int sg = 0; sg < 4; ++sg) {
         Frag<T> pf;
@@ -154,20 +220,32 @@ attn_prefill_kernel(const AttnArgs a) {
         for (int e = 0; e < 8; ++e) pf.v[e] = from_f32<T>(s[sg >> 1][8 * (sg & 1) + e]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const T *vp = &Vt[cur][(32 * dt + ql) * VP + 16 * sg + 4 * half];
           Frag<T> vf;
+          if constexpr (ES == 2) {
+            typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+            u32x4v raw;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vf.v[e] = vp[e];
-            vf.v[4 + e] = vp[8 + e];
+            for (int pp = 0; pp < 2; ++pp) {
+              const u16x4 t = lds_read_tr16(vs + voff[sg][dt][pp]);
+              const uint32_t lo = (uint32_t)t[0] | ((uint32_t)t[1] << 16), hi = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
+              raw[2 * pp] = bf16x2_to_f16x2(lo);
+              raw[2 * pp + 1] = bf16x2_to_f16x2(hi);
+            }
+            vf.v = __builtin_bit_cast(decltype(vf.v), raw);
+          } else {
+            const int d = 32 * dt + ql;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int row = 16 * sg + 8 * pp + 4 * half + e;
+                vf.v[4 * pp + e] = *reinterpret_cast<const float *>(vs + row * RB + (((d >> 2) ^ (row & 7)) << 4) + (d & 3) * 4);
+              }
           }
           mma_32x32x16(o[dt], vf, pf);
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    stash(cur ^ 1);
-    __syncthreads();
   }
 
   if (!wave_live || q0 + ql >= a.T) return;
@@ -182,14 +260,16 @@ attn_prefill_kernel(const AttnArgs a) {
 
 template <typename T, int D, int G>
 static hipError_t launch_attn_g(const AttnArgs &a, hipStream_t s) {  // T: storage type
+  // LDS ring: 3 stages of K+V tiles (2 when a stage is 64 KB, float at d = 128).
+  constexpr int S = (2 * 64 * D * sizeof(T) >= 65536) ? 2 : 3;
   // Two query sub-blocks per wave group when that still gives enough workgroups.
   const long wg2 = (long)a.B * a.n_kv * ((a.T + 63) / 64);
   if (G == 1 || wg2 >= 256) {
     const int nqb = (a.T + 63) / 64;
-    hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, 2>), dim3(nqb * a.B * a.n_kv), dim3(64 * G * 2), 0, s, a);
+    hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, 2, S>), dim3(nqb * a.B * a.n_kv), dim3(64 * G * 2), 0, s, a);
   } else {
     const int nqb = (a.T + 31) / 32;
-    hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, 1>), dim3(nqb * a.B * a.n_kv), dim3(64 * G), 0, s, a);
+    hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, 1, S>), dim3(nqb * a.B * a.n_kv), dim3(64 * G), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -77,6 +77,16 @@ __device__ __forceinline__ void load_frag(Frag<float> &f, const float *p) {
 // Row of the 32x32 accumulator held in register r of a lane (column = lane % 32).
 __device__ __forceinline__ int acc_row(int r, int lane) { return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3); }
 
+// ---------------------------------------------------------------- XCD row ownership
+// Workgroup i of a launch runs on XCD i % 8, and each XCD has its own L2. Row-wise
+// kernels of the prefill (GEMMs, RMSNorm) give XCD x the same row range
+// [x * rows_per_xcd, (x + 1) * rows_per_xcd) of the activations, so the rows one
+// kernel writes are read from the same L2 by the next. Only for M >= 1024: below
+// that, every XCD must get work.
+constexpr int SMOL_XCDS = 8;
+__host__ __device__ inline bool xcd_rows(int M) { return M >= 1024; }
+__host__ __device__ inline int rows_per_xcd(int M) { return ((M + SMOL_XCDS - 1) / SMOL_XCDS + 127) / 128 * 128; }
+
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -120,13 +130,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 
 // Convert a staged chunk from storage type W to operand type Act<W> (same size).
 template <typename W> __device__ __forceinline__ Chunk16 to_operand(const Chunk16 &c) { return c; }
+// Two bfloat16 in one dword -> two float16 (exact in float16's normal range; one
+// v_cvt_pk_f16_f32, round to nearest even, per pair).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 f = {__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
 template <> __device__ __forceinline__ Chunk16 to_operand<bf16>(const Chunk16 &c) {
   Chunk16 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16 lo = (f16)__uint_as_float(c[i] << 16);
-    const f16 hi = (f16)__uint_as_float(c[i] & 0xffff0000u);
-    r[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
+  for (int i = 0; i < 4; ++i) r[i] = bf16x2_to_f16x2(c[i]);
   return r;
 }

@@ -64,6 +64,13 @@ __device__ __forceinline__ const W *b_row(const GemmParams &p, int n) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// 1 = column ownership per XCD, 2 = row ownership, 0 = plain order.
+__host__ __device__ inline int xcd_mode(int M, int N, int BN) {
+  if (N > M && N / BN >= SMOL_XCDS) return 1;
+  if (xcd_rows(M)) return 2;
+  return 0;
+}
+
 // Store N (4 or 8) consecutive floats as type O.
 template <typename O, int N>
 __device__ __forceinline__ void store_vec(O *dst, const float *v) {
@@ -125,13 +132,34 @@ gemm_kernel(const GemmParams p) {
   const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // XCD-aware tile order: workgroup i runs on XCD i % 8, so hand each XCD a
-  // contiguous range of tiles; consecutive tiles share their B (weight) columns.
-  const int tiles_m = (p.M + BM - 1) / BM;
-  const int ntiles = tiles_m * (p.N / BN);
-  int bid = blockIdx.x;
-  if (ntiles % 8 == 0) bid = (bid % 8) * (ntiles / 8) + bid / 8;
-  const int tm = bid % tiles_m, tn = bid / tiles_m;
+  // XCD-aware tile order (workgroup i runs on XCD i % 8; each XCD has its own L2
+  // and whatever misses it streams at roughly HBM rate). Column ownership when the
+  // weights outweigh the activations (N > M): XCD x takes a contiguous slice of N
+  // tiles, so every weight byte is fetched by one XCD only. Otherwise row
+  // ownership (see xcd_rows): XCD x takes the M tiles of its row range. Within an
+  // XCD, M runs fastest so that concurrent workgroups share a weight tile.
+  int tm, tn;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
+  const int local = blockIdx.x / SMOL_XCDS, xcd = blockIdx.x % SMOL_XCDS;
+  switch (xcd_mode(p.M, p.N, BN)) {
+    case 1: {  // columns
+      const int ntx = (tiles_n + SMOL_XCDS - 1) / SMOL_XCDS;
+      tm = local % tiles_m;
+      tn = xcd * ntx + local / tiles_m;
+      if (tn >= tiles_n) return;  // whole workgroup
+      break;
+    }
+    case 2: {  // rows
+      const int mtx = rows_per_xcd(p.M) / BM;
+      tm = xcd * mtx + local % mtx;
+      tn = local / mtx;
+      if (tm >= tiles_m) return;  // whole workgroup
+      break;
+    }
+    default:
+      tm = blockIdx.x % tiles_m;
+      tn = blockIdx.x / tiles_m;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   // DMA sources. Wave w's instruction j fills rows 8*(w*IPW + j) .. +7 of a stage;
@@ -342,7 +370,13 @@ gemm_kernel(const GemmParams p) {
 template <typename W, int BM, int BN, int EPI, int S>
 static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
   if (p.N % BN != 0 || p.K % (128 / (int)sizeof(W)) != 0) return hipErrorInvalidValue;
-  const int tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
+  int tiles;
+  switch (xcd_mode(p.M, p.N, BN)) {
+    case 1: tiles = SMOL_XCDS * ((tiles_n + SMOL_XCDS - 1) / SMOL_XCDS) * tiles_m; break;
+    case 2: tiles = SMOL_XCDS * (rows_per_xcd(p.M) / BM) * tiles_n; break;
+    default: tiles = tiles_m * tiles_n;
+  }
   hipLaunchKernelGGL((gemm_kernel<W, BM, BN, EPI, S>), dim3(tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }

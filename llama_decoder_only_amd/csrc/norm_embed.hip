@@ -16,7 +16,14 @@ template <typename T, typename O, int VPL>
 __global__ void __launch_bounds__(64 * NORM_ROWS)
 rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ w, O *__restrict__ out, int M, int H, float eps) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * NORM_ROWS + (threadIdx.x >> 6);
+  int row;
+  if (xcd_rows(M)) {  // XCD x normalises rows of its own range (same L2 as the GEMMs)
+    const int rpx = rows_per_xcd(M);
+    row = (blockIdx.x % SMOL_XCDS) * rpx + (blockIdx.x / SMOL_XCDS) * NORM_ROWS + (threadIdx.x >> 6);
+    if (row >= min(M, (int)(blockIdx.x % SMOL_XCDS + 1) * rpx)) return;
+  } else {
+    row = blockIdx.x * NORM_ROWS + (threadIdx.x >> 6);
+  }
   if (row >= M) return;
   const float *xr = x + (size_t)row * H;
   O *orow = out + (size_t)row * H;
@@ -48,7 +55,8 @@ rmsnorm_kernel(const float *__restrict__ x, const T *__restrict__ w, O *__restri
 
 template <typename T>
 hipError_t rmsnorm(const float *x, const T *w, Act<T> *out, int M, int H, float eps, hipStream_t s) {
-  const dim3 grid((M + NORM_ROWS - 1) / NORM_ROWS), block(64 * NORM_ROWS);
+  const dim3 grid(xcd_rows(M) ? SMOL_XCDS * rows_per_xcd(M) / NORM_ROWS : (M + NORM_ROWS - 1) / NORM_ROWS);
+  const dim3 block(64 * NORM_ROWS);
   switch (H) {
     case 576: hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 9>), grid, block, 0, s, x, w, out, M, H, eps); break;
     case 2048: hipLaunchKernelGGL((rmsnorm_kernel<T, Act<T>, 32>), grid, block, 0, s, x, w, out, M, H, eps); break;
