@@ -180,7 +180,7 @@ def main():
     # per-kernel-class durations from HIP events (eager step on the same stream)
     kern = {}
     with torch.cuda.stream(stream):
-        for name in ("qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head", "rmsnorm", "embed"):
+        for name in ("qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head", "embed"):
             ms, n = _kernel_time(B, name, step, torch)
             kern[name] = {"total_ms": ms, "launches": n, "avg_us": 1e3 * ms / max(n, 1)}
     dominant = max((k for k in kern if k in flops["per_launch"]), key=lambda k: kern[k]["total_ms"])

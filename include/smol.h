@@ -38,7 +38,7 @@
  *     wq [n_heads*d, H], wk/wv [n_kv*d, H], wo [H, n_heads*d], w_gate/w_up [I, H],
  *     w_down [H, I]; norm weights [H]; embedding [vocab, H].
  *   - Supported shapes: head_dim 64 or 128; hidden, intermediate and vocab multiples
- *     of 64; hidden == n_heads*head_dim; n_heads divisible by n_kv_heads with 1 to 4
+ *     of 64; hidden at most 4096; hidden == n_heads*head_dim; n_heads divisible by n_kv_heads with 1 to 4
  *     query heads per kv head. Anything else returns SMOL_ERR_UNSUPPORTED or
  *     SMOL_ERR_INVALID_ARG. Batch and sequence length are arbitrary (>= 1).
  *   - Calls that share a workspace or a cache must not overlap.
@@ -136,7 +136,10 @@ const char *smol_last_error(void);
  * smol_timing_begin(kernel, max_launches) the next launches of that kernel class
  * (smol_kernel) are bracketed by HIP events on their stream, up to max_launches.
  * smol_timing_end() waits for those events and returns the summed duration in
- * milliseconds and the number of launches timed (host pointers). */
+ * milliseconds and the number of launches timed (host pointers). SMOL_K_EMBED times
+ * the kernel that starts the residual stream (embedding gather, or the copy of x_in
+ * in smol_block_forward); SMOL_K_RMSNORM has no launches of its own, since every
+ * RMSNorm is folded into the GEMMs around it. */
 typedef enum {
   SMOL_K_EMBED = 0, SMOL_K_RMSNORM = 1, SMOL_K_QKV_ROPE = 2, SMOL_K_ATTENTION = 3,
   SMOL_K_O_PROJ = 4, SMOL_K_GATE_UP = 5, SMOL_K_DOWN = 6, SMOL_K_LM_HEAD = 7,

@@ -2,15 +2,17 @@
 // the sequence of kernel launches for a block, a prefill and a decode step.
 //
 // Order of one block (nnterp "SmolLM3", "The block, in order"; tohio block.py):
-//   u = RMSNorm(x; attn_norm)            rmsnorm
-//   q, k, v = u W^T, RoPE on q, k        gemm_qkv_rope (k, v land in the cache)
-//   o = causal GQA attention             attention_prefill / attention_decode
-//   x += o W_o^T                         gemm_residual
-//   u = RMSNorm(x; mlp_norm)             rmsnorm
-//   y = silu(u W_g^T) * (u W_u^T)        gemm_swiglu
-//   x += y W_d^T                         gemm_residual
-// The model adds the embedding gather before and RMSNorm + the tied head after
-// (abi96062 model.py, SmolLM2Model.forward).
+//   u = RMSNorm(x; attn_norm); q, k, v = u W^T     gemm_qkv_rope: RoPE on q, k; k, v
+//                                                  land in the cache
+//   o = causal GQA attention                       attention_prefill / attention_decode
+//   x += o W_o^T                                   gemm_residual
+//   u = RMSNorm(x; mlp_norm); y = silu(u W_g^T) * (u W_u^T)        gemm_swiglu
+//   x += y W_d^T                                   gemm_residual
+// The model gathers the embedding before the blocks and applies the final RMSNorm
+// and the tied head after them (abi96062 model.py, SmolLM2Model.forward). Every
+// RMSNorm is deferred (kernels.h, NormIn / NormOut): the kernel that last wrote x
+// leaves xs = w * x * r_old and the new row sums of squares, and the GEMM that reads
+// xs rescales its output rows. Five launches per block, no separate norm kernels.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
@@ -61,6 +63,7 @@ smol_status check_config(const smol_config *c, Dims *o) {
   if (c->head_dim != 64 && c->head_dim != 128) return fail(SMOL_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c->head_dim);
   if (c->hidden % 64 || c->intermediate % 64 || c->vocab % 64)
     return fail(SMOL_ERR_UNSUPPORTED, "hidden, intermediate and vocab must be multiples of 64");
+  if (c->hidden > 4096) return fail(SMOL_ERR_UNSUPPORTED, "hidden %d (supported: up to 4096)", c->hidden);
   o->H = c->hidden;
   o->nq = c->n_heads;
   o->nkv = c->n_kv_heads;
@@ -91,7 +94,7 @@ size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Workspace carve-up. Offsets in bytes from ws.
 struct Ws {
-  size_t x, u, q, k, v, o, y, part, total;
+  size_t x, xs, q, k, v, o, y, ss_p, ss_q, part, total;
 };
 
 Ws layout(const Dims &D, int op, int B, int T) {
@@ -100,10 +103,12 @@ Ws layout(const Dims &D, int op, int B, int T) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += up(bytes); return at; };
   w.x = take(M * D.H * 4);
-  w.u = take(M * D.H * D.esz);
+  w.xs = take(M * D.H * D.esz);
   w.q = take(M * D.nq * D.d * D.esz);
   w.o = take(M * D.nq * D.d * D.esz);
   w.y = take(M * D.I * D.esz);
+  w.ss_p = take((size_t)(D.H / 64) * M * 4);  // row sums of squares of x per 64 columns,
+  w.ss_q = take((size_t)(D.H / 64) * M * 4);  // two buffers: new and old alternate
   if (op == SMOL_OP_DECODE) {
     int chunk;
     const int cap = std::min(T, D.max_pos);
@@ -164,22 +169,26 @@ struct LayerCtx {
   hipStream_t s;
 };
 
+// One block. On entry xs = attn_norm * x * r_old, ss_p holds the row sums of squares
+// of x and ss_q those r_old came from. On exit the same holds for next_norm (the
+// next block's attn_norm or the final norm; nullptr: nothing is left for a norm).
 template <typename T>
-smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x) {
+smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, const void *next_norm) {
   const Dims &D = *c.D;
   const hipStream_t s = c.s;
   const bool decode = c.cache_len != nullptr;
   const int M = decode ? c.B : c.B * c.T;
   using A = Act<T>;  // activations: MFMA operand type
-  A *u = (A *)(c.ws + c.lay.u);
+  A *xs = (A *)(c.ws + c.lay.xs);
   A *q = (A *)(c.ws + c.lay.q);
   A *o = (A *)(c.ws + c.lay.o);
   A *y = (A *)(c.ws + c.lay.y);
+  float *ss_p = (float *)(c.ws + c.lay.ss_p), *ss_q = (float *)(c.ws + c.lay.ss_q);
 
-  SMOL_LAUNCH(SMOL_K_RMSNORM, smol::rmsnorm<T>(x, (const T *)w->attn_norm, u, M, D.H, D.eps, s));
   smol::QkvOut qo{M, D.H, D.nq * D.d, D.nkv * D.d, D.d, q, c.kc, c.vc,
                   decode ? 1 : c.T, c.cap, D.nkv, c.pos0, c.kv_off, D.max_pos, c.cache_len, c.inv_freq};
-  SMOL_LAUNCH(SMOL_K_QKV_ROPE, smol::gemm_qkv_rope<T>(u, (const T *)w->wq, (const T *)w->wk, (const T *)w->wv, qo, s));
+  SMOL_LAUNCH(SMOL_K_QKV_ROPE, smol::gemm_qkv_rope<T>(xs, smol::NormIn{ss_p, ss_q, D.eps}, (const T *)w->wq,
+                                                      (const T *)w->wk, (const T *)w->wv, qo, s));
   if (decode) {
     int chunk;
     const int splits = smol::decode_splits(std::min(c.cap, D.max_pos), &chunk);
@@ -191,10 +200,14 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x) 
     smol::AttnArgs aa{q, c.kc, c.vc, o, c.B, c.T, D.nq, D.nkv, D.d, c.cap, c.q_key_off};
     SMOL_LAUNCH(SMOL_K_ATTENTION, smol::attention_prefill<T>(aa, s));
   }
-  SMOL_LAUNCH(SMOL_K_O_PROJ, smol::gemm_residual<T>(o, (const T *)w->wo, M, D.H, D.nq * D.d, x, s));
-  SMOL_LAUNCH(SMOL_K_RMSNORM, smol::rmsnorm<T>(x, (const T *)w->mlp_norm, u, M, D.H, D.eps, s));
-  SMOL_LAUNCH(SMOL_K_GATE_UP, smol::gemm_swiglu<T>(u, (const T *)w->w_gate, (const T *)w->w_up, M, D.I, D.H, y, s));
-  SMOL_LAUNCH(SMOL_K_DOWN, smol::gemm_residual<T>(y, (const T *)w->w_down, M, D.H, D.I, x, s));
+  // x += o W_o^T; leaves xs for mlp_norm, the new sums in ss_q (ss_p: the old ones)
+  SMOL_LAUNCH(SMOL_K_O_PROJ, smol::gemm_residual<T>(o, (const T *)w->wo, M, D.H, D.nq * D.d, x,
+                                                    smol::NormOut{ss_p, ss_q, w->mlp_norm, xs, D.eps}, s));
+  SMOL_LAUNCH(SMOL_K_GATE_UP, smol::gemm_swiglu<T>(xs, smol::NormIn{ss_q, ss_p, D.eps}, (const T *)w->w_gate,
+                                                   (const T *)w->w_up, M, D.I, D.H, y, s));
+  // x += y W_d^T; leaves xs for next_norm, the new sums in ss_p (ss_q: the old ones)
+  const smol::NormOut nxt{ss_q, next_norm ? ss_p : nullptr, next_norm, next_norm ? (void *)xs : nullptr, D.eps};
+  SMOL_LAUNCH(SMOL_K_DOWN, smol::gemm_residual<T>(y, (const T *)w->w_down, M, D.H, D.I, x, nxt, s));
   return SMOL_OK;
 }
 
@@ -212,12 +225,22 @@ smol_status check_ws(const Dims &D, int op, int B, int T, void *ws, size_t ws_by
   return SMOL_OK;
 }
 
+// The tied head on the final RMSNorm: logits = u E^T, from the xs the last block left.
 template <typename T>
-smol_status head(const Dims &D, const smol_model_weights *w, float *x, int M, void *logits, char *ws, const Ws &lay,
+smol_status head(const Dims &D, const smol_model_weights *w, int M, void *logits, char *ws, const Ws &lay,
                  hipStream_t s) {
-  Act<T> *u = (Act<T> *)(ws + lay.u);
-  SMOL_LAUNCH(SMOL_K_RMSNORM, smol::rmsnorm<T>(x, (const T *)w->final_norm, u, M, D.H, D.eps, s));
-  SMOL_LAUNCH(SMOL_K_LM_HEAD, smol::gemm_store<T>(u, (const T *)w->embed, M, D.V, D.H, logits, 0, s));
+  const smol::NormIn fin{(const float *)(ws + lay.ss_p), (const float *)(ws + lay.ss_q), D.eps};
+  SMOL_LAUNCH(SMOL_K_LM_HEAD,
+              smol::gemm_store<T>((const Act<T> *)(ws + lay.xs), fin, (const T *)w->embed, M, D.V, D.H, logits, 0, s));
+  return SMOL_OK;
+}
+
+// x = E[ids] or x = src, with what the first block's deferred RMSNorm reads.
+template <typename T>
+smol_status prologue(const Dims &D, const int32_t *ids, const T *E, const float *src, float *x, const T *attn_norm,
+                     int M, char *ws, const Ws &lay, hipStream_t s) {
+  SMOL_LAUNCH(SMOL_K_EMBED, smol::rows_ss<T>(ids, E, src, x, (float *)(ws + lay.ss_p), (float *)(ws + lay.ss_q),
+                                             attn_norm, (Act<T> *)(ws + lay.xs), D.eps, M, D.H, D.V, s));
   return SMOL_OK;
 }
 
@@ -238,8 +261,9 @@ smol_status block_impl(const Dims &D, const smol_layer_weights *w, const float *
     c.kc = ws + lay.k; c.vc = ws + lay.v; c.cap = T_; c.kv_off = pos0; c.q_key_off = 0;
   }
   fill_inv_freq(D, c.inv_freq);
-  if (x_out != x_in) SMOL_LAUNCH(-1, smol::copy_f32(x_in, x_out, (size_t)B * T_ * D.H, s));
-  return run_layer<T>(c, w, x_out);
+  smol_status st = prologue<T>(D, nullptr, nullptr, x_in, x_out, (const T *)w->attn_norm, B * T_, ws, lay, s);
+  if (st != SMOL_OK) return st;
+  return run_layer<T>(c, w, x_out, nullptr);
 }
 
 template <typename T>
@@ -247,7 +271,8 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
                          void *kc, void *vc, int cap, char *ws, const Ws &lay, hipStream_t s) {
   float *x = (float *)(ws + lay.x);
   const int M = B * T_;
-  SMOL_LAUNCH(SMOL_K_EMBED, smol::embed_rows<T>(ids, (const T *)w->embed, x, M, D.H, D.V, s));
+  smol_status st0 = prologue<T>(D, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, M, ws, lay, s);
+  if (st0 != SMOL_OK) return st0;
   LayerCtx c{};
   c.D = &D;
   c.ws = ws;
@@ -266,17 +291,19 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
     } else {
       c.kc = ws + lay.k; c.vc = ws + lay.v; c.cap = T_; c.kv_off = 0; c.q_key_off = 0;
     }
-    smol_status st = run_layer<T>(c, &w->layers[l], x);
+    const void *next = l + 1 < D.L ? w->layers[l + 1].attn_norm : w->final_norm;
+    smol_status st = run_layer<T>(c, &w->layers[l], x, next);
     if (st != SMOL_OK) return st;
   }
-  return head<T>(D, w, x, M, logits, ws, lay, s);
+  return head<T>(D, w, M, logits, ws, lay, s);
 }
 
 template <typename T>
 smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_t *ids, const int32_t *cache_len,
                         int B, void *kc, void *vc, int cap, void *logits, char *ws, const Ws &lay, hipStream_t s) {
   float *x = (float *)(ws + lay.x);
-  SMOL_LAUNCH(SMOL_K_EMBED, smol::embed_rows<T>(ids, (const T *)w->embed, x, B, D.H, D.V, s));
+  smol_status st0 = prologue<T>(D, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, B, ws, lay, s);
+  if (st0 != SMOL_OK) return st0;
   LayerCtx c{};
   c.D = &D;
   c.ws = ws;
@@ -291,10 +318,11 @@ smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_
   for (int l = 0; l < D.L; ++l) {
     c.kc = (char *)kc + l * layer_elems * D.esz;
     c.vc = (char *)vc + l * layer_elems * D.esz;
-    smol_status st = run_layer<T>(c, &w->layers[l], x);
+    const void *next = l + 1 < D.L ? w->layers[l + 1].attn_norm : w->final_norm;
+    smol_status st = run_layer<T>(c, &w->layers[l], x, next);
     if (st != SMOL_OK) return st;
   }
-  return head<T>(D, w, x, B, logits, ws, lay, s);
+  return head<T>(D, w, B, logits, ws, lay, s);
 }
 
 smol_status check_model(const Dims &D, const smol_model_weights *w) {

@@ -43,34 +43,37 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const char *p) {
 }
 
 
-template <typename W, int D, int G, int QW, int S>
-__global__ void __launch_bounds__(64 * G * QW)
+template <typename W, int D, int G, int QW, int KS, int S>
+__global__ void __launch_bounds__(64 * G * QW * KS)
 attn_prefill_kernel(const AttnArgs a) {
   using T = Act<W>;  // operand type of q, p and o; cached k, v (type W) convert as they leave LDS
-  constexpr int NW = G * QW, BQ = 32 * QW, BKV = 64;
+  constexpr int NW = G * QW * KS, BQ = 32 * QW, BKV = 64;
   constexpr int ES = sizeof(W);
-  constexpr int RB = D * ES;                 // bytes per key row
-  constexpr int CPR = RB / 16;               // 16-byte chunks per key row
-  constexpr int TILE_BYTES = BKV * RB;       // K (or V) bytes per tile
-  constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  constexpr int NINS = 2 * BKV * CPR / 64;   // DMA wave-instructions per stage
-  constexpr int IPW = (NINS + NW - 1) / NW;  // per wave (surplus waves repeat the last one)
-  constexpr int DS = D / 16;                 // MFMA K-steps over the head dim
-  constexpr int DT = D / 32;                 // 32-row tiles of O^T
+  constexpr int RB = D * ES;                       // bytes per key row
+  constexpr int CPR = RB / 16;                     // 16-byte chunks per key row
+  constexpr int TILE_BYTES = BKV * RB;             // K (or V) bytes per tile
+  constexpr int STAGE_BYTES = KS * 2 * TILE_BYTES; // one round: KS tiles of K and V
+  constexpr int NINS = STAGE_BYTES / 1024;         // DMA wave-instructions per round
+  constexpr int IPW = (NINS + NW - 1) / NW;        // per wave (surplus waves repeat the last one)
+  constexpr int DS = D / 16;                       // MFMA K-steps over the head dim
+  constexpr int DT = D / 32;                       // 32-row tiles of O^T
+  constexpr int PSTATE = DT * 16 + 2;              // floats per lane of a partial state
   static_assert(S >= 2, "ring depth");
+  static_assert(KS == 1 || (KS - 1) * G * QW * PSTATE * 64 * 4 <= S * STAGE_BYTES, "partials fit the ring");
 
   __shared__ __attribute__((aligned(16))) char smem[S * STAGE_BYTES];
   const uint32_t smem_base = lds_addr(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, ql = lane & 31;
+  const int hq = w % (G * QW), ks = w / (G * QW);  // (head, query sub-block) and key split
   const int nqb = (a.T + BQ - 1) / BQ;
   const int per = a.B * a.n_kv;
   const int qb = nqb - 1 - (int)blockIdx.x / per;  // longest (latest) query blocks first
   const int rem = (int)blockIdx.x % per;
   const int b = rem / a.n_kv, g = rem % a.n_kv;
-  const int h = g * G + w / QW;
-  const int q0 = qb * BQ + (w % QW) * 32;
+  const int h = g * G + hq / QW;
+  const int q0 = qb * BQ + (hq % QW) * 32;
   const int qt = min(q0 + ql, a.T - 1);
   const bool wave_live = q0 < a.T;
   const int ldq = a.n_heads * D;
@@ -79,37 +82,39 @@ attn_prefill_kernel(const AttnArgs a) {
   {
     const T *qp = (const T *)a.q + (size_t)(b * a.T + qt) * ldq + h * D + half * 8;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) load_frag(qf[s], qp + 16 * s);
+    for (int st = 0; st < DS; ++st) load_frag(qf[st], qp + 16 * st);
   }
 
   const int last_q = min(a.T - 1, qb * BQ + BQ - 1);
   const int nkeys = last_q + a.q_key_off + 1;
   const int ntiles = (nkeys + BKV - 1) / BKV;
+  const int nrounds = (ntiles + KS - 1) / KS;
   const int wave_kmax = min(a.T - 1, q0 + 31) + a.q_key_off;
   const int my_kmax = qt + a.q_key_off;
 
   const W *kbase_ptr = (const W *)a.k + (size_t)(b * a.n_kv + g) * a.cap * D;
   const W *vbase_ptr = (const W *)a.v + (size_t)(b * a.n_kv + g) * a.cap * D;
 
-  // DMA: instruction q of a stage fills LDS bytes [q*1024, q*1024 + 1024) of the stage:
-  // chunk index q*64 + lane -> (tile K or V, key row, slot); the slot receives the
-  // row's chunk slot ^ (row & 7). The per-lane geometry is fixed; only the key moves.
+  // DMA: instruction q of a round fills LDS bytes [q*1024, q*1024 + 1024) of the stage:
+  // chunk index q*64 + lane -> (tile of the round, K or V, key row, slot); the slot
+  // receives the row's chunk slot ^ (row & 7). Only the key moves from round to round.
   const W *dma_base[IPW];
   int dma_row[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int q = min(w * IPW + j, NINS - 1);
     const int cidx = q * 64 + lane;
+    const int part = cidx / (BKV * CPR);  // 2 * tile_in_round + (0 = K, 1 = V)
     const int row = (cidx % (BKV * CPR)) / CPR;
     const int c = (cidx % CPR) ^ (row & 7);
-    dma_base[j] = (cidx / (BKV * CPR) == 0 ? kbase_ptr : vbase_ptr) + c * (16 / ES);
-    dma_row[j] = row;
+    dma_base[j] = ((part & 1) == 0 ? kbase_ptr : vbase_ptr) + c * (16 / ES);
+    dma_row[j] = (part >> 1) * BKV + row;  // key offset within the round
   }
-  auto issue = [&](int kt, int slot) {
+  auto issue = [&](int r, int slot) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int q = min(w * IPW + j, NINS - 1);
-      const int key = min(kt * BKV + dma_row[j], nkeys - 1);
+      const int key = min(r * KS * BKV + dma_row[j], nkeys - 1);
       lds_dma16(dma_base[j] + (size_t)key * D, smem_base + slot * STAGE_BYTES + q * 1024);
     }
   };
@@ -147,19 +152,20 @@ attn_prefill_kernel(const AttnArgs a) {
 
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
-    if (st < ntiles) issue(st, st);
+    if (st < nrounds) issue(st, st);
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    if (kt + S - 2 < ntiles)
+  for (int r = 0; r < nrounds; ++r) {
+    if (r + S - 2 < nrounds)
       wait_vmcnt<(S - 2) * IPW>();
     else
       wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();  // tile kt landed for every wave; slot of tile kt-1 is free
-    if (kt + S - 1 < ntiles) issue(kt + S - 1, (kt + S - 1) % S);
-    const char *ks = smem + (kt % S) * STAGE_BYTES;
-    const char *vs = ks + TILE_BYTES;
+    __builtin_amdgcn_s_barrier();  // round r landed for every wave; slot of round r-1 is free
+    if (r + S - 1 < nrounds) issue(r + S - 1, (r + S - 1) % S);
+    const int kt = r * KS + ks;  // this wave's tile
+    const char *ks_ptr = smem + (r % S) * STAGE_BYTES + ks * 2 * TILE_BYTES;
+    const char *vs = ks_ptr + TILE_BYTES;
     const int k0 = kt * BKV;
-    if (wave_live && k0 <= wave_kmax) {
+    if (wave_live && kt < ntiles && k0 <= wave_kmax) {
       // ---- S^T = K . Q^T (lane: one query, 32 of its keys in two 32-key tiles)
       f32x16 s[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
@@ -169,11 +175,11 @@ attn_prefill_kernel(const AttnArgs a) {
           const int row = 32 * i + ql;
           Frag<T> kf;
           if constexpr (ES == 2) {
-            const Chunk16 c = to_operand<W>(*reinterpret_cast<const Chunk16 *>(ks + koff[i][st]));
+            const Chunk16 c = to_operand<W>(*reinterpret_cast<const Chunk16 *>(ks_ptr + koff[i][st]));
             kf.v = __builtin_bit_cast(decltype(kf.v), c);
           } else {
-            const Chunk16 lo = *reinterpret_cast<const Chunk16 *>(ks + swz<RB, ES>(row, 16 * st + half * 8));
-            const Chunk16 hi = *reinterpret_cast<const Chunk16 *>(ks + swz<RB, ES>(row, 16 * st + half * 8 + 4));
+            const Chunk16 lo = *reinterpret_cast<const Chunk16 *>(ks_ptr + swz<RB, ES>(row, 16 * st + half * 8));
+            const Chunk16 hi = *reinterpret_cast<const Chunk16 *>(ks_ptr + swz<RB, ES>(row, 16 * st + half * 8 + 4));
             kf.v = (f32x8){__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]), __uint_as_float(lo[3]),
                            __uint_as_float(hi[0]), __uint_as_float(hi[1]), __uint_as_float(hi[2]), __uint_as_float(hi[3])};
           }
@@ -182,29 +188,32 @@ attn_prefill_kernel(const AttnArgs a) {
       }
       // ---- online softmax. Scores stay unscaled; the running max m_run lives in the
       // scaled (log2) domain, so p = exp2(s * c - m) is one FMA and one v_exp_f32 (its
-      // argument is <= 0, where the plain hardware exp2 needs no range fix-up).
+      // argument is <= 0, where the plain hardware exp2 needs no range fix-up). A key
+      // split may meet tiles where some of its queries see no key yet: their max stays
+      // -inf and their probabilities 0.
       const bool need_mask = k0 + BKV - 1 > q0 + a.q_key_off;
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (need_mask && k0 + 32 * i + acc_row(r, lane) > my_kmax) s[i][r] = -INFINITY;
-          mx = fmaxf(mx, s[i][r]);
+        for (int rr = 0; rr < 16; ++rr) {
+          if (need_mask && k0 + 32 * i + acc_row(rr, lane) > my_kmax) s[i][rr] = -INFINITY;
+          mx = fmaxf(mx, s[i][rr]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx * c_log2);
+      const float m_use = (KS > 1 && m_new == -INFINITY) ? 0.f : m_new;
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[i][r], c_log2, -m_new));
-          s[i][r] = p;
+        for (int rr = 0; rr < 16; ++rr) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[i][rr], c_log2, -m_use));
+          s[i][rr] = p;
           ls += p;
         }
       if (__any(m_new != m_run)) {  // rescale only when some running max moved
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
@@ -248,6 +257,42 @@ attn_prefill_kernel(const AttnArgs a) {
     }
   }
 
+  if constexpr (KS > 1) {
+    // ---- merge the key splits: splits 1..KS-1 park (o, m, l) in LDS, split 0 folds
+    // them into its own state. Split 0 saw tile 0, so its max is finite.
+    __syncthreads();  // every wave is done with the ring
+    float *part = reinterpret_cast<float *>(smem);
+    if (ks > 0) {
+      float *pw = part + ((ks - 1) * G * QW + hq) * PSTATE * 64;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) pw[(dt * 16 + rr) * 64 + lane] = o[dt][rr];
+      pw[(DT * 16) * 64 + lane] = m_run;
+      pw[(DT * 16 + 1) * 64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (ks > 0) return;
+    float m_tot = m_run;
+#pragma unroll
+    for (int k = 1; k < KS; ++k) m_tot = fmaxf(m_tot, part[(((k - 1) * G * QW + hq) * PSTATE + DT * 16) * 64 + lane]);
+    const float f0 = __builtin_amdgcn_exp2f(m_run - m_tot);
+    l_run *= f0;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= f0;
+#pragma unroll
+    for (int k = 1; k < KS; ++k) {
+      const float *pr = part + ((k - 1) * G * QW + hq) * PSTATE * 64;
+      const float mk = pr[(DT * 16) * 64 + lane];
+      const float fk = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - m_tot);
+      l_run += fk * pr[(DT * 16 + 1) * 64 + lane];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) o[dt][rr] += fk * pr[(dt * 16 + rr) * 64 + lane];
+    }
+  }
+
   if (!wave_live || q0 + ql >= a.T) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
@@ -255,21 +300,37 @@ attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) op[32 * dt + acc_row(r, lane)] = from_f32<T>(o[dt][r] * inv);
+    for (int rr = 0; rr < 16; ++rr) op[32 * dt + acc_row(rr, lane)] = from_f32<T>(o[dt][rr] * inv);
+}
+
+template <typename T, int D, int G, int QW, int KS>
+static void launch_attn_cfg(const AttnArgs &a, hipStream_t s) {
+  // LDS ring: 3 rounds when a round is small, else 2.
+  constexpr int ROUND = KS * 2 * 64 * D * (int)sizeof(T);
+  constexpr int S = (3 * ROUND <= 98304) ? 3 : 2;
+  const int nqb = (a.T + 32 * QW - 1) / (32 * QW);
+  hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, QW, KS, S>), dim3(nqb * a.B * a.n_kv), dim3(64 * G * QW * KS), 0, s, a);
 }
 
 template <typename T, int D, int G>
 static hipError_t launch_attn_g(const AttnArgs &a, hipStream_t s) {  // T: storage type
-  // LDS ring: 3 stages of K+V tiles (2 when a stage is 64 KB, float at d = 128).
-  constexpr int S = (2 * 64 * D * sizeof(T) >= 65536) ? 2 : 3;
-  // Two query sub-blocks per wave group when that still gives enough workgroups.
-  const long wg2 = (long)a.B * a.n_kv * ((a.T + 63) / 64);
-  if (G == 1 || wg2 >= 256) {
-    const int nqb = (a.T + 63) / 64;
-    hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, 2, S>), dim3(nqb * a.B * a.n_kv), dim3(64 * G * 2), 0, s, a);
+  // Short sequences have few key tiles per query block and too few workgroups to
+  // fill the chip: split each block's keys over 4 wave groups (one workgroup per
+  // 32 queries). Long ones have work enough; 64 queries per workgroup halve the
+  // K/V traffic per query.
+  // The split count is capped so that a 2-round ring of KS K+V tile pairs fits LDS.
+  constexpr int PAIR = 2 * 64 * D * (int)sizeof(T);
+  constexpr bool can4 = 2 * 4 * PAIR <= 160 * 1024 && G * 4 <= 16;
+  constexpr bool can2 = 2 * 2 * PAIR <= 160 * 1024 && G * 2 <= 16;
+  const int keys = a.T + a.q_key_off;
+  if (can4 && keys <= 1024) {
+    launch_attn_cfg<T, D, G, 1, can4 ? 4 : 1>(a, s);
+  } else if (can2 && keys <= 4096) {
+    launch_attn_cfg<T, D, G, 1, can2 ? 2 : 1>(a, s);
+  } else if (G == 1 || (long)a.B * a.n_kv * ((a.T + 63) / 64) >= 256) {
+    launch_attn_cfg<T, D, G, 2, 1>(a, s);
   } else {
-    const int nqb = (a.T + 31) / 32;
-    hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, 1, S>), dim3(nqb * a.B * a.n_kv), dim3(64 * G), 0, s, a);
+    launch_attn_cfg<T, D, G, 1, 1>(a, s);
   }
   return hipGetLastError();
 }

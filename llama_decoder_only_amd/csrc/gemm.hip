@@ -5,17 +5,30 @@
 // row for a 32x32x16 MFMA step. Weight rows arrive in the storage type W and are
 // converted to the activations' operand type Act<W> as their fragments leave LDS.
 //
-// A workgroup of four waves (2 x 2) owns a BM x BN tile; K is staged through an
-// S-deep ring of LDS stages, 128 bytes per row each, filled by direct global->LDS
-// copies (no register staging) that run S-1 stages ahead of the MFMAs; one barrier
-// per stage hands a filled slot to all waves and frees the slot just consumed.
-// Weight fragments are converted from W to the operand type as they leave LDS.
-// When the K loop ends, the
-// float accumulators go to LDS (reusing the staging buffers) and the epilogue
-// walks the tile row-major, so every global write is a contiguous 8- or 16-byte
-// vector and each epilogue sees whole rows of the tile:
+// A workgroup owns a BM x BN tile, computed by WM x WN waves, times KW groups of
+// waves that split each stage's K steps between them (more waves per SIMD to hide
+// the LDS -> convert -> MFMA chain when the grid is small; their partial sums are
+// added in a fixed order at the end). K is staged through an S-deep ring of LDS
+// stages (128 bytes of weights per row each), filled by direct global->LDS copies
+// (no register staging) that run S-1 stages ahead of the MFMAs; one barrier per
+// stage hands a filled slot to all waves and frees the slot just consumed.
+//
+// RMSNorm, deferred (u = w * x * r with r = 1 / sqrt(mean(x^2) + eps) per row,
+// abi96062 components.py, RMSNorm). A residual epilogue, which holds the updated
+// rows x only one BN-column slice at a time, cannot know r yet; it stores
+// xs = w_next * x * r_old, with r_old the row's r before this update (close to r,
+// so xs stays in the operand type's range at any scale of x), plus the row's sums
+// of squares per 64 columns. The GEMM that reads xs as A then scales each output
+// row by r / r_old, both taken from those partial sums, which makes its result
+// u B^T up to the one rounding of xs.
+//
+// When the K loop ends, the float accumulators go to LDS (reusing the staging
+// buffers) and the epilogue walks the tile row-major, so every global write is a
+// contiguous 8- or 16-byte vector and each epilogue sees whole rows of the tile:
 //   EPI_STORE     C = acc                          lm_head logits
-//   EPI_RESIDUAL  X += acc (float X)               o_proj / down_proj + residual
+//   EPI_RESIDUAL  X += acc (float X)               o_proj / down_proj + residual; also
+//                                                  xs and the new sums of squares for
+//                                                  the next norm
 //   EPI_SWIGLU    Y = silu(gate) * up              gate/up projection: tile columns
 //                                                  [0, BN/2) read gate rows and
 //                                                  [BN/2, BN) the matching up rows
@@ -42,7 +55,35 @@ struct GemmParams {
   int seq, cap, n_kv, pos0, kv_off, max_pos;
   const int *cache_len;
   float inv_freq[64];
+  // Row sums of squares of the residual stream, H/64 partials per row:
+  // ss[j * M + row] over columns [64 j, 64 j + 64).
+  //   A GEMM on xs (EPI != EPI_RESIDUAL, ss_new != nullptr): output row scaled by
+  //   r(ss_new) / r(ss_old).
+  //   EPI_RESIDUAL: writes ss_new of the updated X when ss_new != nullptr, and, when
+  //   xs != nullptr, xs = norm_w * X * r(ss_old).
+  const float *ss_old;
+  float *ss_new;
+  const void *norm_w;
+  void *xs;
+  int ss_cols;  // H
+  float eps;
 };
+
+// r = 1 / sqrt(mean(x^2) + eps) of one row from its H/64 partial sums of squares,
+// added in part order (16 loads in flight per round; indices clamped in bounds and
+// the extras masked out of the sum).
+__device__ __forceinline__ float row_r(const float *ss, int M, int row, int H, float eps) {
+  const int parts = H / 64;
+  float q = 0.f;
+  for (int q0 = 0; q0 < parts; q0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = ss[(size_t)min(q0 + e, parts - 1) * M + row];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) q += (q0 + e < parts) ? v[e] : 0.f;
+  }
+  return 1.0f / sqrtf(q / (float)H + eps);
+}
 
 // Source row of logical B column n.
 template <typename W, int EPI, int BN>
@@ -104,33 +145,49 @@ __device__ __forceinline__ Chunk16 lds_chunk(const char *row, int c, int sw) {
   return *reinterpret_cast<const Chunk16 *>(row + ((c ^ sw) << 4));
 }
 
-template <typename W, int BM, int BN, int EPI, int S>
-__global__ void __launch_bounds__(256)
+template <typename W, int BM, int BN, int WM, int WN, int RB, int EPI, int S, int KW>
+__global__ void __launch_bounds__(64 * WM * WN * KW)
 gemm_kernel(const GemmParams p) {
   using T = Act<W>;  // MFMA operand type; weight fragments convert from W as they are read
+  using TA = T;      // A element type as staged in LDS
   static_assert(sizeof(T) == sizeof(W), "storage and operand types have the same width");
-  constexpr int NT = 256;
-  constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 MFMA tiles per wave (2 x 2 waves)
-  constexpr int ROWS = BM + BN;              // LDS rows per stage: A rows, then B rows
-  constexpr int STAGE_BYTES = ROWS * 128;    // 128 bytes of K per row per stage
-  constexpr int IPW = ROWS / 32;             // DMA instructions per wave per stage (8 rows each)
-  constexpr int KE = 128 / sizeof(T);        // K elements per stage
+  constexpr int NWG = WM * WN;               // waves per K group
+  constexpr int NW = NWG * KW, NT = 64 * NW;
+  constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);  // 32x32 MFMA tiles per wave
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave layout must tile the block");
+  constexpr int KE = RB / sizeof(W);         // K elements per stage
+  constexpr int RA = KE * sizeof(TA);        // A bytes per row per stage
+  constexpr int CPRA = RA / 16, CPR = RB / 16;  // 16-byte chunks per A / B row per stage
+  constexpr int A_BYTES = BM * RA;           // stage layout: A rows, then B rows
+  constexpr int STAGE_BYTES = A_BYTES + BN * RB;
+  static_assert(A_BYTES % 1024 == 0 && (BN * RB) % 1024 == 0, "whole DMA instructions per operand");
+  static_assert(CPRA >= 8 && CPR >= 8, "the XOR swizzle spans 8 chunks");
+  constexpr int NINS = STAGE_BYTES / 1024;   // DMA wave-instructions per stage
+  constexpr int IPW = NINS / NW;             // per wave
+  static_assert(IPW * NW == NINS, "DMA instructions must split evenly over the waves");
   constexpr int KSTEPS = KE / 16;
-  constexpr int CPF = 16 * sizeof(T) / 16 / 2;  // 16-byte chunks per 8-element fragment (1 or 2)
+  static_assert(KSTEPS % KW == 0, "K groups split the stage's K steps evenly");
+  constexpr int CPF = sizeof(T) / 2;         // 16-byte chunks per 8-element fragment (1 or 2)
   constexpr int OP = BN + 4;                 // float pitch of the epilogue tile
-  // The epilogue walks the tile in row chunks of ER rows that fit the staging LDS.
-  constexpr int ER = (BM * OP * 4 <= S * STAGE_BYTES) ? BM : 32 * TM;
+  // The epilogue walks the tile in row chunks of ER rows (a multiple of 32) that fit
+  // the staging LDS.
+  constexpr int ER = (BM * OP * 4 <= S * STAGE_BYTES) ? BM
+                     : (BM / 2 * OP * 4 <= S * STAGE_BYTES) ? BM / 2
+                     : (BM / 4 * OP * 4 <= S * STAGE_BYTES) ? BM / 4 : 32;
   static_assert(ER * OP * 4 <= S * STAGE_BYTES, "epilogue chunk must fit the staging LDS");
   static_assert(S >= 2, "at least double buffering");
+  static_assert((S - 2) * IPW <= 63, "vmcnt counts at most 63 outstanding loads");
 
   __shared__ __attribute__((aligned(16))) char smem[S * STAGE_BYTES];
+  __shared__ float s_row[BM];  // per-row factor of the deferred RMSNorm (see GemmParams)
   float *tile = reinterpret_cast<float *>(smem);
   const uint32_t smem_base = lds_addr(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int kw = wave / NWG;                 // K group
+  const int wm = (wave % NWG) % WM, wn = (wave % NWG) / WM;
 
   // XCD-aware tile order (workgroup i runs on XCD i % 8; each XCD has its own L2
   // and whatever misses it streams at roughly HBM rate). Column ownership when the
@@ -162,24 +219,32 @@ gemm_kernel(const GemmParams p) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // DMA sources. Wave w's instruction j fills rows 8*(w*IPW + j) .. +7 of a stage;
-  // lane l writes slot l % 8 of row 8*(..) + l / 8 and so fetches the row's 16-byte
-  // chunk (l % 8) ^ (row & 7): an XOR swizzle that keeps fragment reads (32 rows,
+  // DMA sources. Stage byte q*1024 + 16*lane is written by wave instruction q:
+  // chunk index q*64 + lane -> (row, slot) of the A or B rows; the slot receives the
+  // row's chunk slot ^ (row & 7), an XOR swizzle that keeps fragment reads (32 rows,
   // one chunk each) free of bank conflicts without padding.
   const char *src[IPW];
+  int adv[IPW];  // bytes per stage along the source row
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int r = 8 * (wave * IPW + j) + (lane >> 3);
-    const int c = (lane & 7) ^ (r & 7);
-    if (r < BM)
-      src[j] = (const char *)((const T *)p.A + (size_t)min(m0 + r, p.M - 1) * p.lda) + c * 16;
-    else
-      src[j] = (const char *)b_row<W, EPI, BN>(p, n0 + r - BM) + c * 16;
+    const int cidx = (wave * IPW + j) * 64 + lane;
+    if (cidx < A_BYTES / 16) {
+      const int r = cidx / CPRA;
+      const int c = (cidx % CPRA) ^ (r & 7);
+      src[j] = (const char *)((const TA *)p.A + (size_t)min(m0 + r, p.M - 1) * p.lda) + c * 16;
+      adv[j] = RA;
+    } else {
+      const int cb = cidx - A_BYTES / 16;
+      const int r = cb / CPR;
+      const int c = (cb % CPR) ^ (r & 7);
+      src[j] = (const char *)b_row<W, EPI, BN>(p, n0 + r) + c * 16;
+      adv[j] = RB;
+    }
   }
   auto issue = [&](int stage, int slot) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j)
-      lds_dma16(src[j] + stage * 128, smem_base + slot * STAGE_BYTES + (8 * (wave * IPW + j)) * 128);
+      lds_dma16(src[j] + (size_t)stage * adv[j], smem_base + slot * STAGE_BYTES + (wave * IPW + j) * 1024);
   };
 
   f32x16 acc[TM][TN];
@@ -195,6 +260,18 @@ gemm_kernel(const GemmParams p) {
 
   const int sw = lane & 7;  // row & 7 for every fragment row this lane reads
   const int half = lane >> 5;
+
+  // Row factors of the deferred RMSNorm, for the epilogue (made visible by its first
+  // barrier). Loaded after the first stages are issued so that the latencies
+  // overlap; these loads are older than every later DMA, so the ring's vmcnt
+  // accounting holds (the compiler waits for them here, with stage 0).
+  const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
+  if (scaled && tid < BM) {
+    const int row = min(m0 + tid, p.M - 1);
+    const float r_old = row_r(p.ss_old, p.M, row, p.ss_cols, p.eps);
+    s_row[tid] = EPI == EPI_RESIDUAL ? r_old : row_r(p.ss_new, p.M, row, p.ss_cols, p.eps) / r_old;
+  }
+
   for (int kb = 0; kb < nk; ++kb) {
     // stage kb has landed (for this wave) once at most S-2 later stages are pending
     if (kb + S - 2 < nk)
@@ -203,15 +280,16 @@ gemm_kernel(const GemmParams p) {
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // ... and for every wave; also all reads of stage kb-1 are done
     if (kb + S - 1 < nk) issue(kb + S - 1, (kb + S - 1) % S);  // refill the slot of stage kb-1
-    const char *sa = smem + (kb % S) * STAGE_BYTES + (wm * 32 * TM + (lane & 31)) * 128;
-    const char *sb = smem + (kb % S) * STAGE_BYTES + (BM + wn * 32 * TN + (lane & 31)) * 128;
+    const char *sa = smem + (kb % S) * STAGE_BYTES + (wm * 32 * TM + (lane & 31)) * RA;
+    const char *sb = smem + (kb % S) * STAGE_BYTES + A_BYTES + (wn * 32 * TN + (lane & 31)) * RB;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
+    for (int t = 0; t < KSTEPS / KW; ++t) {
+      const int s = t * KW + kw;            // this group's K step within the stage
       Frag<T> fa[TM], fb[TN];
       const int c0 = (2 * s + half) * CPF;  // first chunk of this lane's 8 K values
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const char *row = sa + i * 32 * 128;
+        const char *row = sa + i * 32 * RA;
         if constexpr (CPF == 1) {
           const Chunk16 c = lds_chunk<T>(row, c0, sw);
           fa[i].v = __builtin_bit_cast(decltype(fa[i].v), c);
@@ -223,7 +301,7 @@ gemm_kernel(const GemmParams p) {
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const char *row = sb + j * 32 * 128;
+        const char *row = sb + j * 32 * RB;
         if constexpr (CPF == 1) {
           const Chunk16 c = to_operand<W>(lds_chunk<W>(row, c0, sw));
           fb[j].v = __builtin_bit_cast(decltype(fb[j].v), c);
@@ -243,22 +321,32 @@ gemm_kernel(const GemmParams p) {
 
   // ------------------------------------------------------------ accumulators -> LDS
   // Row chunk ec holds tile rows [ec*ER, ec*ER + ER): the waves whose rows fall in it
-  // write their accumulators, then the epilogue walks those rows.
+  // write their accumulators (K group KW-1 first, then each lower group adds its
+  // own, a fixed order), then the epilogue walks those rows.
 #pragma unroll
   for (int ec = 0; ec < BM / ER; ++ec) {
     const int r_lo = ec * ER;
-    if (ER == BM || wm == ec) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+    for (int g = KW - 1; g >= 0; --g) {
+      if (kw == g) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int i = 0; i < TM; ++i) {
+          const int rb = wm * 32 * TM + i * 32;  // first tile row of accumulator block i
+          if (rb < r_lo || rb >= r_lo + ER) continue;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            tile[(wm * 32 * TM + i * 32 + acc_row(r, lane) - r_lo) * OP + wn * 32 * TN + j * 32 + (lane & 31)] =
-                acc[i][j][r];
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float &t = tile[(rb + acc_row(r, lane) - r_lo) * OP + wn * 32 * TN + j * 32 + (lane & 31)];
+              t = (g == KW - 1) ? acc[i][j][r] : t + acc[i][j][r];
+            }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
     const int em0 = m0 + r_lo;  // first global row of this chunk
+    // deferred-RMSNorm factor of tile row r of this chunk (1 when not scaled)
+    auto rowf = [&](int r) { return (EPI != EPI_RESIDUAL && scaled) ? s_row[r_lo + r] : 1.0f; };
 
     // ------------------------------------------------------------ epilogue (row-major walk)
     if constexpr (EPI == EPI_STORE) {
@@ -267,14 +355,22 @@ gemm_kernel(const GemmParams p) {
         for (int it = tid; it < ER * BN / V; it += NT) {
           const int r = it / (BN / V), c = (it % (BN / V)) * V;
           if (em0 + r >= p.M) continue;
-          store_vec<float, V>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, &tile[r * OP + c]);
+          const float f = rowf(r);
+          float v[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
+          store_vec<float, V>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
         }
       } else {
         constexpr int V = 8;
         for (int it = tid; it < ER * BN / V; it += NT) {
           const int r = it / (BN / V), c = (it % (BN / V)) * V;
           if (em0 + r >= p.M) continue;
-          if constexpr (sizeof(W) == 2) store_vec<W, V>((W *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, &tile[r * OP + c]);
+          const float f = rowf(r);
+          float v[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
+          if constexpr (sizeof(W) == 2) store_vec<W, V>((W *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
         }
       }
     } else if constexpr (EPI == EPI_RESIDUAL) {
@@ -282,9 +378,26 @@ gemm_kernel(const GemmParams p) {
       for (int it = tid; it < ER * BN / V; it += NT) {
         const int r = it / (BN / V), c = (it % (BN / V)) * V;
         if (em0 + r >= p.M) continue;
-        f32x4 *x = reinterpret_cast<f32x4 *>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c);
+        const int row = em0 + r, col = n0 + c;
+        f32x4 *x = reinterpret_cast<f32x4 *>((float *)p.C + (size_t)row * p.ldc + col);
         const f32x4 t = *reinterpret_cast<const f32x4 *>(&tile[r * OP + c]);
-        *x = *x + t;
+        const f32x4 xn = *x + t;
+        *x = xn;
+        if (p.ss_new) {
+          // the 16 consecutive items (lanes) of one 64-column segment of a row
+          float q = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+#pragma unroll
+          for (int o = 8; o > 0; o >>= 1) q += __shfl_xor(q, o, 64);
+          if ((c & 63) == 0) p.ss_new[(size_t)(col >> 6) * p.M + row] = q;
+        }
+        if (scaled) {
+          const float r_old = s_row[r_lo + r];
+          const W *w = (const W *)p.norm_w + col;
+          float v[V];
+#pragma unroll
+          for (int e = 0; e < V; ++e) v[e] = to_f32(w[e]) * (xn[e] * r_old);
+          store_vec<T, V>((T *)p.xs + (size_t)row * p.ldc + col, v);
+        }
       }
     } else if constexpr (EPI == EPI_SWIGLU) {
       constexpr int HB = BN / 2;
@@ -293,9 +406,10 @@ gemm_kernel(const GemmParams p) {
       for (int it = tid; it < ER * HB / V; it += NT) {
         const int r = it / (HB / V), c = (it % (HB / V)) * V;
         if (em0 + r >= p.M) continue;
+        const float f = rowf(r);
         float y[V];
   #pragma unroll
-        for (int e = 0; e < V; ++e) y[e] = silu(tile[r * OP + c + e]) * tile[r * OP + HB + c + e];
+        for (int e = 0; e < V; ++e) y[e] = silu(tile[r * OP + c + e] * f) * (tile[r * OP + HB + c + e] * f);
         store_vec<T, V>((T *)p.C + (size_t)(em0 + r) * p.ldc + n0 / 2 + c, y);
       }
     } else if constexpr (EPI == EPI_QKV_ROPE) {
@@ -334,11 +448,12 @@ gemm_kernel(const GemmParams p) {
           idx = pos - p.kv_off;
         }
         const float *t = &tile[r * OP + hi * D];
+        const float f = rowf(r);
         float lo[4], up[4];
   #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lo[e] = t[e0 + e];
-          up[e] = t[HALF + e0 + e];
+          lo[e] = t[e0 + e] * f;
+          up[e] = t[HALF + e0 + e] * f;
         }
         if (kind != 2) {
   #pragma unroll
@@ -363,65 +478,103 @@ gemm_kernel(const GemmParams p) {
     }
     __syncthreads();  // the next chunk overwrites the tile
   }
+
 }
 
 // ---------------------------------------------------------------- launchers
 
-template <typename W, int BM, int BN, int EPI, int S>
-static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
-  if (p.N % BN != 0 || p.K % (128 / (int)sizeof(W)) != 0) return hipErrorInvalidValue;
-  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
-  int tiles;
-  switch (xcd_mode(p.M, p.N, BN)) {
-    case 1: tiles = SMOL_XCDS * ((tiles_n + SMOL_XCDS - 1) / SMOL_XCDS) * tiles_m; break;
-    case 2: tiles = SMOL_XCDS * (rows_per_xcd(p.M) / BM) * tiles_n; break;
-    default: tiles = tiles_m * tiles_n;
-  }
-  hipLaunchKernelGGL((gemm_kernel<W, BM, BN, EPI, S>), dim3(tiles), dim3(256), 0, s, p);
-  return hipGetLastError();
+// Whether a tile configuration meets the kernel's static requirements.
+template <typename W, int BM, int BN, int WM, int WN, int RB, int S, int KW>
+constexpr bool gemm_cfg_ok() {
+  constexpr int KE = RB / sizeof(W);
+  constexpr int stage = (BM + BN) * RB, nw = WM * WN * KW;
+  return BM % (32 * WM) == 0 && BN % (32 * WN) == 0 && (BM * RB) % 1024 == 0 && (BN * RB) % 1024 == 0 &&
+         RB >= 128 && (stage / 1024) % nw == 0 && (S - 2) * (stage / 1024 / nw) <= 63 && (KE / 16) % KW == 0 &&
+         S * stage <= 160 * 1024 && nw <= 16;
 }
 
-// Tile choice (measured on MI355X over the model's shapes: a 2-stage ring was never
-// slower than 3 or 4 stages): 128 x 128 when that still gives >= 2 workgroups per
-// CU (lm_head), else 128 x 64 under the same rule (gate/up), else 64 x 64 for
-// parallelism on small N (o_proj, down, QKV, every decode GEMM); 64 x 128 when a
-// 128-wide head must stay in one tile for RoPE.
+template <typename W, int BM, int BN, int WM, int WN, int RB, int EPI, int S, int KW>
+static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
+  if constexpr (!gemm_cfg_ok<W, BM, BN, WM, WN, RB, S, KW>()) {
+    return hipErrorInvalidConfiguration;
+  } else {
+    if (p.N % BN != 0 || p.K % (RB / (int)sizeof(W)) != 0) return hipErrorInvalidValue;
+    const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
+    if (scaled && (!p.ss_old || (EPI != EPI_RESIDUAL && p.ss_cols != p.K) || (EPI == EPI_RESIDUAL && !p.norm_w)))
+      return hipErrorInvalidValue;
+    if ((p.ss_new || scaled) && p.ss_cols % 64 != 0) return hipErrorInvalidValue;
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
+    int tiles;
+    switch (xcd_mode(p.M, p.N, BN)) {
+      case 1: tiles = SMOL_XCDS * ((tiles_n + SMOL_XCDS - 1) / SMOL_XCDS) * tiles_m; break;
+      case 2: tiles = SMOL_XCDS * (rows_per_xcd(p.M) / BM) * tiles_n; break;
+      default: tiles = tiles_m * tiles_n;
+    }
+    hipLaunchKernelGGL((gemm_kernel<W, BM, BN, WM, WN, RB, EPI, S, KW>), dim3(tiles), dim3(64 * WM * WN * KW), 0, s, p);
+    return hipGetLastError();
+  }
+}
+
+// Tile choice, from sweeps on MI355X over the model's shapes (2-stage rings were
+// never slower than deeper ones; 256-byte stages did not pay):
+//   * >= 512 tiles of 128 x 128: 128 x 128 with the four waves side by side along N,
+//     so each converted weight fragment feeds four MFMAs (lm_head);
+//   * >= 512 tiles of 64 x 128: the same 1 x 4 wave layout (gate/up);
+//   * otherwise 64 x 64 in a 2 x 2 wave layout, for parallelism on small N (o_proj,
+//     down, QKV and every decode GEMM); 64 x 128 when a 128-wide head must stay in one
+//     tile for RoPE.
+// Grids of a few hundred tiles leave one wave per SIMD, whose LDS -> convert -> MFMA
+// chain then runs exposed: those split each stage's K steps over two wave groups.
 template <typename T, int EPI>
 static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
-  const long tm128 = (p.M + 127) / 128;
-  const long t128 = (p.N % 128 == 0) ? tm128 * (p.N / 128) : 0;
-  if (t128 >= 512) return launch_cfg<T, 128, 128, EPI, 2>(p, s);
-  if (EPI == EPI_QKV_ROPE && p.head_dim == 128) return launch_cfg<T, 64, 128, EPI, 2>(p, s);
-  if (tm128 * (p.N / 64) >= 512) return launch_cfg<T, 128, 64, EPI, 2>(p, s);
-  return launch_cfg<T, 64, 64, EPI, 2>(p, s);
+  const long tm128 = (p.M + 127) / 128, tm64 = (p.M + 63) / 64;
+  if (p.N % 128 == 0 && tm128 * (p.N / 128) >= 512) return launch_cfg<T, 128, 128, 1, 4, 128, EPI, 2, 1>(p, s);
+  if (EPI == EPI_QKV_ROPE && p.head_dim == 128) return launch_cfg<T, 64, 128, 2, 2, 128, EPI, 2, 2>(p, s);
+  if (EPI != EPI_QKV_ROPE && p.N % 128 == 0 && tm64 * (p.N / 128) >= 512)
+    return launch_cfg<T, 64, 128, 1, 4, 128, EPI, 2, 2>(p, s);
+  return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 2, 2>(p, s);
+}
+
+static void set_norm_in(GemmParams &p, const NormIn &n, int H) {
+  p.ss_new = const_cast<float *>(n.ss_new);
+  p.ss_old = n.ss_old;
+  p.ss_cols = H;
+  p.eps = n.eps;
 }
 
 template <typename T>
-hipError_t gemm_store(const Act<T> *A, const T *B, int M, int N, int K, void *C, int c_f32, hipStream_t s) {
+hipError_t gemm_store(const Act<T> *A, const NormIn &nrm, const T *B, int M, int N, int K, void *C, int c_f32,
+                      hipStream_t s) {
   GemmParams p{};
   p.A = A; p.lda = K; p.B0 = B; p.M = M; p.N = N; p.K = K; p.C = C; p.ldc = N; p.c_f32 = c_f32;
+  set_norm_in(p, nrm, K);
   return launch_gemm<T, EPI_STORE>(p, s);
 }
 
 template <typename T>
-hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, hipStream_t s) {
+hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, const NormOut &nrm, hipStream_t s) {
   GemmParams p{};
   p.A = A; p.lda = K; p.B0 = B; p.M = M; p.N = N; p.K = K; p.C = X; p.ldc = N;
+  p.ss_old = nrm.ss_old; p.ss_new = nrm.ss_new; p.norm_w = nrm.w; p.xs = nrm.xs; p.ss_cols = N; p.eps = nrm.eps;
   return launch_gemm<T, EPI_RESIDUAL>(p, s);
 }
 
 template <typename T>
-hipError_t gemm_swiglu(const Act<T> *A, const T *Wg, const T *Wu, int M, int I, int K, Act<T> *Y, hipStream_t s) {
+hipError_t gemm_swiglu(const Act<T> *A, const NormIn &nrm, const T *Wg, const T *Wu, int M, int I, int K, Act<T> *Y,
+                       hipStream_t s) {
   GemmParams p{};
   p.A = A; p.lda = K; p.B0 = Wg; p.B1 = Wu; p.M = M; p.N = 2 * I; p.K = K; p.C = Y; p.ldc = I;
+  set_norm_in(p, nrm, K);
   return launch_gemm<T, EPI_SWIGLU>(p, s);
 }
 
 template <typename T>
-hipError_t gemm_qkv_rope(const Act<T> *A, const T *Wq, const T *Wk, const T *Wv, const QkvOut &o, hipStream_t s) {
+hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const T *Wk, const T *Wv, const QkvOut &o,
+                         hipStream_t s) {
   GemmParams p{};
   p.A = A; p.lda = o.hidden; p.B0 = Wq; p.B1 = Wk; p.B2 = Wv;
   p.M = o.M; p.N = o.nq_cols + 2 * o.nkv_cols; p.K = o.hidden;
+  set_norm_in(p, nrm, o.hidden);
   p.nq_cols = o.nq_cols; p.nkv_cols = o.nkv_cols; p.head_dim = o.head_dim;
   p.q_out = o.q; p.k_out = o.k; p.v_out = o.v;
   p.seq = o.seq; p.cap = o.cap; p.n_kv = o.n_kv; p.pos0 = o.pos0; p.kv_off = o.kv_off; p.max_pos = o.max_pos;
@@ -430,11 +583,15 @@ hipError_t gemm_qkv_rope(const Act<T> *A, const T *Wq, const T *Wk, const T *Wv,
   return launch_gemm<T, EPI_QKV_ROPE>(p, s);
 }
 
-#define SMOL_INST(T)                                                                                           \
-  template hipError_t gemm_store<T>(const Act<T> *, const T *, int, int, int, void *, int, hipStream_t);        \
-  template hipError_t gemm_residual<T>(const Act<T> *, const T *, int, int, int, float *, hipStream_t);          \
-  template hipError_t gemm_swiglu<T>(const Act<T> *, const T *, const T *, int, int, int, Act<T> *, hipStream_t); \
-  template hipError_t gemm_qkv_rope<T>(const Act<T> *, const T *, const T *, const T *, const QkvOut &, hipStream_t);
+#define SMOL_INST(T)                                                                                          \
+  template hipError_t gemm_store<T>(const Act<T> *, const NormIn &, const T *, int, int, int, void *, int,     \
+                                    hipStream_t);                                                              \
+  template hipError_t gemm_residual<T>(const Act<T> *, const T *, int, int, int, float *, const NormOut &,     \
+                                       hipStream_t);                                                           \
+  template hipError_t gemm_swiglu<T>(const Act<T> *, const NormIn &, const T *, const T *, int, int, int,      \
+                                     Act<T> *, hipStream_t);                                                   \
+  template hipError_t gemm_qkv_rope<T>(const Act<T> *, const NormIn &, const T *, const T *, const T *,        \
+                                       const QkvOut &, hipStream_t);
 SMOL_INST(float)
 SMOL_INST(bf16)
 

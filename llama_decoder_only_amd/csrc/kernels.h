@@ -21,21 +21,45 @@ struct QkvOut {
   const float *inv_freq;  // host array, head_dim / 2 entries
 };
 
+// The deferred RMSNorm u = w * x * r, r = 1 / sqrt(mean(x^2) + eps) per row of the
+// float residual stream x [M, H]. Whoever updates x also leaves, for the next norm,
+//   xs [M, H] (operand type) = w * x * r_old, r_old: the row's r before the update;
+//   the row sums of squares of the new x as H/64 partials, ss[j * M + row] over
+//   columns [64 j, 64 j + 64) (ss_new; ss_old keeps those from before the update).
+// A GEMM with xs as its A operand scales output row m by r(ss_new) / r(ss_old).
+struct NormIn {
+  const float *ss_new, *ss_old;  // ss_new == nullptr: A is used as it is
+  float eps;
+};
+// What a residual GEMM leaves for the next norm: ss_new (nullptr: nothing) and, when
+// xs != nullptr, xs with norm weight w and r_old from ss_old.
+struct NormOut {
+  const float *ss_old;
+  float *ss_new;
+  const void *w;
+  void *xs;
+  float eps;
+};
+
 // T is the storage type (weights, cache, logits); activations are Act<T>.
 template <typename T>
-hipError_t gemm_store(const Act<T> *A, const T *B, int M, int N, int K, void *C, int c_f32, hipStream_t s);
+hipError_t gemm_store(const Act<T> *A, const NormIn &nrm, const T *B, int M, int N, int K, void *C, int c_f32,
+                      hipStream_t s);
 template <typename T>
-hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, hipStream_t s);
+hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, const NormOut &nrm, hipStream_t s);
 template <typename T>
-hipError_t gemm_swiglu(const Act<T> *A, const T *Wg, const T *Wu, int M, int I, int K, Act<T> *Y, hipStream_t s);
+hipError_t gemm_swiglu(const Act<T> *A, const NormIn &nrm, const T *Wg, const T *Wu, int M, int I, int K, Act<T> *Y,
+                       hipStream_t s);
 template <typename T>
-hipError_t gemm_qkv_rope(const Act<T> *A, const T *Wq, const T *Wk, const T *Wv, const QkvOut &o, hipStream_t s);
+hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const T *Wk, const T *Wv, const QkvOut &o,
+                         hipStream_t s);
 
+// x[m] = E[ids[m]] (ids != nullptr: the embedding gather) or x[m] = src[m], and what
+// the first deferred RMSNorm reads: the row sums of squares into both ss_new and
+// ss_old, and xs = w * x * r with the row's own r (w == nullptr: no xs).
 template <typename T>
-hipError_t rmsnorm(const float *x, const T *w, Act<T> *out, int M, int H, float eps, hipStream_t s);
-template <typename T>
-hipError_t embed_rows(const int32_t *ids, const T *E, float *x, int M, int H, int V, hipStream_t s);
-hipError_t copy_f32(const float *src, float *dst, size_t n, hipStream_t s);
+hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, float *ss_new, float *ss_old,
+                   const T *w, Act<T> *xs, float eps, int M, int H, int V, hipStream_t s);
 
 // Causal GQA attention over a [B, n_kv, cap, d] key/value store. Query t of
 // sequence b sits at key index t + q_key_off; it sees key indices <= that.
