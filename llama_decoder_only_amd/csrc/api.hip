@@ -94,7 +94,7 @@ size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Workspace carve-up. Offsets in bytes from ws.
 struct Ws {
-  size_t x, xs, q, k, v, o, y, ss_p, ss_q, part, total;
+  size_t x, xs, q, k, v, o, y, ss_p, ss_q, rope, part, total;
 };
 
 Ws layout(const Dims &D, int op, int B, int T) {
@@ -109,6 +109,7 @@ Ws layout(const Dims &D, int op, int B, int T) {
   w.y = take(M * D.I * D.esz);
   w.ss_p = take((size_t)(D.H / 64) * M * 4);  // row sums of squares of x per 64 columns,
   w.ss_q = take((size_t)(D.H / 64) * M * 4);  // two buffers: new and old alternate
+  w.rope = take(M * (D.d / 2) * 8);             // (cos, sin) of each row's RoPE angles
   if (op == SMOL_OP_DECODE) {
     int chunk;
     const int cap = std::min(T, D.max_pos);
@@ -186,7 +187,8 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, 
   float *ss_p = (float *)(c.ws + c.lay.ss_p), *ss_q = (float *)(c.ws + c.lay.ss_q);
 
   smol::QkvOut qo{M, D.H, D.nq * D.d, D.nkv * D.d, D.d, q, c.kc, c.vc,
-                  decode ? 1 : c.T, c.cap, D.nkv, c.pos0, c.kv_off, D.max_pos, c.cache_len, c.inv_freq};
+                  decode ? 1 : c.T, c.cap, D.nkv, c.pos0, c.kv_off, D.max_pos, c.cache_len,
+                  (const float2 *)(c.ws + c.lay.rope)};
   SMOL_LAUNCH(SMOL_K_QKV_ROPE, smol::gemm_qkv_rope<T>(xs, smol::NormIn{ss_p, ss_q, D.eps}, (const T *)w->wq,
                                                       (const T *)w->wk, (const T *)w->wv, qo, s));
   if (decode) {
@@ -235,12 +237,18 @@ smol_status head(const Dims &D, const smol_model_weights *w, int M, void *logits
   return SMOL_OK;
 }
 
-// x = E[ids] or x = src, with what the first block's deferred RMSNorm reads.
+// x = E[ids] or x = src, with what the first block's deferred RMSNorm reads and the
+// RoPE table of the call's rows (positions as LayerCtx c defines them).
 template <typename T>
-smol_status prologue(const Dims &D, const int32_t *ids, const T *E, const float *src, float *x, const T *attn_norm,
-                     int M, char *ws, const Ws &lay, hipStream_t s) {
-  SMOL_LAUNCH(SMOL_K_EMBED, smol::rows_ss<T>(ids, E, src, x, (float *)(ws + lay.ss_p), (float *)(ws + lay.ss_q),
-                                             attn_norm, (Act<T> *)(ws + lay.xs), D.eps, M, D.H, D.V, s));
+smol_status prologue(const LayerCtx &c, const int32_t *ids, const T *E, const float *src, float *x,
+                     const T *attn_norm, int M) {
+  const Dims &D = *c.D;
+  const hipStream_t s = c.s;
+  smol::RopeIn rope{(float2 *)(c.ws + c.lay.rope), D.d / 2, c.pos0, c.T, c.cache_len, {}};
+  for (int i = 0; i < D.d / 2; ++i) rope.inv_freq[i] = c.inv_freq[i];
+  SMOL_LAUNCH(SMOL_K_EMBED, smol::rows_ss<T>(ids, E, src, x, (float *)(c.ws + c.lay.ss_p),
+                                             (float *)(c.ws + c.lay.ss_q), attn_norm, (Act<T> *)(c.ws + c.lay.xs),
+                                             D.eps, M, D.H, D.V, rope, s));
   return SMOL_OK;
 }
 
@@ -261,7 +269,7 @@ smol_status block_impl(const Dims &D, const smol_layer_weights *w, const float *
     c.kc = ws + lay.k; c.vc = ws + lay.v; c.cap = T_; c.kv_off = pos0; c.q_key_off = 0;
   }
   fill_inv_freq(D, c.inv_freq);
-  smol_status st = prologue<T>(D, nullptr, nullptr, x_in, x_out, (const T *)w->attn_norm, B * T_, ws, lay, s);
+  smol_status st = prologue<T>(c, nullptr, nullptr, x_in, x_out, (const T *)w->attn_norm, B * T_);
   if (st != SMOL_OK) return st;
   return run_layer<T>(c, w, x_out, nullptr);
 }
@@ -271,8 +279,6 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
                          void *kc, void *vc, int cap, char *ws, const Ws &lay, hipStream_t s) {
   float *x = (float *)(ws + lay.x);
   const int M = B * T_;
-  smol_status st0 = prologue<T>(D, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, M, ws, lay, s);
-  if (st0 != SMOL_OK) return st0;
   LayerCtx c{};
   c.D = &D;
   c.ws = ws;
@@ -282,6 +288,8 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
   c.pos0 = 0;
   c.s = s;
   fill_inv_freq(D, c.inv_freq);
+  smol_status st0 = prologue<T>(c, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, M);
+  if (st0 != SMOL_OK) return st0;
   const size_t layer_elems = (size_t)B * D.nkv * cap * D.d;
   for (int l = 0; l < D.L; ++l) {
     if (kc) {
@@ -302,8 +310,6 @@ template <typename T>
 smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_t *ids, const int32_t *cache_len,
                         int B, void *kc, void *vc, int cap, void *logits, char *ws, const Ws &lay, hipStream_t s) {
   float *x = (float *)(ws + lay.x);
-  smol_status st0 = prologue<T>(D, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, B, ws, lay, s);
-  if (st0 != SMOL_OK) return st0;
   LayerCtx c{};
   c.D = &D;
   c.ws = ws;
@@ -314,6 +320,8 @@ smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_
   c.cache_len = cache_len;
   c.s = s;
   fill_inv_freq(D, c.inv_freq);
+  smol_status st0 = prologue<T>(c, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, B);
+  if (st0 != SMOL_OK) return st0;
   const size_t layer_elems = (size_t)B * D.nkv * cap * D.d;
   for (int l = 0; l < D.L; ++l) {
     c.kc = (char *)kc + l * layer_elems * D.esz;

@@ -54,7 +54,7 @@ struct GemmParams {
   void *q_out, *k_out, *v_out;
   int seq, cap, n_kv, pos0, kv_off, max_pos;
   const int *cache_len;
-  float inv_freq[64];
+  const float2 *rope;  // [M, head_dim / 2] (cos, sin) of each row's RoPE angles
   // Row sums of squares of the residual stream, H/64 partials per row:
   // ss[j * M + row] over columns [64 j, 64 j + 64).
   //   A GEMM on xs (EPI != EPI_RESIDUAL, ss_new != nullptr): output row scaled by
@@ -103,6 +103,12 @@ __device__ __forceinline__ const W *b_row(const GemmParams &p, int n) {
   }
 }
 
+// Position of GEMM row `row` in the QKV epilogue: cache_len[row] in a decode step
+// (one row per sequence), else pos0 + the row's index within its sequence.
+__device__ __forceinline__ int qkv_pos(const GemmParams &p, int row) {
+  return p.cache_len ? p.cache_len[row] : p.pos0 + row % p.seq;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // 1 = column ownership per XCD, 2 = row ownership, 0 = plain order.
@@ -138,8 +144,19 @@ __device__ __forceinline__ void store_vec(O *dst, const float *v) {
   }
 }
 
+// XOR swizzle of a staged row with CPR 16-byte chunks: chunk c of row r sits at slot
+// c ^ (r & 7). A fragment read (ds_read_b128) takes one chunk from each of 32
+// consecutive rows; measured on gfx950, that pattern then runs at the conflict-free
+// rate (about 9 clocks per wave instruction), while unswizzled 128-byte rows take
+// four times as long.
+template <int CPR>
+__host__ __device__ constexpr int lds_swz(int r) {
+  static_assert(CPR >= 8, "the swizzle spans 8 chunks");
+  return r & 7;
+}
+
 // Fragment of 8 consecutive K values of one row from a swizzled LDS stage row:
-// 16-byte chunk c of row r sits at slot c ^ (r & 7) (see gemm_kernel).
+// 16-byte chunk c of row r sits at slot c ^ lds_swz<CPR>(r) (see gemm_kernel).
 template <typename T>
 __device__ __forceinline__ Chunk16 lds_chunk(const char *row, int c, int sw) {
   return *reinterpret_cast<const Chunk16 *>(row + ((c ^ sw) << 4));
@@ -221,8 +238,8 @@ gemm_kernel(const GemmParams p) {
 
   // DMA sources. Stage byte q*1024 + 16*lane is written by wave instruction q:
   // chunk index q*64 + lane -> (row, slot) of the A or B rows; the slot receives the
-  // row's chunk slot ^ (row & 7), an XOR swizzle that keeps fragment reads (32 rows,
-  // one chunk each) free of bank conflicts without padding.
+  // row's chunk slot ^ lds_swz(row), an XOR swizzle that keeps fragment reads (32
+  // rows, one chunk each) free of bank conflicts without padding.
   const char *src[IPW];
   int adv[IPW];  // bytes per stage along the source row
 #pragma unroll
@@ -230,13 +247,13 @@ gemm_kernel(const GemmParams p) {
     const int cidx = (wave * IPW + j) * 64 + lane;
     if (cidx < A_BYTES / 16) {
       const int r = cidx / CPRA;
-      const int c = (cidx % CPRA) ^ (r & 7);
+      const int c = (cidx % CPRA) ^ lds_swz<CPRA>(r);
       src[j] = (const char *)((const TA *)p.A + (size_t)min(m0 + r, p.M - 1) * p.lda) + c * 16;
       adv[j] = RA;
     } else {
       const int cb = cidx - A_BYTES / 16;
       const int r = cb / CPR;
-      const int c = (cb % CPR) ^ (r & 7);
+      const int c = (cb % CPR) ^ lds_swz<CPR>(r);
       src[j] = (const char *)b_row<W, EPI, BN>(p, n0 + r) + c * 16;
       adv[j] = RB;
     }
@@ -253,19 +270,59 @@ gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
+  // Epilogue operands that come from memory, loaded now so that their latency hides
+  // under the K loop (older than every DMA below, so the ring's vmcnt accounting
+  // holds). Items as in the epilogue walks. Residual: the thread's X values (4 floats
+  // an item) and, for xs, the norm weights of those columns. QKV: the RoPE (cos, sin)
+  // of the item's 4 frequencies and, in a decode step, the row's position.
+  const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
+  constexpr int XPI = BM * BN / 4 / NT;
+  constexpr bool XPRE = EPI == EPI_RESIDUAL && ER == BM && XPI >= 1 && XPI <= 4 && XPI * NT * 4 == BM * BN;
+  f32x4 xpre[XPRE ? XPI : 1];
+  float wpre[XPRE ? XPI : 1][4];
+  if constexpr (XPRE) {
+#pragma unroll
+    for (int k = 0; k < XPI; ++k) {
+      const int it = tid + k * NT;
+      const int r = it / (BN / 4), c = (it % (BN / 4)) * 4;
+      xpre[k] = *reinterpret_cast<const f32x4 *>((const float *)p.C + (size_t)min(m0 + r, p.M - 1) * p.ldc + n0 + c);
+      if (scaled) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wpre[k][e] = to_f32(((const W *)p.norm_w)[n0 + c + e]);
+      }
+    }
+  }
+  constexpr int QPI = BM * (BN / 8) / NT;  // QKV items (4 rotation pairs) per thread
+  constexpr bool QPRE = EPI == EPI_QKV_ROPE && ER == BM && QPI >= 1 && QPI <= 2 && QPI * NT * 8 == BM * BN;
+  f32x4 cspre[QPRE ? QPI : 1][2];
+  int pospre[QPRE ? QPI : 1];
+  if constexpr (QPRE) {
+    const int HALF = p.head_dim / 2, per_row = BN / 8;
+#pragma unroll
+    for (int k = 0; k < QPI; ++k) {
+      const int it = tid + k * NT;
+      const int r = it / per_row, e0 = ((it % per_row) % (HALF / 4)) * 4;
+      const int row = min(m0 + r, p.M - 1);
+      const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.rope + (size_t)row * HALF + e0);
+      cspre[k][0] = cs[0];
+      cspre[k][1] = cs[1];
+      pospre[k] = p.cache_len ? p.cache_len[row] : 0;
+    }
+  }
+
   const int nk = p.K / KE;
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (st < nk) issue(st, st);
 
-  const int sw = lane & 7;  // row & 7 for every fragment row this lane reads
+  static_assert(CPRA == CPR, "A and B rows share the swizzle");
+  const int sw = lds_swz<CPR>(lane & 31);  // for every fragment row this lane reads (rows = lane mod 32)
   const int half = lane >> 5;
 
   // Row factors of the deferred RMSNorm, for the epilogue (made visible by its first
   // barrier). Loaded after the first stages are issued so that the latencies
   // overlap; these loads are older than every later DMA, so the ring's vmcnt
   // accounting holds (the compiler waits for them here, with stage 0).
-  const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
   if (scaled && tid < BM) {
     const int row = min(m0 + tid, p.M - 1);
     const float r_old = row_r(p.ss_old, p.M, row, p.ss_cols, p.eps);
@@ -375,13 +432,13 @@ gemm_kernel(const GemmParams p) {
       }
     } else if constexpr (EPI == EPI_RESIDUAL) {
       constexpr int V = 4;
-      for (int it = tid; it < ER * BN / V; it += NT) {
+      auto item = [&](int it, const f32x4 *pre, const float *wp) {
         const int r = it / (BN / V), c = (it % (BN / V)) * V;
-        if (em0 + r >= p.M) continue;
+        if (em0 + r >= p.M) return;
         const int row = em0 + r, col = n0 + c;
         f32x4 *x = reinterpret_cast<f32x4 *>((float *)p.C + (size_t)row * p.ldc + col);
         const f32x4 t = *reinterpret_cast<const f32x4 *>(&tile[r * OP + c]);
-        const f32x4 xn = *x + t;
+        const f32x4 xn = (pre ? *pre : *x) + t;
         *x = xn;
         if (p.ss_new) {
           // the 16 consecutive items (lanes) of one 64-column segment of a row
@@ -395,9 +452,15 @@ gemm_kernel(const GemmParams p) {
           const W *w = (const W *)p.norm_w + col;
           float v[V];
 #pragma unroll
-          for (int e = 0; e < V; ++e) v[e] = to_f32(w[e]) * (xn[e] * r_old);
+          for (int e = 0; e < V; ++e) v[e] = (wp ? wp[e] : to_f32(w[e])) * (xn[e] * r_old);
           store_vec<T, V>((T *)p.xs + (size_t)row * p.ldc + col, v);
         }
+      };
+      if constexpr (XPRE) {
+#pragma unroll
+        for (int k = 0; k < XPI; ++k) item(tid + k * NT, &xpre[k], wpre[k]);
+      } else {
+        for (int it = tid; it < ER * BN / V; it += NT) item(it, nullptr, nullptr);
       }
     } else if constexpr (EPI == EPI_SWIGLU) {
       constexpr int HB = BN / 2;
@@ -414,15 +477,14 @@ gemm_kernel(const GemmParams p) {
       }
     } else if constexpr (EPI == EPI_QKV_ROPE) {
       // Items: (row, head within the tile, 4 consecutive dims e0.. of the first half);
-      // each item rotates the pairs (e, e + d/2) for its 4 dims.
+      // each item rotates the pairs (e, e + d/2) for its 4 dims. BN / 8 items a row.
       const int D = p.head_dim, HALF = D / 2;
-      const int heads = BN / D;
-      const int per_row = heads * (HALF / 4);
-      for (int it = tid; it < ER * per_row; it += NT) {
+      const int per_row = BN / 8;
+      auto item = [&](int it, const f32x4 *cs_pre, int pos_pre) {
         const int r = it / per_row, rem = it % per_row;
         const int hi = rem / (HALF / 4), e0 = (rem % (HALF / 4)) * 4;
         const int row = em0 + r;
-        if (row >= p.M) continue;
+        if (row >= p.M) return;
         const int ncol = n0 + hi * D;  // first column of this head
         int kind, head;                // 0 = q, 1 = k, 2 = v
         if (ncol < p.nq_cols) {
@@ -435,17 +497,15 @@ gemm_kernel(const GemmParams p) {
           kind = 2;
           head = (ncol - p.nq_cols - p.nkv_cols) / D;
         }
-        int b, pos, idx;
+        int b, idx;
         bool valid = true;
         if (p.cache_len) {
           b = row;
-          pos = p.cache_len[b];
-          idx = pos;
-          valid = pos >= 0 && pos < p.cap && pos < p.max_pos;
+          idx = cs_pre ? pos_pre : p.cache_len[row];
+          valid = idx >= 0 && idx < p.cap && idx < p.max_pos;
         } else {
           b = row / p.seq;
-          pos = p.pos0 + (row - b * p.seq);
-          idx = pos - p.kv_off;
+          idx = qkv_pos(p, row) - p.kv_off;
         }
         const float *t = &tile[r * OP + hi * D];
         const float f = rowf(r);
@@ -456,13 +516,21 @@ gemm_kernel(const GemmParams p) {
           up[e] = t[HALF + e0 + e] * f;
         }
         if (kind != 2) {
+          f32x4 cs0, cs1;  // (cos, sin) of frequencies e0 .. e0 + 3
+          if (cs_pre) {
+            cs0 = cs_pre[0];
+            cs1 = cs_pre[1];
+          } else {
+            const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.rope + (size_t)row * HALF + e0);
+            cs0 = cs[0];
+            cs1 = cs[1];
+          }
+          const float c[4] = {cs0[0], cs0[2], cs1[0], cs1[2]}, sn[4] = {cs0[1], cs0[3], cs1[1], cs1[3]};
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float s, c;
-            sincosf((float)pos * p.inv_freq[e0 + e], &s, &c);
             const float a = lo[e], bb = up[e];
-            lo[e] = a * c - bb * s;
-            up[e] = bb * c + a * s;
+            lo[e] = a * c[e] - bb * sn[e];
+            up[e] = bb * c[e] + a * sn[e];
           }
         }
         if (kind == 0) {
@@ -474,11 +542,16 @@ gemm_kernel(const GemmParams p) {
           store_vec<W, 4>(dst + e0, lo);
           store_vec<W, 4>(dst + HALF + e0, up);
         }
+      };
+      if constexpr (QPRE) {
+#pragma unroll
+        for (int k = 0; k < QPI; ++k) item(tid + k * NT, cspre[k], pospre[k]);
+      } else {
+        for (int it = tid; it < ER * per_row; it += NT) item(it, nullptr, 0);
       }
     }
     __syncthreads();  // the next chunk overwrites the tile
   }
-
 }
 
 // ---------------------------------------------------------------- launchers
@@ -499,6 +572,7 @@ static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
     return hipErrorInvalidConfiguration;
   } else {
     if (p.N % BN != 0 || p.K % (RB / (int)sizeof(W)) != 0) return hipErrorInvalidValue;
+    if (EPI == EPI_QKV_ROPE && (p.head_dim > BN || BN % p.head_dim != 0)) return hipErrorInvalidValue;
     const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
     if (scaled && (!p.ss_old || (EPI != EPI_RESIDUAL && p.ss_cols != p.K) || (EPI == EPI_RESIDUAL && !p.norm_w)))
       return hipErrorInvalidValue;
@@ -528,7 +602,7 @@ static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
 template <typename T, int EPI>
 static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   const long tm128 = (p.M + 127) / 128, tm64 = (p.M + 63) / 64;
-  if (p.N % 128 == 0 && tm128 * (p.N / 128) >= 512) return launch_cfg<T, 128, 128, 1, 4, 128, EPI, 2, 1>(p, s);
+  if (p.N % 128 == 0 && tm128 * (p.N / 128) >= 512) return launch_cfg<T, 128, 128, 1, 4, 128, EPI, 2, 2>(p, s);
   if (EPI == EPI_QKV_ROPE && p.head_dim == 128) return launch_cfg<T, 64, 128, 2, 2, 128, EPI, 2, 2>(p, s);
   if (EPI != EPI_QKV_ROPE && p.N % 128 == 0 && tm64 * (p.N / 128) >= 512)
     return launch_cfg<T, 64, 128, 1, 4, 128, EPI, 2, 2>(p, s);
@@ -579,7 +653,8 @@ hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const 
   p.q_out = o.q; p.k_out = o.k; p.v_out = o.v;
   p.seq = o.seq; p.cap = o.cap; p.n_kv = o.n_kv; p.pos0 = o.pos0; p.kv_off = o.kv_off; p.max_pos = o.max_pos;
   p.cache_len = o.cache_len;
-  for (int i = 0; i < o.head_dim / 2 && i < 64; ++i) p.inv_freq[i] = o.inv_freq[i];
+  p.rope = o.rope;
+  if (!o.rope || o.head_dim % 8 != 0) return hipErrorInvalidValue;
   return launch_gemm<T, EPI_QKV_ROPE>(p, s);
 }
 

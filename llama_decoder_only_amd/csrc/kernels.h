@@ -18,7 +18,7 @@ struct QkvOut {
   void *q, *k, *v;
   int seq, cap, n_kv, pos0, kv_off, max_pos;
   const int *cache_len;
-  const float *inv_freq;  // host array, head_dim / 2 entries
+  const float2 *rope;     // [M, head_dim / 2] (cos, sin) of each row's angles (RopeIn)
 };
 
 // The deferred RMSNorm u = w * x * r, r = 1 / sqrt(mean(x^2) + eps) per row of the
@@ -57,9 +57,18 @@ hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const 
 // x[m] = E[ids[m]] (ids != nullptr: the embedding gather) or x[m] = src[m], and what
 // the first deferred RMSNorm reads: the row sums of squares into both ss_new and
 // ss_old, and xs = w * x * r with the row's own r (w == nullptr: no xs).
+// The RoPE angles of every row, computed once per forward: cs[row * half + i] =
+// (cos, sin)(pos(row) * inv_freq[i]), pos(row) = cache_len[row] when cache_len != nullptr
+// (a decode step) else pos0 + row % seq.
+struct RopeIn {
+  float2 *cs;  // nullptr: none
+  int half, pos0, seq;
+  const int *cache_len;
+  float inv_freq[64];
+};
 template <typename T>
 hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, float *ss_new, float *ss_old,
-                   const T *w, Act<T> *xs, float eps, int M, int H, int V, hipStream_t s);
+                   const T *w, Act<T> *xs, float eps, int M, int H, int V, const RopeIn &rope, hipStream_t s);
 
 // Causal GQA attention over a [B, n_kv, cap, d] key/value store. Query t of
 // sequence b sits at key index t + q_key_off; it sees key indices <= that.

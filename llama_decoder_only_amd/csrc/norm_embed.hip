@@ -11,15 +11,23 @@ namespace smol {
 // One wavefront per row: x[row] = E[ids[row]] (ids != nullptr) or x[row] = src[row];
 // the row's sums of squares per 64 columns into ss_new and ss_old ([H/64, M]); and,
 // when w != nullptr, xs[row] = w * x * r with the row's r -- the input of the first
-// deferred RMSNorm. An id outside [0, V) makes the row (and its sums) NaN.
+// deferred RMSNorm; and the row's RoPE (cos, sin) table (RopeIn). An id outside
+// [0, V) makes the row (and its sums) NaN.
 template <typename T>
 __global__ void __launch_bounds__(256)
 rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const float *src, float *x,
                float *__restrict__ ss_new, float *__restrict__ ss_old, const T *__restrict__ w,
-               Act<T> *__restrict__ xs, float eps, int M, int H, int V) {
+               Act<T> *__restrict__ xs, float eps, int M, int H, int V, const RopeIn rope) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
+  if (rope.cs && lane < rope.half) {
+    // RoPE angle i of this row (abi96062 components.py, RotaryEmbedding: pos * omega_i)
+    const int pos = rope.cache_len ? rope.cache_len[row] : rope.pos0 + row % rope.seq;
+    float sn, cs;
+    sincosf((float)pos * rope.inv_freq[lane], &sn, &cs);
+    rope.cs[(size_t)row * rope.half + lane] = make_float2(cs, sn);
+  }
   float *xr = x + (size_t)row * H;
   const int id = ids ? ids[row] : 0;
   const bool bad = ids && (id < 0 || id >= V);
@@ -45,17 +53,17 @@ rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const f
 
 template <typename T>
 hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, float *ss_new, float *ss_old,
-                   const T *w, Act<T> *xs, float eps, int M, int H, int V, hipStream_t s) {
-  if (H % 64 != 0) return hipErrorInvalidValue;
+                   const T *w, Act<T> *xs, float eps, int M, int H, int V, const RopeIn &rope, hipStream_t s) {
+  if (H % 64 != 0 || rope.half > 64 || (rope.cs && !rope.cache_len && rope.seq <= 0)) return hipErrorInvalidValue;
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL((rows_ss_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, s, ids, E, src, x, ss_new, ss_old, w, xs,
-                     eps, M, H, V);
+                     eps, M, H, V, rope);
   return hipGetLastError();
 }
 
 template hipError_t rows_ss<float>(const int32_t *, const float *, const float *, float *, float *, float *,
-                                   const float *, float *, float, int, int, int, hipStream_t);
+                                   const float *, float *, float, int, int, int, const RopeIn &, hipStream_t);
 template hipError_t rows_ss<bf16>(const int32_t *, const bf16 *, const float *, float *, float *, float *, const bf16 *,
-                                  f16 *, float, int, int, int, hipStream_t);
+                                  f16 *, float, int, int, int, const RopeIn &, hipStream_t);
 
 }  // namespace smol
