@@ -73,8 +73,9 @@ def _time_steps(fn, steps, torch):
 
 
 def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
-    """Average duration (ms) of one kernel class over one eager step, from HIP events the
-    library records around each of its launches on the launch stream."""
+    """Summed duration (ms) and count of one kernel class's launches over one eager step,
+    from the start/stop events the HIP runtime records at each of those dispatches
+    (the library launches them with hipExtLaunchKernelGGL while timing is on)."""
     torch.cuda.synchronize()
     B.smol_timing_begin(kernel, max_launches)
     run_once()
@@ -177,7 +178,7 @@ def main():
     tokens = s.batch * s.seq
     value = tokens / step_s
 
-    # per-kernel-class durations from HIP events (eager step on the same stream)
+    # per-kernel-class durations from dispatch events (eager step on the same stream)
     kern = {}
     with torch.cuda.stream(stream):
         for name in ("qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head", "embed"):

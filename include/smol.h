@@ -134,9 +134,11 @@ const char *smol_last_error(void);
 
 /* Kernel-duration measurement (diagnostic, not for captured streams). After
  * smol_timing_begin(kernel, max_launches) the next launches of that kernel class
- * (smol_kernel) are bracketed by HIP events on their stream, up to max_launches.
- * smol_timing_end() waits for those events and returns the summed duration in
- * milliseconds and the number of launches timed (host pointers). SMOL_K_EMBED times
+ * (smol_kernel), up to max_launches, are timed by a start/stop event pair that the
+ * HIP runtime records at the kernel's dispatch (hipExtLaunchKernelGGL): the kernel's
+ * own execution time, as a kernel trace reports it. smol_timing_end() waits for
+ * those events and returns the summed duration in milliseconds and the number of
+ * launches timed (host pointers). SMOL_K_EMBED times
  * the kernel that starts the residual stream (embedding gather, or the copy of x_in
  * in smol_block_forward); SMOL_K_RMSNORM has no launches of its own, since every
  * RMSNorm is folded into the GEMMs around it. */

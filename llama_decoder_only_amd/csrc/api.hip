@@ -128,22 +128,31 @@ Ws layout(const Dims &D, int op, int B, int T) {
 struct Timing {
   std::mutex mu;
   int kernel = -1, max = 0, count = 0;
-  std::vector<hipEvent_t> ev;  // start/stop pairs
+  bool armed = false, used = false;  // a pair is offered to / taken by the next launch
+  std::vector<hipEvent_t> ev;        // start/stop pairs
 } g_timing;
 
 }  // namespace
 
 namespace smol {
 
-void timing_before(int kernel, hipStream_t s) {
-  if (g_timing.kernel != kernel || g_timing.count >= g_timing.max) return;
-  (void)hipEventRecord(g_timing.ev[2 * g_timing.count], s);
+void timing_before(int kernel, hipStream_t) {
+  g_timing.armed = g_timing.kernel == kernel && g_timing.count < g_timing.max;
+  g_timing.used = false;
 }
 
-void timing_after(int kernel, hipStream_t s) {
-  if (g_timing.kernel != kernel || g_timing.count >= g_timing.max) return;
-  (void)hipEventRecord(g_timing.ev[2 * g_timing.count + 1], s);
-  ++g_timing.count;
+bool timing_take(hipEvent_t *start, hipEvent_t *stop) {
+  if (!g_timing.armed) return false;
+  g_timing.armed = false;
+  g_timing.used = true;
+  *start = g_timing.ev[2 * g_timing.count];
+  *stop = g_timing.ev[2 * g_timing.count + 1];
+  return true;
+}
+
+void timing_after(int, hipStream_t) {
+  if (g_timing.used) ++g_timing.count;
+  g_timing.armed = g_timing.used = false;
 }
 
 }  // namespace smol
@@ -232,8 +241,8 @@ template <typename T>
 smol_status head(const Dims &D, const smol_model_weights *w, int M, void *logits, char *ws, const Ws &lay,
                  hipStream_t s) {
   const smol::NormIn fin{(const float *)(ws + lay.ss_p), (const float *)(ws + lay.ss_q), D.eps};
-  SMOL_LAUNCH(SMOL_K_LM_HEAD,
-              smol::gemm_store<T>((const Act<T> *)(ws + lay.xs), fin, (const T *)w->embed, M, D.V, D.H, logits, 0, s));
+  SMOL_LAUNCH(SMOL_K_LM_HEAD, smol::gemm_store<T>((const Act<T> *)(ws + lay.xs), fin, (const T *)w->embed, M, D.V, D.H,
+                                                  logits, 0, s));
   return SMOL_OK;
 }
 

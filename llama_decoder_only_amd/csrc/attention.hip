@@ -304,12 +304,12 @@ attn_prefill_kernel(const AttnArgs a) {
 }
 
 template <typename T, int D, int G, int QW, int KS>
-static void launch_attn_cfg(const AttnArgs &a, hipStream_t s) {
+static hipError_t launch_attn_cfg(const AttnArgs &a, hipStream_t s) {
   // LDS ring: 3 rounds when a round is small, else 2.
   constexpr int ROUND = KS * 2 * 64 * D * (int)sizeof(T);
   constexpr int S = (3 * ROUND <= 98304) ? 3 : 2;
   const int nqb = (a.T + 32 * QW - 1) / (32 * QW);
-  hipLaunchKernelGGL((attn_prefill_kernel<T, D, G, QW, KS, S>), dim3(nqb * a.B * a.n_kv), dim3(64 * G * QW * KS), 0, s, a);
+  return launch(attn_prefill_kernel<T, D, G, QW, KS, S>, dim3(nqb * a.B * a.n_kv), dim3(64 * G * QW * KS), s, a);
 }
 
 template <typename T, int D, int G>
@@ -323,16 +323,10 @@ static hipError_t launch_attn_g(const AttnArgs &a, hipStream_t s) {  // T: stora
   constexpr bool can4 = 2 * 4 * PAIR <= 160 * 1024 && G * 4 <= 16;
   constexpr bool can2 = 2 * 2 * PAIR <= 160 * 1024 && G * 2 <= 16;
   const int keys = a.T + a.q_key_off;
-  if (can4 && keys <= 1024) {
-    launch_attn_cfg<T, D, G, 1, can4 ? 4 : 1>(a, s);
-  } else if (can2 && keys <= 4096) {
-    launch_attn_cfg<T, D, G, 1, can2 ? 2 : 1>(a, s);
-  } else if (G == 1 || (long)a.B * a.n_kv * ((a.T + 63) / 64) >= 256) {
-    launch_attn_cfg<T, D, G, 2, 1>(a, s);
-  } else {
-    launch_attn_cfg<T, D, G, 1, 1>(a, s);
-  }
-  return hipGetLastError();
+  if (can4 && keys <= 1024) return launch_attn_cfg<T, D, G, 1, can4 ? 4 : 1>(a, s);
+  if (can2 && keys <= 4096) return launch_attn_cfg<T, D, G, 1, can2 ? 2 : 1>(a, s);
+  if (G == 1 || (long)a.B * a.n_kv * ((a.T + 63) / 64) >= 256) return launch_attn_cfg<T, D, G, 2, 1>(a, s);
+  return launch_attn_cfg<T, D, G, 1, 1>(a, s);
 }
 
 template <typename T, int D>

@@ -197,14 +197,13 @@ decode_combine_kernel(const DecodeAttnArgs a) {
 template <typename T, int D, int G>
 static hipError_t launch_dec(const DecodeAttnArgs &a, hipStream_t s) {
   timing_before(8, s);
-  hipLaunchKernelGGL((decode_attn_kernel<T, D, G>), dim3(a.splits, a.n_kv, a.B), dim3(DEC_THREADS), 0, s, a);
+  hipError_t e = launch(decode_attn_kernel<T, D, G>, dim3(a.splits, a.n_kv, a.B), dim3(DEC_THREADS), s, a);
   timing_after(8, s);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   timing_before(9, s);
-  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.B * a.n_heads), dim3(D), 0, s, a);
+  e = launch(decode_combine_kernel<T, D>, dim3(a.B * a.n_heads), dim3(D), s, a);
   timing_after(9, s);
-  return hipGetLastError();
+  return e;
 }
 
 template <typename T, int D>

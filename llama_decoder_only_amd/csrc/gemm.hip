@@ -258,6 +258,7 @@ gemm_kernel(const GemmParams p) {
       adv[j] = RB;
     }
   }
+  const int nk = p.K / KE;
   auto issue = [&](int stage, int slot) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j)
@@ -310,7 +311,6 @@ gemm_kernel(const GemmParams p) {
     }
   }
 
-  const int nk = p.K / KE;
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (st < nk) issue(st, st);
@@ -584,8 +584,7 @@ static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
       case 2: tiles = SMOL_XCDS * (rows_per_xcd(p.M) / BM) * tiles_n; break;
       default: tiles = tiles_m * tiles_n;
     }
-    hipLaunchKernelGGL((gemm_kernel<W, BM, BN, WM, WN, RB, EPI, S, KW>), dim3(tiles), dim3(64 * WM * WN * KW), 0, s, p);
-    return hipGetLastError();
+    return launch(gemm_kernel<W, BM, BN, WM, WN, RB, EPI, S, KW>, dim3(tiles), dim3(64 * WM * WN * KW), s, p);
   }
 }
 

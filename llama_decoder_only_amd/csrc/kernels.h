@@ -2,6 +2,7 @@
 // stream and returns hipGetLastError() of its launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,8 +95,23 @@ template <typename T>
 hipError_t attention_decode(const DecodeAttnArgs &a, hipStream_t s);
 int decode_splits(int cap, int *chunk);
 
-// kernel-class timing hooks (see smol_timing_begin)
+// Kernel-class timing (see smol_timing_begin). timing_before arms the next launch()
+// of that class with a start/stop event pair, which hipExtLaunchKernelGGL records at
+// the dispatch itself: the pair brackets the kernel's own execution, not the queue
+// around it. timing_after counts the launch.
 void timing_before(int kernel, hipStream_t s);
 void timing_after(int kernel, hipStream_t s);
+bool timing_take(hipEvent_t *start, hipEvent_t *stop);  // the armed pair, handed out once
+
+// Every kernel of the library starts here.
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0, e1;
+  if (timing_take(&e0, &e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
 
 }  // namespace smol

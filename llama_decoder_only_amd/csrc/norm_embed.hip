@@ -56,9 +56,8 @@ hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, f
                    const T *w, Act<T> *xs, float eps, int M, int H, int V, const RopeIn &rope, hipStream_t s) {
   if (H % 64 != 0 || rope.half > 64 || (rope.cs && !rope.cache_len && rope.seq <= 0)) return hipErrorInvalidValue;
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL((rows_ss_kernel<T>), dim3((M + 3) / 4), dim3(256), 0, s, ids, E, src, x, ss_new, ss_old, w, xs,
-                     eps, M, H, V, rope);
-  return hipGetLastError();
+  return launch(rows_ss_kernel<T>, dim3((M + 3) / 4), dim3(256), s, ids, E, src, x, ss_new, ss_old, w, xs, eps, M, H,
+                V, rope);
 }
 
 template hipError_t rows_ss<float>(const int32_t *, const float *, const float *, float *, float *, float *,
