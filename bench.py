@@ -83,6 +83,29 @@ def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
     return ms, n
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_prefill_b4s512_gemms.md")
+
+
+def measured_traffic(key: str):
+    """HBM bytes per launch of a kernel from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE passes scaled by a plain copy of known size), or None when the kernel
+    sources have changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("source-sha256: ", "source-files: ", key + ": ")))
+    if key not in fields or "source-sha256" not in fields or "source-files" not in fields:
+        return None
+    h = hashlib.sha256()
+    for f in fields["source-files"].split():
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return int(fields[key]) if h.hexdigest() == fields["source-sha256"].strip() else None
+
+
 def cpu_baseline(s, model, ids_np, budget_s=12.0):
     """The CPU oracle (numpy float64, as it stands) on whole sequences of the same prefill,
     one after another until about budget_s seconds have passed."""
@@ -117,6 +140,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (outside the timed region): "
+                         "a known-size reference for hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -153,6 +179,13 @@ def main():
             step()
     torch.cuda.synchronize()
     eager_ref = logits.clone()
+    if args.copy_check:
+        src = torch.ones(args.copy_check << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     eager_s = _time_steps(lambda: step(), args.steps, torch)
     graph_s = None
@@ -187,8 +220,11 @@ def main():
     dominant = max((k for k in kern if k in flops["per_launch"]), key=lambda k: kern[k]["total_ms"])
     avg_s = kern[dominant]["avg_us"] * 1e-6
     ach = flops["per_launch"][dominant] / avg_s / 1e12
+    traffic = measured_traffic("down-traffic-bytes-per-launch") if dominant == "down" else None
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "traffic_source": os.path.relpath(TRAFFIC_PROFILE, ROOT) if traffic is not None else None,
                 "algorithmic_flop_per_launch": flops["per_launch"][dominant],
                 "avg_launch_us": round(kern[dominant]["avg_us"], 2)}
 
