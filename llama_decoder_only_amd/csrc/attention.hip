@@ -83,6 +83,17 @@ attn_prefill_kernel(const AttnArgs a) {
     const T *qp = (const T *)a.q + (size_t)(b * a.T + qt) * ldq + h * D + half * 8;
 #pragma unroll
     for (int st = 0; st < DS; ++st) load_frag(qf[st], qp + 16 * st);
+    // Use the fragments once here, before the ring starts: the compiler then waits for
+    // these loads now. Left to their first use inside the key loop, its vmcnt waits
+    // (which also count the ring's DMAs, invisible to it) would stall every round on
+    // the loads just issued for a later round.
+    typedef uint32_t QWords __attribute__((ext_vector_type(sizeof(qf[0].v) / 4)));
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const QWords u = __builtin_bit_cast(QWords, qf[st].v);
+#pragma unroll
+      for (int i = 0; i < (int)(sizeof(QWords) / 4); ++i) asm volatile("" ::"v"(u[i]));
+    }
   }
 
   const int last_q = min(a.T - 1, qb * BQ + BQ - 1);
