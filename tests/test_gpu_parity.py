@@ -316,6 +316,46 @@ def test_decode_bf16_full_size():
     assert torch.equal(kc[5, :, :, :P], B.to_device(ks[5])[:, :, :P])
 
 
+def test_decode_bf16_ragged_lengths():
+    """Batch 48 with a different cache length per sequence: around the 256-key split
+    edges of the decode attention, at position 0, at the last slot of the cache, and
+    one with no room left (NaN logits, no cache write). Each valid sequence against
+    the oracle's decode of that sequence alone."""
+    s = S.workload("decode_bf16", n_layers=2, batch=48)
+    say("decode bf16 ragged cache lengths, B=48")
+    model = S.model_weights(s, 0)
+    md = B.upload_model(model)
+    cap = 600
+    edge = [0, 1, 63, 64, 255, 256, 257, 300, 511, 512, 513, cap - 1]
+    rng = np.random.default_rng(7)
+    lens = edge + [int(x) for x in rng.integers(0, cap, size=s.batch - len(edge) - 1)] + [cap]
+    ks, vs = [], []
+    kc = torch.empty(s.n_layers, s.batch, s.n_kv_heads, cap, s.head_dim, dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    for l in range(s.n_layers):
+        k, v = S.kv_cache_values(s, 0, l, cap)
+        ks.append(k)
+        vs.append(v)
+        kc[l] = B.to_device(k)
+        vc[l] = B.to_device(v)
+    ids_np = S.token_ids(s, 0, S.T_DECODE_IDS)[:, 0]
+    ids = torch.from_numpy(ids_np.copy()).to(DEV)
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    got = to_np(_decode(s, md, ids, cl, kc, vc))
+    om, oc = omodel(model), ocfg(s)
+    worst = 0.0
+    for b_, P in enumerate(lens[:-1]):
+        kb = [k.f64[b_:b_ + 1, :, :P] for k in ks]
+        vb = [v.f64[b_:b_ + 1, :, :P] for v in vs]
+        want, nk, nv = O.decode_step(ids_np[b_:b_ + 1], P, om, oc, kb, vb)
+        worst = max(worst, rel(got[b_:b_ + 1], want))
+        assert rel(to_np(kc[1, b_, :, P]), nk[1][0]) <= TOL_BF16
+    say(f"worst rel = {worst:.3e}")
+    assert worst <= TOL_BF16
+    assert np.isnan(got[-1]).all()
+    assert torch.equal(kc[:, -1], torch.stack([B.to_device(k)[-1] for k in ks]))
+
+
 def test_decode_invalid_cache_len_gives_nan_and_no_write():
     s = S.workload("model_f32", n_layers=2, batch=3, seq=1)
     say("decode invalid cache_len")
