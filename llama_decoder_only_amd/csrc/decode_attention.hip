@@ -183,13 +183,34 @@ decode_combine_kernel(const DecodeAttnArgs a) {
   }
   const float *part = a.part + ((size_t)b * a.n_heads + h) * a.splits * (D + 2);
   const int used = (P + a.chunk) / a.chunk;  // splits that hold keys 0 .. P
-  float m = -INFINITY;
-  for (int s = 0; s < used; ++s) m = fmaxf(m, part[s * (D + 2)]);
-  float l = 0.f, acc = 0.f;
-  for (int s = 0; s < used; ++s) {
-    const float f = exp2f(part[s * (D + 2)] - m);
-    l += f * part[s * (D + 2) + 1];
-    acc += f * part[s * (D + 2) + 2 + d];
+  // Online merge in rounds of R splits, every load of a round in flight at once
+  // (indices clamped in bounds, surplus entries masked out).
+  constexpr int R = 8;
+  float m = -INFINITY, l = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < used; s0 += R) {
+    float ms[R], ls[R], os[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const float *ps = part + (size_t)min(s0 + i, used - 1) * (D + 2);
+      ms[i] = ps[0];
+      ls[i] = ps[1];
+      os[i] = ps[2 + d];
+    }
+    float mr = m;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (s0 + i < used) mr = fmaxf(mr, ms[i]);
+    const float f = exp2f(m - mr);  // split 0 makes mr finite
+    l *= f;
+    acc *= f;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (s0 + i < used) {
+        const float fi = exp2f(ms[i] - mr);
+        l += fi * ls[i];
+        acc += fi * os[i];
+      }
+    m = mr;
   }
   *out = from_f32<A>(acc / l);
 }
