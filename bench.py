@@ -72,6 +72,63 @@ def _time_steps(fn, steps, torch):
     return (time.perf_counter() - t0) / steps
 
 
+def _rep_ms(fn, reps, torch, stream, before=None):
+    """Per-rep durations (ms) from events recorded on `stream` around each call of fn;
+    `before` runs (untimed) ahead of each rep."""
+    out = []
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            if before is not None:
+                before()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1))
+    return out
+
+
+def _pct(ms):
+    a = np.asarray(ms)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.median(a)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "reps": len(ms)}
+
+
+def ceilings(torch, dev):
+    """Achieved ceilings on this GPU, as context for the roofline fractions: a plain
+    device copy (bytes read + written per second) and a large bf16 GEMM through
+    torch.matmul (hipBLASLt, used as a black box)."""
+    n = 1 << 28  # 1 GiB of float32
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * 4 * n * 10 / (time.perf_counter() - t0) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        z = torch.matmul(x, y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        z = torch.matmul(x, y)
+    torch.cuda.synchronize()
+    gemm_tflops = 2 * m ** 3 * 10 / (time.perf_counter() - t0) / 1e12
+    del x, y, z
+    return {"copy_gbps": round(copy_gbps, 1), "copy_frac_of_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
+            "bf16_gemm_8192_tflops": round(gemm_tflops, 1),
+            "bf16_gemm_frac_of_peak": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+            "how": "torch copy_ of 1 GiB float32; torch.matmul 8192^3 bf16 (hipBLASLt)"}
+
+
 def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
     """Summed duration (ms) and count of one kernel class's launches over one eager step,
     from the start/stop events the HIP runtime records at each of those dispatches
@@ -206,6 +263,7 @@ def main():
         graph_s = _time_steps(lambda: g.replay(), args.steps, torch)
         mode = "hip_graph"
     step_s = graph_s if graph_s is not None else eager_s
+    rep_ms = _rep_ms((lambda: g.replay()) if graph_s is not None else step, args.steps, torch, stream)
 
     flops = prefill_flops(s)
     tokens = s.batch * s.seq
@@ -247,6 +305,7 @@ def main():
         "mfma_frac": round(flops["total"] / step_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         "algorithmic_gflop_per_step": round(flops["total"] / 1e9, 2),
         "eager_ms_per_step": round(eager_s * 1e3, 4),
+        "rep_ms": _pct(rep_ms),
         "roofline": roofline,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
     }
@@ -286,7 +345,13 @@ def main():
                     raise RuntimeError("decode graph replay differs from the eager result")
             dfn = dg.replay
             dmode = "hip_graph"
-        d_s = _time_steps(dfn, args.decode_steps, torch)
+        # warm: steps back to back; cold (the headline): MALL and L2 flushed by a 512 MiB
+        # write before each step
+        warm_s = _time_steps(dfn, args.decode_steps, torch)
+        flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        cold_ms = _rep_ms(dfn, args.decode_steps, torch, stream, before=lambda: flush.fill_(1.0))
+        del flush
+        d_s = float(np.median(cold_ms)) * 1e-3
         db = decode_bytes(sd, P)
         with torch.cuda.stream(stream):
             ms, n = _kernel_time(B, "decode_attention", dstep, torch)
@@ -294,8 +359,11 @@ def main():
         att_gbps = db["decode_attention_per_launch"] / att_s / 1e9
         out["decode"] = {
             "workload": "decode step: batch 64, 2047 cached positions (+1 new), 30 layers, bf16",
-            "timing": dmode,
+            "timing": dmode + ", cold: MALL/L2 flushed by a 512 MiB write before each step (median)",
             "ms_per_step": round(d_s * 1e3, 4),
+            "rep_ms_cold": _pct(cold_ms),
+            "warm_ms_per_step": round(warm_s * 1e3, 4),
+            "warm_hbm_gbps": round(db["total"] / warm_s / 1e9, 1),
             "tokens_per_s": round(sd.batch / d_s, 1),
             "algorithmic_gb_per_step": round(db["total"] / 1e9, 4),
             "hbm_gbps": round(db["total"] / d_s / 1e9, 1),
@@ -306,6 +374,9 @@ def main():
                          "avg_launch_us": round(att_s * 1e6, 2)},
         }
         del kc, vc
+
+    if not args.no_decode:
+        out["ceilings"] = ceilings(torch, dev)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(s, model, ids_np)
