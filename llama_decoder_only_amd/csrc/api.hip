@@ -94,7 +94,7 @@ size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Workspace carve-up. Offsets in bytes from ws.
 struct Ws {
-  size_t x, xs, q, k, v, o, y, ss_p, ss_q, rope, part, total;
+  size_t x, xs, q, k, v, o, y, ss_p, ss_q, rope, part, gpart, total;
 };
 
 Ws layout(const Dims &D, int op, int B, int T) {
@@ -110,6 +110,13 @@ Ws layout(const Dims &D, int op, int B, int T) {
   w.ss_p = take((size_t)(D.H / 64) * M * 4);  // row sums of squares of x per 64 columns,
   w.ss_q = take((size_t)(D.H / 64) * M * 4);  // two buffers: new and old alternate
   w.rope = take(M * (D.d / 2) * 8);             // (cos, sin) of each row's RoPE angles
+  {  // K-split partial sums of the GEMMs that split (few tiles: small M), shared in turn
+    const int m = (int)M, e = (int)D.esz;
+    const size_t f = std::max({smol::gemm_part_floats(m, D.nq * D.d + 2 * D.nkv * D.d, D.H, e),
+                               smol::gemm_part_floats(m, D.H, D.nq * D.d, e), smol::gemm_part_floats(m, 2 * D.I, D.H, e),
+                               smol::gemm_part_floats(m, D.H, D.I, e), smol::gemm_part_floats(m, D.V, D.H, e)});
+    w.gpart = take(f * 4);
+  }
   if (op == SMOL_OP_DECODE) {
     int chunk;
     const int cap = std::min(T, D.max_pos);
@@ -194,12 +201,13 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, 
   A *o = (A *)(c.ws + c.lay.o);
   A *y = (A *)(c.ws + c.lay.y);
   float *ss_p = (float *)(c.ws + c.lay.ss_p), *ss_q = (float *)(c.ws + c.lay.ss_q);
+  float *gpart = (float *)(c.ws + c.lay.gpart);
 
   smol::QkvOut qo{M, D.H, D.nq * D.d, D.nkv * D.d, D.d, q, c.kc, c.vc,
                   decode ? 1 : c.T, c.cap, D.nkv, c.pos0, c.kv_off, D.max_pos, c.cache_len,
                   (const float2 *)(c.ws + c.lay.rope)};
   SMOL_LAUNCH(SMOL_K_QKV_ROPE, smol::gemm_qkv_rope<T>(xs, smol::NormIn{ss_p, ss_q, D.eps}, (const T *)w->wq,
-                                                      (const T *)w->wk, (const T *)w->wv, qo, s));
+                                                      (const T *)w->wk, (const T *)w->wv, qo, gpart, s));
   if (decode) {
     int chunk;
     const int splits = smol::decode_splits(std::min(c.cap, D.max_pos), &chunk);
@@ -213,12 +221,12 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, 
   }
   // x += o W_o^T; leaves xs for mlp_norm, the new sums in ss_q (ss_p: the old ones)
   SMOL_LAUNCH(SMOL_K_O_PROJ, smol::gemm_residual<T>(o, (const T *)w->wo, M, D.H, D.nq * D.d, x,
-                                                    smol::NormOut{ss_p, ss_q, w->mlp_norm, xs, D.eps}, s));
+                                                    smol::NormOut{ss_p, ss_q, w->mlp_norm, xs, D.eps}, gpart, s));
   SMOL_LAUNCH(SMOL_K_GATE_UP, smol::gemm_swiglu<T>(xs, smol::NormIn{ss_q, ss_p, D.eps}, (const T *)w->w_gate,
-                                                   (const T *)w->w_up, M, D.I, D.H, y, s));
+                                                   (const T *)w->w_up, M, D.I, D.H, y, gpart, s));
   // x += y W_d^T; leaves xs for next_norm, the new sums in ss_p (ss_q: the old ones)
   const smol::NormOut nxt{ss_q, next_norm ? ss_p : nullptr, next_norm, next_norm ? (void *)xs : nullptr, D.eps};
-  SMOL_LAUNCH(SMOL_K_DOWN, smol::gemm_residual<T>(y, (const T *)w->w_down, M, D.H, D.I, x, nxt, s));
+  SMOL_LAUNCH(SMOL_K_DOWN, smol::gemm_residual<T>(y, (const T *)w->w_down, M, D.H, D.I, x, nxt, gpart, s));
   return SMOL_OK;
 }
 
@@ -242,7 +250,7 @@ smol_status head(const Dims &D, const smol_model_weights *w, int M, void *logits
                  hipStream_t s) {
   const smol::NormIn fin{(const float *)(ws + lay.ss_p), (const float *)(ws + lay.ss_q), D.eps};
   SMOL_LAUNCH(SMOL_K_LM_HEAD, smol::gemm_store<T>((const Act<T> *)(ws + lay.xs), fin, (const T *)w->embed, M, D.V, D.H,
-                                                  logits, 0, s));
+                                                  logits, 0, (float *)(ws + lay.gpart), s));
   return SMOL_OK;
 }
 

@@ -15,7 +15,10 @@
 // (lane % 32) and half of that query's keys in registers: the row max / sum of
 // the online softmax needs only in-register reductions plus one exchange with
 // lane ^ 32. P then feeds O^T = V^T . P^T straight from those registers; the V^T
-// fragments come from transposing LDS reads (ds_read_b64_tr_b16).
+// fragments come from transposing LDS reads (ds_read_b64_tr_b16). A bf16 cache is
+// converted to the fp16 operand type once per staged round, in LDS, when waves walk
+// many rounds; with a 4-way key split (short key ranges, one or two rounds) each wave
+// converts the fragments it reads instead, which spares the extra barrier per round.
 // Keys come in tiles in increasing order, so tile 0 (always visible) fixes a
 // finite running max before any fully masked tile can occur.
 #include "common.h"
@@ -58,6 +61,7 @@ attn_prefill_kernel(const AttnArgs a) {
   constexpr int DS = D / 16;                       // MFMA K-steps over the head dim
   constexpr int DT = D / 32;                       // 32-row tiles of O^T
   constexpr int PSTATE = DT * 16 + 2;              // floats per lane of a partial state
+  constexpr bool LCONV = ES == 2 && KS < 4;        // convert each round in LDS on arrival
   static_assert(S >= 2, "ring depth");
   static_assert(KS == 1 || (KS - 1) * G * QW * PSTATE * 64 * 4 <= S * STAGE_BYTES, "partials fit the ring");
 
@@ -171,6 +175,16 @@ attn_prefill_kernel(const AttnArgs a) {
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // round r landed for every wave; slot of round r-1 is free
+    if constexpr (LCONV) {
+      // bf16 cache: convert the round's K and V tiles to the operand type once, in
+      // place (same width, same swizzled layout), instead of in every wave that reads
+      // them. The barrier waits for the LDS writes only: the DMA of a later round may
+      // still be in flight.
+      Chunk16 *t = reinterpret_cast<Chunk16 *>(smem + (r % S) * STAGE_BYTES);
+      for (int i = tid; i < STAGE_BYTES / 16; i += NW * 64) t[i] = to_operand<W>(t[i]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+    }
     if (r + S - 1 < nrounds) issue(r + S - 1, (r + S - 1) % S);
     const int kt = r * KS + ks;  // this wave's tile
     const char *ks_ptr = smem + (r % S) * STAGE_BYTES + ks * 2 * TILE_BYTES;
@@ -186,7 +200,8 @@ attn_prefill_kernel(const AttnArgs a) {
           const int row = 32 * i + ql;
           Frag<T> kf;
           if constexpr (ES == 2) {
-            const Chunk16 c = to_operand<W>(*reinterpret_cast<const Chunk16 *>(ks_ptr + koff[i][st]));
+            Chunk16 c = *reinterpret_cast<const Chunk16 *>(ks_ptr + koff[i][st]);
+            if constexpr (!LCONV) c = to_operand<W>(c);
             kf.v = __builtin_bit_cast(decltype(kf.v), c);
           } else {
             const Chunk16 lo = *reinterpret_cast<const Chunk16 *>(ks_ptr + swz<RB, ES>(row, 16 * st + half * 8));
@@ -248,8 +263,8 @@ attn_prefill_kernel(const AttnArgs a) {
             for (int pp = 0; pp < 2; ++pp) {
               const u16x4 t = lds_read_tr16(vs + voff[sg][dt][pp]);
               const uint32_t lo = (uint32_t)t[0] | ((uint32_t)t[1] << 16), hi = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
-              raw[2 * pp] = bf16x2_to_f16x2(lo);
-              raw[2 * pp + 1] = bf16x2_to_f16x2(hi);
+              raw[2 * pp] = LCONV ? lo : bf16x2_to_f16x2(lo);
+              raw[2 * pp + 1] = LCONV ? hi : bf16x2_to_f16x2(hi);
             }
             vf.v = __builtin_bit_cast(decltype(vf.v), raw);
           } else {

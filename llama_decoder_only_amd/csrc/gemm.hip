@@ -67,6 +67,10 @@ struct GemmParams {
   void *xs;
   int ss_cols;  // H
   float eps;
+  // K split (EPI_SPLIT): ksplit workgroups per tile, each over K / ksplit; split i
+  // writes its unscaled partial sums to part[i * M * N + row * N + col].
+  int ksplit;
+  float *part;
 };
 
 // r = 1 / sqrt(mean(x^2) + eps) of one row from its H/64 partial sums of squares,
@@ -162,12 +166,216 @@ __device__ __forceinline__ Chunk16 lds_chunk(const char *row, int c, int sw) {
   return *reinterpret_cast<const Chunk16 *>(row + ((c ^ sw) << 4));
 }
 
+// Epilogue operands that come from memory, loaded by a kernel before its main work
+// so that their latency hides under it. Items as in epilogue_rows' walks, item
+// tid + k * NT for k < XPI (QPI). Residual: the thread's X values (4 floats an item)
+// and, when scaled, the norm weights of those columns. QKV: the RoPE (cos, sin) of
+// the item's 4 frequencies and, in a decode step, the row's position.
+template <typename W, int BN, int NT, int XPI>
+__device__ __forceinline__ void prefetch_residual(const GemmParams &p, int m0, int n0, int tid, bool scaled,
+                                                  f32x4 *xpre, float (*wpre)[4]) {
+#pragma unroll
+  for (int k = 0; k < XPI; ++k) {
+    const int it = tid + k * NT;
+    const int r = it / (BN / 4), c = (it % (BN / 4)) * 4;
+    xpre[k] = *reinterpret_cast<const f32x4 *>((const float *)p.C + (size_t)min(m0 + r, p.M - 1) * p.ldc + n0 + c);
+    if (scaled) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wpre[k][e] = to_f32(((const W *)p.norm_w)[n0 + c + e]);
+    }
+  }
+}
+template <int BN, int NT, int QPI>
+__device__ __forceinline__ void prefetch_qkv(const GemmParams &p, int m0, int tid, f32x4 (*cspre)[2], int *pospre) {
+  const int HALF = p.head_dim / 2, per_row = BN / 8;
+#pragma unroll
+  for (int k = 0; k < QPI; ++k) {
+    const int it = tid + k * NT;
+    const int r = it / per_row, e0 = ((it % per_row) % (HALF / 4)) * 4;
+    const int row = min(m0 + r, p.M - 1);
+    const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.rope + (size_t)row * HALF + e0);
+    cspre[k][0] = cs[0];
+    cspre[k][1] = cs[1];
+    pospre[k] = p.cache_len ? p.cache_len[row] : 0;
+  }
+}
+
+// Deferred-RMSNorm factor of one row: r_old for a residual epilogue (it scales xs),
+// r(ss_new) / r(ss_old) for a GEMM that reads xs.
+template <int EPI>
+__device__ __forceinline__ float row_factor(const GemmParams &p, int row) {
+  const float r_old = row_r(p.ss_old, p.M, row, p.ss_cols, p.eps);
+  return EPI == EPI_RESIDUAL ? r_old : row_r(p.ss_new, p.M, row, p.ss_cols, p.eps) / r_old;
+}
+
+// The epilogue of ER rows of a tile, from the float accumulator sums in LDS (tile,
+// pitch OP, row r at tile + r * OP): em0 is the global row of tile row 0, n0 the
+// tile's first column, srow[r] the row's deferred-RMSNorm factor (read only when
+// scaled). XPI > 0 / QPI > 0: the residual / QKV operands from memory were
+// prefetched into xpre, wpre / cspre, pospre, XPI / QPI items per thread.
+template <typename W, int BN, int EPI, int NT, int ER, int OP, int XPI, int QPI>
+__device__ __forceinline__ void epilogue_rows(const GemmParams &p, const float *tile, const float *srow, bool scaled,
+                                              int em0, int n0, int tid, const f32x4 *xpre, const float (*wpre)[4],
+                                              const f32x4 (*cspre)[2], const int *pospre) {
+  using T = Act<W>;
+  // deferred-RMSNorm factor of tile row r of this chunk (1 when not scaled)
+  auto rowf = [&](int r) { return (EPI != EPI_RESIDUAL && scaled) ? srow[r] : 1.0f; };
+
+  // ------------------------------------------------------------ epilogue (row-major walk)
+  if constexpr (EPI == EPI_STORE) {
+    if (p.c_f32 || sizeof(W) == 4) {
+      constexpr int V = 4;
+      for (int it = tid; it < ER * BN / V; it += NT) {
+        const int r = it / (BN / V), c = (it % (BN / V)) * V;
+        if (em0 + r >= p.M) continue;
+        const float f = rowf(r);
+        float v[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
+        store_vec<float, V>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
+      }
+    } else {
+      constexpr int V = 8;
+      for (int it = tid; it < ER * BN / V; it += NT) {
+        const int r = it / (BN / V), c = (it % (BN / V)) * V;
+        if (em0 + r >= p.M) continue;
+        const float f = rowf(r);
+        float v[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
+        if constexpr (sizeof(W) == 2) store_vec<W, V>((W *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
+      }
+    }
+  } else if constexpr (EPI == EPI_RESIDUAL) {
+    constexpr int V = 4;
+    auto item = [&](int it, const f32x4 *pre, const float *wp) {
+      const int r = it / (BN / V), c = (it % (BN / V)) * V;
+      if (em0 + r >= p.M) return;
+      const int row = em0 + r, col = n0 + c;
+      f32x4 *x = reinterpret_cast<f32x4 *>((float *)p.C + (size_t)row * p.ldc + col);
+      const f32x4 t = *reinterpret_cast<const f32x4 *>(&tile[r * OP + c]);
+      const f32x4 xn = (pre ? *pre : *x) + t;
+      *x = xn;
+      if (p.ss_new) {
+        // the 16 consecutive items (lanes) of one 64-column segment of a row
+        float q = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) q += __shfl_xor(q, o, 64);
+        if ((c & 63) == 0) p.ss_new[(size_t)(col >> 6) * p.M + row] = q;
+      }
+      if (scaled) {
+        const float r_old = srow[r];
+        const W *w = (const W *)p.norm_w + col;
+        float v[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = (wp ? wp[e] : to_f32(w[e])) * (xn[e] * r_old);
+        store_vec<T, V>((T *)p.xs + (size_t)row * p.ldc + col, v);
+      }
+    };
+    if constexpr (XPI > 0) {
+#pragma unroll
+      for (int k = 0; k < XPI; ++k) item(tid + k * NT, &xpre[k], wpre[k]);
+    } else {
+      for (int it = tid; it < ER * BN / V; it += NT) item(it, nullptr, nullptr);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    constexpr int HB = BN / 2;
+    constexpr int V = 16 / sizeof(T);
+    static_assert(HB % V == 0, "output row segment");
+    for (int it = tid; it < ER * HB / V; it += NT) {
+      const int r = it / (HB / V), c = (it % (HB / V)) * V;
+      if (em0 + r >= p.M) continue;
+      const float f = rowf(r);
+      float y[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) y[e] = silu(tile[r * OP + c + e] * f) * (tile[r * OP + HB + c + e] * f);
+      store_vec<T, V>((T *)p.C + (size_t)(em0 + r) * p.ldc + n0 / 2 + c, y);
+    }
+  } else if constexpr (EPI == EPI_QKV_ROPE) {
+    // Items: (row, head within the tile, 4 consecutive dims e0.. of the first half);
+    // each item rotates the pairs (e, e + d/2) for its 4 dims. BN / 8 items a row.
+    const int D = p.head_dim, HALF = D / 2;
+    const int per_row = BN / 8;
+    auto item = [&](int it, const f32x4 *cs_pre, int pos_pre) {
+      const int r = it / per_row, rem = it % per_row;
+      const int hi = rem / (HALF / 4), e0 = (rem % (HALF / 4)) * 4;
+      const int row = em0 + r;
+      if (row >= p.M) return;
+      const int ncol = n0 + hi * D;  // first column of this head
+      int kind, head;                // 0 = q, 1 = k, 2 = v
+      if (ncol < p.nq_cols) {
+        kind = 0;
+        head = ncol / D;
+      } else if (ncol < p.nq_cols + p.nkv_cols) {
+        kind = 1;
+        head = (ncol - p.nq_cols) / D;
+      } else {
+        kind = 2;
+        head = (ncol - p.nq_cols - p.nkv_cols) / D;
+      }
+      int b, idx;
+      bool valid = true;
+      if (p.cache_len) {
+        b = row;
+        idx = cs_pre ? pos_pre : p.cache_len[row];
+        valid = idx >= 0 && idx < p.cap && idx < p.max_pos;
+      } else {
+        b = row / p.seq;
+        idx = qkv_pos(p, row) - p.kv_off;
+      }
+      const float *t = &tile[r * OP + hi * D];
+      const float f = rowf(r);
+      float lo[4], up[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = t[e0 + e] * f;
+        up[e] = t[HALF + e0 + e] * f;
+      }
+      if (kind != 2) {
+        f32x4 cs0, cs1;  // (cos, sin) of frequencies e0 .. e0 + 3
+        if (cs_pre) {
+          cs0 = cs_pre[0];
+          cs1 = cs_pre[1];
+        } else {
+          const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.rope + (size_t)row * HALF + e0);
+          cs0 = cs[0];
+          cs1 = cs[1];
+        }
+        const float c[4] = {cs0[0], cs0[2], cs1[0], cs1[2]}, sn[4] = {cs0[1], cs0[3], cs1[1], cs1[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = lo[e], bb = up[e];
+          lo[e] = a * c[e] - bb * sn[e];
+          up[e] = bb * c[e] + a * sn[e];
+        }
+      }
+      if (kind == 0) {
+        T *q = (T *)p.q_out + (size_t)row * p.nq_cols + head * D;
+        store_vec<T, 4>(q + e0, lo);
+        store_vec<T, 4>(q + HALF + e0, up);
+      } else if (valid) {
+        W *dst = (W *)(kind == 1 ? p.k_out : p.v_out) + (((size_t)b * p.n_kv + head) * p.cap + idx) * D;
+        store_vec<W, 4>(dst + e0, lo);
+        store_vec<W, 4>(dst + HALF + e0, up);
+      }
+    };
+    if constexpr (QPI > 0) {
+#pragma unroll
+      for (int k = 0; k < QPI; ++k) item(tid + k * NT, cspre[k], pospre[k]);
+    } else {
+      for (int it = tid; it < ER * per_row; it += NT) item(it, nullptr, 0);
+    }
+  }
+}
+
 template <typename W, int BM, int BN, int WM, int WN, int RB, int EPI, int S, int KW>
 __global__ void __launch_bounds__(64 * WM * WN * KW)
 gemm_kernel(const GemmParams p) {
   using T = Act<W>;  // MFMA operand type; weight fragments convert from W as they are read
   using TA = T;      // A element type as staged in LDS
   static_assert(sizeof(T) == sizeof(W), "storage and operand types have the same width");
+  constexpr int EK = EPI & ~EPI_SPLIT;          // the epilogue; its B row order
+  constexpr bool SPLIT = (EPI & EPI_SPLIT) != 0;  // K split over workgroups: partial sums out
   constexpr int NWG = WM * WN;               // waves per K group
   constexpr int NW = NWG * KW, NT = 64 * NW;
   constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);  // 32x32 MFMA tiles per wave
@@ -212,10 +420,12 @@ gemm_kernel(const GemmParams p) {
   // tiles, so every weight byte is fetched by one XCD only. Otherwise row
   // ownership (see xcd_rows): XCD x takes the M tiles of its row range. Within an
   // XCD, M runs fastest so that concurrent workgroups share a weight tile.
-  int tm, tn;
+  int tm, tn, split = 0;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
   const int local = blockIdx.x / SMOL_XCDS, xcd = blockIdx.x % SMOL_XCDS;
-  switch (xcd_mode(p.M, p.N, BN)) {
+  // K split (a grid of a few tiles): workgroup i takes tile i mod tiles, split
+  // i / tiles, so the tiles of one split (which share A) run side by side.
+  switch (SPLIT ? 3 : xcd_mode(p.M, p.N, BN)) {
     case 1: {  // columns
       const int ntx = (tiles_n + SMOL_XCDS - 1) / SMOL_XCDS;
       tm = local % tiles_m;
@@ -228,6 +438,13 @@ gemm_kernel(const GemmParams p) {
       tm = xcd * mtx + local % mtx;
       tn = local / mtx;
       if (tm >= tiles_m) return;  // whole workgroup
+      break;
+    }
+    case 3: {  // K split
+      const int t = blockIdx.x % (tiles_m * tiles_n);
+      split = blockIdx.x / (tiles_m * tiles_n);
+      tm = t % tiles_m;
+      tn = t / tiles_m;
       break;
     }
     default:
@@ -254,11 +471,15 @@ gemm_kernel(const GemmParams p) {
       const int cb = cidx - A_BYTES / 16;
       const int r = cb / CPR;
       const int c = (cb % CPR) ^ lds_swz<CPR>(r);
-      src[j] = (const char *)b_row<W, EPI, BN>(p, n0 + r) + c * 16;
+      src[j] = (const char *)b_row<W, EK, BN>(p, n0 + r) + c * 16;
       adv[j] = RB;
     }
   }
-  const int nk = p.K / KE;
+  const int nk = p.K / KE / (SPLIT ? p.ksplit : 1);  // stages of this workgroup
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) src[j] += (size_t)split * nk * adv[j];
+  }
   auto issue = [&](int stage, int slot) {
 #pragma unroll
     for (int j = 0; j < IPW; ++j)
@@ -276,40 +497,17 @@ gemm_kernel(const GemmParams p) {
   // holds). Items as in the epilogue walks. Residual: the thread's X values (4 floats
   // an item) and, for xs, the norm weights of those columns. QKV: the RoPE (cos, sin)
   // of the item's 4 frequencies and, in a decode step, the row's position.
-  const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
+  const bool scaled = SPLIT ? false : EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
   constexpr int XPI = BM * BN / 4 / NT;
   constexpr bool XPRE = EPI == EPI_RESIDUAL && ER == BM && XPI >= 1 && XPI <= 4 && XPI * NT * 4 == BM * BN;
   f32x4 xpre[XPRE ? XPI : 1];
   float wpre[XPRE ? XPI : 1][4];
-  if constexpr (XPRE) {
-#pragma unroll
-    for (int k = 0; k < XPI; ++k) {
-      const int it = tid + k * NT;
-      const int r = it / (BN / 4), c = (it % (BN / 4)) * 4;
-      xpre[k] = *reinterpret_cast<const f32x4 *>((const float *)p.C + (size_t)min(m0 + r, p.M - 1) * p.ldc + n0 + c);
-      if (scaled) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wpre[k][e] = to_f32(((const W *)p.norm_w)[n0 + c + e]);
-      }
-    }
-  }
+  if constexpr (XPRE) prefetch_residual<W, BN, NT, XPI>(p, m0, n0, tid, scaled, xpre, wpre);
   constexpr int QPI = BM * (BN / 8) / NT;  // QKV items (4 rotation pairs) per thread
   constexpr bool QPRE = EPI == EPI_QKV_ROPE && ER == BM && QPI >= 1 && QPI <= 2 && QPI * NT * 8 == BM * BN;
   f32x4 cspre[QPRE ? QPI : 1][2];
   int pospre[QPRE ? QPI : 1];
-  if constexpr (QPRE) {
-    const int HALF = p.head_dim / 2, per_row = BN / 8;
-#pragma unroll
-    for (int k = 0; k < QPI; ++k) {
-      const int it = tid + k * NT;
-      const int r = it / per_row, e0 = ((it % per_row) % (HALF / 4)) * 4;
-      const int row = min(m0 + r, p.M - 1);
-      const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.rope + (size_t)row * HALF + e0);
-      cspre[k][0] = cs[0];
-      cspre[k][1] = cs[1];
-      pospre[k] = p.cache_len ? p.cache_len[row] : 0;
-    }
-  }
+  if constexpr (QPRE) prefetch_qkv<BN, NT, QPI>(p, m0, tid, cspre, pospre);
 
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
@@ -323,11 +521,7 @@ gemm_kernel(const GemmParams p) {
   // barrier). Loaded after the first stages are issued so that the latencies
   // overlap; these loads are older than every later DMA, so the ring's vmcnt
   // accounting holds (the compiler waits for them here, with stage 0).
-  if (scaled && tid < BM) {
-    const int row = min(m0 + tid, p.M - 1);
-    const float r_old = row_r(p.ss_old, p.M, row, p.ss_cols, p.eps);
-    s_row[tid] = EPI == EPI_RESIDUAL ? r_old : row_r(p.ss_new, p.M, row, p.ss_cols, p.eps) / r_old;
-  }
+  if (scaled && tid < BM) s_row[tid] = row_factor<EPI>(p, min(m0 + tid, p.M - 1));
 
   for (int kb = 0; kb < nk; ++kb) {
     // stage kb has landed (for this wave) once at most S-2 later stages are pending
@@ -402,156 +596,74 @@ gemm_kernel(const GemmParams p) {
       __syncthreads();
     }
     const int em0 = m0 + r_lo;  // first global row of this chunk
-    // deferred-RMSNorm factor of tile row r of this chunk (1 when not scaled)
-    auto rowf = [&](int r) { return (EPI != EPI_RESIDUAL && scaled) ? s_row[r_lo + r] : 1.0f; };
-
-    // ------------------------------------------------------------ epilogue (row-major walk)
-    if constexpr (EPI == EPI_STORE) {
-      if (p.c_f32 || sizeof(W) == 4) {
-        constexpr int V = 4;
-        for (int it = tid; it < ER * BN / V; it += NT) {
-          const int r = it / (BN / V), c = (it % (BN / V)) * V;
-          if (em0 + r >= p.M) continue;
-          const float f = rowf(r);
-          float v[V];
-#pragma unroll
-          for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
-          store_vec<float, V>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
-        }
-      } else {
-        constexpr int V = 8;
-        for (int it = tid; it < ER * BN / V; it += NT) {
-          const int r = it / (BN / V), c = (it % (BN / V)) * V;
-          if (em0 + r >= p.M) continue;
-          const float f = rowf(r);
-          float v[V];
-#pragma unroll
-          for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
-          if constexpr (sizeof(W) == 2) store_vec<W, V>((W *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
-        }
+    if constexpr (SPLIT) {
+      // a K split's share of the tile, unscaled: the reduction applies the epilogue
+      float *P = p.part + (size_t)split * p.M * p.N;
+      for (int it = tid; it < ER * BN / 4; it += NT) {
+        const int r = it / (BN / 4), c = (it % (BN / 4)) * 4;
+        if (em0 + r < p.M) store_vec<float, 4>(P + (size_t)(em0 + r) * p.N + n0 + c, &tile[r * OP + c]);
       }
-    } else if constexpr (EPI == EPI_RESIDUAL) {
-      constexpr int V = 4;
-      auto item = [&](int it, const f32x4 *pre, const float *wp) {
-        const int r = it / (BN / V), c = (it % (BN / V)) * V;
-        if (em0 + r >= p.M) return;
-        const int row = em0 + r, col = n0 + c;
-        f32x4 *x = reinterpret_cast<f32x4 *>((float *)p.C + (size_t)row * p.ldc + col);
-        const f32x4 t = *reinterpret_cast<const f32x4 *>(&tile[r * OP + c]);
-        const f32x4 xn = (pre ? *pre : *x) + t;
-        *x = xn;
-        if (p.ss_new) {
-          // the 16 consecutive items (lanes) of one 64-column segment of a row
-          float q = xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3];
-#pragma unroll
-          for (int o = 8; o > 0; o >>= 1) q += __shfl_xor(q, o, 64);
-          if ((c & 63) == 0) p.ss_new[(size_t)(col >> 6) * p.M + row] = q;
-        }
-        if (scaled) {
-          const float r_old = s_row[r_lo + r];
-          const W *w = (const W *)p.norm_w + col;
-          float v[V];
-#pragma unroll
-          for (int e = 0; e < V; ++e) v[e] = (wp ? wp[e] : to_f32(w[e])) * (xn[e] * r_old);
-          store_vec<T, V>((T *)p.xs + (size_t)row * p.ldc + col, v);
-        }
-      };
-      if constexpr (XPRE) {
-#pragma unroll
-        for (int k = 0; k < XPI; ++k) item(tid + k * NT, &xpre[k], wpre[k]);
-      } else {
-        for (int it = tid; it < ER * BN / V; it += NT) item(it, nullptr, nullptr);
-      }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      constexpr int HB = BN / 2;
-      constexpr int V = 16 / sizeof(T);
-      static_assert(HB % V == 0, "output row segment");
-      for (int it = tid; it < ER * HB / V; it += NT) {
-        const int r = it / (HB / V), c = (it % (HB / V)) * V;
-        if (em0 + r >= p.M) continue;
-        const float f = rowf(r);
-        float y[V];
-  #pragma unroll
-        for (int e = 0; e < V; ++e) y[e] = silu(tile[r * OP + c + e] * f) * (tile[r * OP + HB + c + e] * f);
-        store_vec<T, V>((T *)p.C + (size_t)(em0 + r) * p.ldc + n0 / 2 + c, y);
-      }
-    } else if constexpr (EPI == EPI_QKV_ROPE) {
-      // Items: (row, head within the tile, 4 consecutive dims e0.. of the first half);
-      // each item rotates the pairs (e, e + d/2) for its 4 dims. BN / 8 items a row.
-      const int D = p.head_dim, HALF = D / 2;
-      const int per_row = BN / 8;
-      auto item = [&](int it, const f32x4 *cs_pre, int pos_pre) {
-        const int r = it / per_row, rem = it % per_row;
-        const int hi = rem / (HALF / 4), e0 = (rem % (HALF / 4)) * 4;
-        const int row = em0 + r;
-        if (row >= p.M) return;
-        const int ncol = n0 + hi * D;  // first column of this head
-        int kind, head;                // 0 = q, 1 = k, 2 = v
-        if (ncol < p.nq_cols) {
-          kind = 0;
-          head = ncol / D;
-        } else if (ncol < p.nq_cols + p.nkv_cols) {
-          kind = 1;
-          head = (ncol - p.nq_cols) / D;
-        } else {
-          kind = 2;
-          head = (ncol - p.nq_cols - p.nkv_cols) / D;
-        }
-        int b, idx;
-        bool valid = true;
-        if (p.cache_len) {
-          b = row;
-          idx = cs_pre ? pos_pre : p.cache_len[row];
-          valid = idx >= 0 && idx < p.cap && idx < p.max_pos;
-        } else {
-          b = row / p.seq;
-          idx = qkv_pos(p, row) - p.kv_off;
-        }
-        const float *t = &tile[r * OP + hi * D];
-        const float f = rowf(r);
-        float lo[4], up[4];
-  #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lo[e] = t[e0 + e] * f;
-          up[e] = t[HALF + e0 + e] * f;
-        }
-        if (kind != 2) {
-          f32x4 cs0, cs1;  // (cos, sin) of frequencies e0 .. e0 + 3
-          if (cs_pre) {
-            cs0 = cs_pre[0];
-            cs1 = cs_pre[1];
-          } else {
-            const f32x4 *cs = reinterpret_cast<const f32x4 *>(p.rope + (size_t)row * HALF + e0);
-            cs0 = cs[0];
-            cs1 = cs[1];
-          }
-          const float c[4] = {cs0[0], cs0[2], cs1[0], cs1[2]}, sn[4] = {cs0[1], cs0[3], cs1[1], cs1[3]};
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = lo[e], bb = up[e];
-            lo[e] = a * c[e] - bb * sn[e];
-            up[e] = bb * c[e] + a * sn[e];
-          }
-        }
-        if (kind == 0) {
-          T *q = (T *)p.q_out + (size_t)row * p.nq_cols + head * D;
-          store_vec<T, 4>(q + e0, lo);
-          store_vec<T, 4>(q + HALF + e0, up);
-        } else if (valid) {
-          W *dst = (W *)(kind == 1 ? p.k_out : p.v_out) + (((size_t)b * p.n_kv + head) * p.cap + idx) * D;
-          store_vec<W, 4>(dst + e0, lo);
-          store_vec<W, 4>(dst + HALF + e0, up);
-        }
-      };
-      if constexpr (QPRE) {
-#pragma unroll
-        for (int k = 0; k < QPI; ++k) item(tid + k * NT, cspre[k], pospre[k]);
-      } else {
-        for (int it = tid; it < ER * per_row; it += NT) item(it, nullptr, 0);
-      }
+    } else {
+      epilogue_rows<W, BN, EK, NT, ER, OP, XPRE ? XPI : 0, QPRE ? QPI : 0>(p, tile, s_row + r_lo, scaled, em0, n0, tid,
+                                                                          xpre, wpre, cspre, pospre);
     }
     __syncthreads();  // the next chunk overwrites the tile
   }
+}
+
+// The second half of a K-split GEMM: adds the ksplit partial tiles in split order
+// (a fixed order, so results do not depend on scheduling) and applies the epilogue.
+// A workgroup owns RM rows x BN columns; BN is the GEMM's tile width, so the SwiGLU
+// gate/up column pairing and the RoPE heads line up with the GEMM's tiles.
+template <typename W, int EPI, int BN, int RM, int NT>
+__global__ void __launch_bounds__(NT) gemm_reduce_kernel(const GemmParams p) {
+  constexpr int LPI = RM * BN / 4 / NT;  // float4 items of the tile per thread
+  static_assert(LPI >= 1 && LPI * NT * 4 == RM * BN, "threads cover the tile");
+  constexpr int OP = BN + 4;
+  __shared__ __attribute__((aligned(16))) float tile[RM * OP];
+  __shared__ float s_row[RM];
+  const int tid = threadIdx.x;
+  const int tiles_r = (p.M + RM - 1) / RM;
+  const int m0 = ((int)blockIdx.x % tiles_r) * RM, n0 = ((int)blockIdx.x / tiles_r) * BN;
+  const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
+
+  constexpr int XPI = LPI;
+  constexpr bool XPRE = EPI == EPI_RESIDUAL && XPI <= 4;
+  f32x4 xpre[XPRE ? XPI : 1];
+  float wpre[XPRE ? XPI : 1][4];
+  if constexpr (XPRE) prefetch_residual<W, BN, NT, XPI>(p, m0, n0, tid, scaled, xpre, wpre);
+  constexpr int QPI = RM * (BN / 8) / NT;
+  constexpr bool QPRE = EPI == EPI_QKV_ROPE && QPI >= 1 && QPI <= 2 && QPI * NT * 8 == RM * BN;
+  f32x4 cspre[QPRE ? QPI : 1][2];
+  int pospre[QPRE ? QPI : 1];
+  if constexpr (QPRE) prefetch_qkv<BN, NT, QPI>(p, m0, tid, cspre, pospre);
+
+  f32x4 acc[LPI];
+  const size_t split_stride = (size_t)p.M * p.N;
+#pragma unroll
+  for (int k = 0; k < LPI; ++k) {
+    const int it = tid + k * NT;
+    const int r = it / (BN / 4), c = (it % (BN / 4)) * 4;
+    const float *src = p.part + (size_t)min(m0 + r, p.M - 1) * p.N + n0 + c;
+    acc[k] = (f32x4){};
+    for (int s0 = 0; s0 < p.ksplit; s0 += 8) {  // 8 loads in flight; indices clamped, extras masked
+      f32x4 v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = *reinterpret_cast<const f32x4 *>(src + min(s0 + e, p.ksplit - 1) * split_stride);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (s0 + e < p.ksplit) acc[k] += v[e];
+    }
+  }
+  if (scaled && tid < RM) s_row[tid] = row_factor<EPI>(p, min(m0 + tid, p.M - 1));
+#pragma unroll
+  for (int k = 0; k < LPI; ++k) {
+    const int it = tid + k * NT;
+    *reinterpret_cast<f32x4 *>(&tile[(it / (BN / 4)) * OP + (it % (BN / 4)) * 4]) = acc[k];
+  }
+  __syncthreads();
+  epilogue_rows<W, BN, EPI, NT, RM, OP, XPRE ? XPI : 0, QPRE ? QPI : 0>(p, tile, s_row, scaled, m0, n0, tid, xpre, wpre,
+                                                                        cspre, pospre);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -566,18 +678,27 @@ constexpr bool gemm_cfg_ok() {
          S * stage <= 160 * 1024 && nw <= 16;
 }
 
+// What every launch of an epilogue EPI on BN-wide tiles with ke K values per stage
+// requires of the parameters.
+template <int EPI>
+static hipError_t check_params(const GemmParams &p, int BN, int ke) {
+  if (p.N % BN != 0 || p.K % ke != 0) return hipErrorInvalidValue;
+  if (EPI == EPI_QKV_ROPE && (p.head_dim > BN || BN % p.head_dim != 0 || !p.rope)) return hipErrorInvalidValue;
+  if (EPI == EPI_RESIDUAL && p.ss_new && BN % 64 != 0) return hipErrorInvalidValue;  // sums per 64 columns
+  const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
+  if (scaled && (!p.ss_old || (EPI != EPI_RESIDUAL && p.ss_cols != p.K) || (EPI == EPI_RESIDUAL && !p.norm_w)))
+    return hipErrorInvalidValue;
+  if ((p.ss_new || scaled) && p.ss_cols % 64 != 0) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
 template <typename W, int BM, int BN, int WM, int WN, int RB, int EPI, int S, int KW>
 static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
   if constexpr (!gemm_cfg_ok<W, BM, BN, WM, WN, RB, S, KW>()) {
     return hipErrorInvalidConfiguration;
   } else {
-    if (p.N % BN != 0 || p.K % (RB / (int)sizeof(W)) != 0) return hipErrorInvalidValue;
-    if (EPI == EPI_QKV_ROPE && (p.head_dim > BN || BN % p.head_dim != 0 || !p.rope)) return hipErrorInvalidValue;
-    if (EPI == EPI_RESIDUAL && p.ss_new && BN % 64 != 0) return hipErrorInvalidValue;  // sums per 64 columns
-    const bool scaled = EPI == EPI_RESIDUAL ? p.xs != nullptr : p.ss_new != nullptr;
-    if (scaled && (!p.ss_old || (EPI != EPI_RESIDUAL && p.ss_cols != p.K) || (EPI == EPI_RESIDUAL && !p.norm_w)))
-      return hipErrorInvalidValue;
-    if ((p.ss_new || scaled) && p.ss_cols % 64 != 0) return hipErrorInvalidValue;
+    const hipError_t e = check_params<EPI>(p, BN, RB / (int)sizeof(W));
+    if (e != hipSuccess) return e;
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
     int tiles;
     switch (xcd_mode(p.M, p.N, BN)) {
@@ -587,6 +708,56 @@ static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
     }
     return launch(gemm_kernel<W, BM, BN, WM, WN, RB, EPI, S, KW>, dim3(tiles), dim3(64 * WM * WN * KW), s, p);
   }
+}
+
+// K split for grids of few tiles (a decode step: M = batch). Such a grid streams all
+// the weights through the few CUs that own a tile, each at what one workgroup's
+// loads in flight allow (about 0.3 us per 128-byte stage). Dividing every 64 x 64
+// tile's K stages over ks workgroups (ks a divisor of the stage count, at most
+// SMOL_KSPLIT_MAX, at most 256 workgroups) spreads the weight stream over many CUs;
+// gemm_reduce_kernel then adds the ks partial tiles in a fixed order and runs the
+// epilogue. That second launch costs about 5 us (the floor of a dependent kernel
+// here: dispatch, a cold first load, the store drain), so only long K loops split:
+// measured at batch 64, the down projection (K = 1536, 24 stages) drops from 12.3
+// to 4.9 + 4.6 us, while K = 576 (9 stages) takes 8 us unsplit and 10-11 us split.
+#ifndef SMOL_KSPLIT_MAX
+#define SMOL_KSPLIT_MAX 8
+#endif
+constexpr int SMOL_KSPLIT_MIN_STAGES = 16;
+static int ksplit_plan(int M, int N, int K, int esz) {
+  if (N % 64 != 0) return 1;
+  const long tiles = (long)((M + 63) / 64) * (N / 64);
+  if (tiles >= 128) return 1;
+  const int nk = K / (128 / esz);
+  if (nk < SMOL_KSPLIT_MIN_STAGES) return 1;
+  int best = 1;
+  for (int ks = 2; ks <= SMOL_KSPLIT_MAX && ks <= nk; ++ks)
+    if (nk % ks == 0 && tiles * ks <= 256) best = ks;
+  return best;
+}
+
+size_t gemm_part_floats(int M, int N, int K, int esz) {
+  const int ks = ksplit_plan(M, N, K, esz);
+  return ks > 1 ? (size_t)ks * M * N : 0;
+}
+
+template <typename W, int EPI>
+static hipError_t launch_split(GemmParams p, int ks, hipStream_t s) {
+  constexpr int RB = 128;
+  hipError_t e = check_params<EPI>(p, 64, ks * (RB / (int)sizeof(W)));
+  if (e != hipSuccess) return e;
+  p.ksplit = ks;
+  const int tiles = ((p.M + 63) / 64) * (p.N / 64);
+  // A timed class spans both launches: from the GEMM's start to the reduction's end.
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  timing_take(&e0, &e1);
+  constexpr int WM = 2, WN = 2, KW = 2;
+  e = launch_ev(gemm_kernel<W, 64, 64, WM, WN, RB, EPI | EPI_SPLIT, 4, KW>, dim3(tiles * ks), dim3(64 * WM * WN * KW), s,
+                e0, nullptr, p);
+  if (e != hipSuccess) return e;
+  constexpr int RM = 16, NT = EPI == EPI_QKV_ROPE ? 128 : 256;
+  return launch_ev(gemm_reduce_kernel<W, EPI, 64, RM, NT>, dim3(((p.M + RM - 1) / RM) * (p.N / 64)), dim3(NT), s,
+                   nullptr, e1, p);
 }
 
 // Tile choice, from sweeps on MI355X over the model's shapes (2-stage rings were
@@ -605,6 +776,10 @@ static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
 // warm prefill GEMMs gain nothing from depth).
 template <typename T, int EPI>
 static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
+  if (p.part && (EPI != EPI_QKV_ROPE || p.head_dim == 64)) {
+    const int ks = ksplit_plan(p.M, p.N, p.K, sizeof(T));
+    if (ks > 1) return launch_split<T, EPI>(p, ks, s);
+  }
   const long tm128 = (p.M + 127) / 128, tm64 = (p.M + 63) / 64;
   if (EPI != EPI_QKV_ROPE || p.head_dim == 64)
     if (tm64 * (p.N / 64) < 128 && p.N % 64 == 0) return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 4, 2>(p, s);
@@ -624,16 +799,19 @@ static void set_norm_in(GemmParams &p, const NormIn &n, int H) {
 
 template <typename T>
 hipError_t gemm_store(const Act<T> *A, const NormIn &nrm, const T *B, int M, int N, int K, void *C, int c_f32,
-                      hipStream_t s) {
+                      float *part, hipStream_t s) {
   GemmParams p{};
+  p.part = part;
   p.A = A; p.lda = K; p.B0 = B; p.M = M; p.N = N; p.K = K; p.C = C; p.ldc = N; p.c_f32 = c_f32;
   set_norm_in(p, nrm, K);
   return launch_gemm<T, EPI_STORE>(p, s);
 }
 
 template <typename T>
-hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, const NormOut &nrm, hipStream_t s) {
+hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, const NormOut &nrm, float *part,
+                         hipStream_t s) {
   GemmParams p{};
+  p.part = part;
   p.A = A; p.lda = K; p.B0 = B; p.M = M; p.N = N; p.K = K; p.C = X; p.ldc = N;
   p.ss_old = nrm.ss_old; p.ss_new = nrm.ss_new; p.norm_w = nrm.w; p.xs = nrm.xs; p.ss_cols = N; p.eps = nrm.eps;
   return launch_gemm<T, EPI_RESIDUAL>(p, s);
@@ -641,8 +819,9 @@ hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float
 
 template <typename T>
 hipError_t gemm_swiglu(const Act<T> *A, const NormIn &nrm, const T *Wg, const T *Wu, int M, int I, int K, Act<T> *Y,
-                       hipStream_t s) {
+                       float *part, hipStream_t s) {
   GemmParams p{};
+  p.part = part;
   p.A = A; p.lda = K; p.B0 = Wg; p.B1 = Wu; p.M = M; p.N = 2 * I; p.K = K; p.C = Y; p.ldc = I;
   set_norm_in(p, nrm, K);
   return launch_gemm<T, EPI_SWIGLU>(p, s);
@@ -650,8 +829,9 @@ hipError_t gemm_swiglu(const Act<T> *A, const NormIn &nrm, const T *Wg, const T 
 
 template <typename T>
 hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const T *Wk, const T *Wv, const QkvOut &o,
-                         hipStream_t s) {
+                         float *part, hipStream_t s) {
   GemmParams p{};
+  p.part = part;
   p.A = A; p.lda = o.hidden; p.B0 = Wq; p.B1 = Wk; p.B2 = Wv;
   p.M = o.M; p.N = o.nq_cols + 2 * o.nkv_cols; p.K = o.hidden;
   set_norm_in(p, nrm, o.hidden);
@@ -666,13 +846,13 @@ hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const 
 
 #define SMOL_INST(T)                                                                                          \
   template hipError_t gemm_store<T>(const Act<T> *, const NormIn &, const T *, int, int, int, void *, int,     \
-                                    hipStream_t);                                                              \
+                                    float *, hipStream_t);                                                     \
   template hipError_t gemm_residual<T>(const Act<T> *, const T *, int, int, int, float *, const NormOut &,     \
-                                       hipStream_t);                                                           \
+                                       float *, hipStream_t);                                                  \
   template hipError_t gemm_swiglu<T>(const Act<T> *, const NormIn &, const T *, const T *, int, int, int,      \
-                                     Act<T> *, hipStream_t);                                                   \
+                                     Act<T> *, float *, hipStream_t);                                          \
   template hipError_t gemm_qkv_rope<T>(const Act<T> *, const NormIn &, const T *, const T *, const T *,        \
-                                       const QkvOut &, hipStream_t);
+                                       const QkvOut &, float *, hipStream_t);
 SMOL_INST(float)
 SMOL_INST(bf16)
 

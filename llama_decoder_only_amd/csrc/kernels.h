@@ -10,7 +10,8 @@
 
 namespace smol {
 
-enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_QKV_ROPE = 3 };
+enum { EPI_STORE = 0, EPI_RESIDUAL = 1, EPI_SWIGLU = 2, EPI_QKV_ROPE = 3,
+       EPI_SPLIT = 16 };  // flag: a K split's partial sums instead of the epilogue
 
 // Where the QKV projection writes: q [M, nq_cols]; k, v into [B, n_kv, cap, d] at
 // index pos - kv_off (prefill: pos = pos0 + t) or cache_len[b] (decode, M == B).
@@ -43,17 +44,21 @@ struct NormOut {
 };
 
 // T is the storage type (weights, cache, logits); activations are Act<T>.
+// part: float scratch for K-split partial sums, gemm_part_floats(M, N, K, sizeof(T))
+// floats (nullptr: never split). Calls on one stream may share it.
 template <typename T>
 hipError_t gemm_store(const Act<T> *A, const NormIn &nrm, const T *B, int M, int N, int K, void *C, int c_f32,
-                      hipStream_t s);
+                      float *part, hipStream_t s);
 template <typename T>
-hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, const NormOut &nrm, hipStream_t s);
+hipError_t gemm_residual(const Act<T> *A, const T *B, int M, int N, int K, float *X, const NormOut &nrm, float *part,
+                         hipStream_t s);
 template <typename T>
 hipError_t gemm_swiglu(const Act<T> *A, const NormIn &nrm, const T *Wg, const T *Wu, int M, int I, int K, Act<T> *Y,
-                       hipStream_t s);
+                       float *part, hipStream_t s);
 template <typename T>
 hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const T *Wk, const T *Wv, const QkvOut &o,
-                         hipStream_t s);
+                         float *part, hipStream_t s);
+size_t gemm_part_floats(int M, int N, int K, int esz);  // 0: that GEMM does not split
 
 // x[m] = E[ids[m]] (ids != nullptr: the embedding gather) or x[m] = src[m], and what
 // the first deferred RMSNorm reads: the row sums of squares into both ss_new and
@@ -103,15 +108,24 @@ void timing_before(int kernel, hipStream_t s);
 void timing_after(int kernel, hipStream_t s);
 bool timing_take(hipEvent_t *start, hipEvent_t *stop);  // the armed pair, handed out once
 
-// Every kernel of the library starts here.
+// A launch that records start (at the dispatch) and/or stop (at the kernel's end)
+// when they are not null.
 template <typename... Params, typename... Args>
-hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
-  hipEvent_t e0, e1;
-  if (timing_take(&e0, &e1))
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+hipError_t launch_ev(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start,
+                     hipEvent_t stop, Args... args) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
   return hipGetLastError();
+}
+
+// Every single-kernel operation of the library launches here.
+template <typename... Params, typename... Args>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  timing_take(&e0, &e1);
+  return launch_ev(kernel, grid, block, s, e0, e1, args...);
 }
 
 }  // namespace smol
