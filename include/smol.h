@@ -126,6 +126,53 @@ smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w
                              void *k_cache, void *v_cache, int cache_cap, void *logits,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* Next token of each sequence from one row of logits per sequence (the generation
+ * loop of Sualeh77 model.py, "7. Top-level SmolLM2-135M Model Architecture",
+ * generate, and abi96062 model.py, SmolLM2Model.generate).
+ *   logits: row b starts at logits + b * row_stride elements; vocab elements, of
+ *     dtype (float or bfloat16). For the last position of a prefill [B, T, V] pass
+ *     logits + (T-1)*V and row_stride T*V; for a decode step [B, V], 0 and V.
+ *   temperature == 0: greedy, next_ids[b] = index of the largest logit (lowest index
+ *     among equal maxima).
+ *   temperature > 0: z = logit / temperature; top_k in 1 .. vocab-1 keeps the tokens
+ *     whose logit is >= the k-th largest logit (0 or >= vocab: off); top_p < 1 then
+ *     keeps, in descending logit order (equal logits by ascending index), every token
+ *     up to and including the first at which the cumulative softmax probability of
+ *     the tokens kept so far exceeds top_p (top_p >= 1: off). next_ids[b] is the first
+ *     index, in vocabulary order, at which the cumulative softmax probability of the
+ *     kept z exceeds uniforms[b] (inverse CDF).
+ *   uniforms [batch] float in [0, 1) (device; read only when temperature > 0): the
+ *     caller's random numbers, one per row.
+ *   next_ids [batch] int32 (device, written): the chosen index, or -1 for a row that
+ *     holds a NaN, or (when sampling) whose largest logit is infinite.
+ * Errors: SMOL_ERR_INVALID_ARG for null pointers, batch < 1, vocab < 1, row_stride <
+ * vocab when batch > 1, a negative or NaN temperature or top_p, top_k < 0 or an
+ * unknown dtype. Every float sum is taken in a fixed order, so a call with the same
+ * inputs returns the same ids. Uses no workspace. */
+smol_status smol_sample(const void *logits, int dtype, int batch, int vocab, int64_t row_stride,
+                        float temperature, int top_k, float top_p, const float *uniforms,
+                        int32_t *next_ids, void *stream);
+
+/* Generation (the loop of Sualeh77 model.py, "7. Top-level SmolLM2-135M Model
+ * Architecture", generate: the prompt once, then one cached decode step per new
+ * token). prompt_ids [batch, prompt_len] int32; the prompt fills the caches
+ * [n_layers, batch, n_kv, cache_cap, head_dim] at 0 .. prompt_len-1 and the logits
+ * of its last position give token 0 through smol_sample's rule (temperature, top_k,
+ * top_p; uniforms [max_new, batch] device, row j for token j, NULL when temperature
+ * is 0). Token j >= 1 comes from a decode step that feeds token j-1 at position
+ * prompt_len + j - 1. out_ids [max_new, batch] int32 (device, written; token j of
+ * sequence b at j * batch + b). All max_new tokens are produced: a caller that stops
+ * at an end-of-sequence id trims afterwards. Requires prompt_len + max_new - 1 <=
+ * min(cache_cap, max_pos). ws: smol_generate_workspace_size() bytes, 256-byte
+ * aligned. Everything is enqueued on `stream`; nothing synchronises, so the whole
+ * call can be captured into one HIP graph. */
+smol_status smol_generate_workspace_size(const smol_config *cfg, int batch, int prompt_len, int max_new,
+                                         int cache_cap, size_t *bytes);
+smol_status smol_generate(const smol_config *cfg, const smol_model_weights *w, const int32_t *prompt_ids,
+                          int batch, int prompt_len, int max_new, float temperature, int top_k, float top_p,
+                          const float *uniforms, int32_t *out_ids, void *k_cache, void *v_cache,
+                          int cache_cap, void *ws, size_t ws_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *smol_status_string(smol_status s);
 
@@ -145,7 +192,7 @@ const char *smol_last_error(void);
 typedef enum {
   SMOL_K_EMBED = 0, SMOL_K_RMSNORM = 1, SMOL_K_QKV_ROPE = 2, SMOL_K_ATTENTION = 3,
   SMOL_K_O_PROJ = 4, SMOL_K_GATE_UP = 5, SMOL_K_DOWN = 6, SMOL_K_LM_HEAD = 7,
-  SMOL_K_DECODE_ATTENTION = 8, SMOL_K_DECODE_COMBINE = 9, SMOL_K_COUNT = 10
+  SMOL_K_DECODE_ATTENTION = 8, SMOL_K_DECODE_COMBINE = 9, SMOL_K_SAMPLE = 10, SMOL_K_COUNT = 11
 } smol_kernel;
 smol_status smol_timing_begin(int kernel, int max_launches);
 smol_status smol_timing_end(float *total_ms, int *launches);

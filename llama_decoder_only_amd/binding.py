@@ -23,8 +23,9 @@ SMOL_OK, SMOL_ERR_INVALID_ARG, SMOL_ERR_UNSUPPORTED, SMOL_ERR_WORKSPACE, SMOL_ER
 SMOL_F32, SMOL_BF16 = 0, 1
 SMOL_OP_BLOCK, SMOL_OP_PREFILL, SMOL_OP_DECODE = 0, 1, 2
 KERNELS = ["embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head",
-           "decode_attention", "decode_combine"]
+           "decode_attention", "decode_combine", "sample"]
 EXPORTED = ["smol_workspace_size", "smol_block_forward", "smol_model_prefill", "smol_decode_step",
+            "smol_sample", "smol_generate_workspace_size", "smol_generate",
             "smol_status_string", "smol_last_error", "smol_timing_begin", "smol_timing_end"]
 
 
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
                                          vp, sz, vp]
         L.smol_decode_step.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, vp, i32, vp, vp, i32, vp, vp,
                                        sz, vp]
+        f32, i64 = ctypes.c_float, ctypes.c_int64
+        L.smol_sample.argtypes = [vp, i32, i32, i32, i64, f32, i32, f32, vp, vp, vp]
+        L.smol_generate_workspace_size.argtypes = [cfgp, i32, i32, i32, i32, ctypes.POINTER(sz)]
+        L.smol_generate.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, i32, i32, i32, f32, i32, f32, vp,
+                                    vp, vp, vp, i32, vp, sz, vp]
         L.smol_status_string.argtypes = [i32]
         L.smol_status_string.restype = ctypes.c_char_p
         L.smol_last_error.argtypes = []
@@ -233,6 +239,59 @@ def smol_decode_step(cfg: Config, w: ModelWeights, ids: torch.Tensor, cache_len:
                                   _ptr(k_cache), _ptr(v_cache), cap, _ptr(logits), _ptr(ws), ws.numel(),
                                   _stream(stream)))
     return logits
+
+
+def smol_sample(logits: torch.Tensor, next_ids: torch.Tensor, temperature: float = 0.0, top_k: int = 0,
+                top_p: float = 1.0, uniforms: Optional[torch.Tensor] = None, row_offset: int = 0,
+                row_stride: Optional[int] = None, stream=None) -> torch.Tensor:
+    """logits [B, V] (or any rows: row b at element row_offset + b * row_stride), float32 or
+    bfloat16; next_ids int32 [B] (written); uniforms float32 [B] in [0, 1) when sampling."""
+    B = next_ids.shape[0]
+    V = logits.shape[-1]
+    if row_stride is None:
+        row_stride = V
+    if row_offset + (B - 1) * row_stride + V > logits.numel():
+        raise ValueError("rows run past the logits tensor")
+    dt = SMOL_BF16 if logits.dtype == torch.bfloat16 else SMOL_F32
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("logits must be float32 or bfloat16")
+    base = _ptr(logits) + row_offset * logits.element_size()
+    _check(lib().smol_sample(base, dt, B, V, row_stride, float(temperature), int(top_k), float(top_p), _ptr(uniforms),
+                             _ptr(next_ids), _stream(stream)))
+    return next_ids
+
+
+def smol_generate_workspace_size(cfg: Config, batch: int, prompt_len: int, max_new: int, cache_cap: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().smol_generate_workspace_size(ctypes.byref(cfg.c()), batch, prompt_len, max_new, cache_cap,
+                                              ctypes.byref(n)))
+    return int(n.value)
+
+
+def smol_generate(cfg: Config, w: ModelWeights, prompt_ids: torch.Tensor, max_new: int, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, out_ids: torch.Tensor, temperature: float = 0.0, top_k: int = 0,
+                  top_p: float = 1.0, uniforms: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """prompt_ids int32 [B, T]; caches [L, B, n_kv, cap, d]; out_ids int32 [max_new, B] (written);
+    uniforms float32 [max_new, B] when temperature > 0."""
+    B, T = prompt_ids.shape
+    cap = k_cache.shape[3]
+    if ws is None:
+        ws = torch.empty(smol_generate_workspace_size(cfg, B, T, max_new, cap), dtype=torch.uint8,
+                         device=prompt_ids.device)
+    _check(lib().smol_generate(ctypes.byref(cfg.c()), ctypes.byref(w.c), _ptr(prompt_ids), B, T, max_new,
+                               float(temperature), int(top_k), float(top_p), _ptr(uniforms), _ptr(out_ids),
+                               _ptr(k_cache), _ptr(v_cache), cap, _ptr(ws), ws.numel(), _stream(stream)))
+    return out_ids
+
+
+def trim_at_eos(out_ids: np.ndarray, eos_id: int) -> np.ndarray:
+    """Tokens [max_new, B] cut after the first step at which every sequence's new token
+    is eos_id (the stopping rule of Sualeh77 model.py, "7. Top-level", generate)."""
+    for j in range(out_ids.shape[0]):
+        if (out_ids[j] == eos_id).all():
+            return out_ids[: j + 1]
+    return out_ids
 
 
 def smol_timing_begin(kernel: str, max_launches: int):

@@ -320,6 +320,7 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
     smol_status st = run_layer<T>(c, &w->layers[l], x, next);
     if (st != SMOL_OK) return st;
   }
+  if (!logits) return SMOL_OK;  // generation: the head runs on the last positions only
   return head<T>(D, w, M, logits, ws, lay, s);
 }
 
@@ -348,6 +349,65 @@ smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_
     if (st != SMOL_OK) return st;
   }
   return head<T>(D, w, B, logits, ws, lay, s);
+}
+
+// Generation workspace: one region that the prefill and then the decode steps use in
+// turn (same stream, never at once), then the last-position state, the logits of one
+// step and the per-step positions.
+struct GenWs {
+  Ws pre, dec;
+  size_t xs_last, ssp_last, ssq_last, logits, pos, total;
+};
+
+GenWs gen_layout(const Dims &D, int B, int T, int max_new, int cap) {
+  GenWs g{};
+  g.pre = layout(D, SMOL_OP_PREFILL, B, T);
+  g.dec = layout(D, SMOL_OP_DECODE, B, cap);
+  size_t off = std::max(g.pre.total, g.dec.total);
+  auto take = [&](size_t bytes) { size_t at = off; off += up(bytes); return at; };
+  g.xs_last = take((size_t)B * D.H * D.esz);
+  g.ssp_last = take((size_t)(D.H / 64) * B * 4);
+  g.ssq_last = take((size_t)(D.H / 64) * B * 4);
+  g.logits = take((size_t)B * D.V * D.esz);
+  g.pos = take((size_t)std::max(1, max_new - 1) * B * 4);
+  g.total = off;
+  return g;
+}
+
+template <typename T>
+smol_status generate_impl(const Dims &D, const smol_model_weights *w, const int32_t *prompt, int B, int T_,
+                          int max_new, float temperature, int top_k, float top_p, const float *uniforms,
+                          int32_t *out_ids, void *kc, void *vc, int cap, char *ws, const GenWs &g, hipStream_t s) {
+  smol_status st = prefill_impl<T>(D, w, prompt, B, T_, nullptr, kc, vc, cap, ws, g.pre, s);
+  if (st != SMOL_OK) return st;
+  using A = Act<T>;
+  A *xs_last = (A *)(ws + g.xs_last);
+  float *ssp = (float *)(ws + g.ssp_last), *ssq = (float *)(ws + g.ssq_last);
+  T *logits = (T *)(ws + g.logits);
+  int32_t *pos = (int32_t *)(ws + g.pos);
+  hipError_t e = smol::gather_last<T>((const A *)(ws + g.pre.xs), (const float *)(ws + g.pre.ss_p),
+                                      (const float *)(ws + g.pre.ss_q), B, T_, D.H, xs_last, ssp, ssq, s);
+  if (e != hipSuccess) return fail(SMOL_ERR_HIP, "gather_last: %s", hipGetErrorString(e));
+  SMOL_LAUNCH(SMOL_K_LM_HEAD, smol::gemm_store<T>(xs_last, smol::NormIn{ssp, ssq, D.eps}, (const T *)w->embed, B, D.V,
+                                                  D.H, logits, 0, nullptr, s));
+  auto sample = [&](int step) -> smol_status {
+    SMOL_LAUNCH(SMOL_K_SAMPLE, smol::sample_next<T>(logits, D.V, B, D.V, temperature, top_k, top_p,
+                                                    uniforms ? uniforms + (size_t)step * B : nullptr,
+                                                    out_ids + (size_t)step * B, s));
+    return SMOL_OK;
+  };
+  if ((st = sample(0)) != SMOL_OK) return st;
+  if (max_new > 1) {
+    e = smol::fill_positions(pos, B, max_new - 1, T_, s);
+    if (e != hipSuccess) return fail(SMOL_ERR_HIP, "fill_positions: %s", hipGetErrorString(e));
+  }
+  for (int step = 1; step < max_new; ++step) {
+    st = decode_impl<T>(D, w, out_ids + (size_t)(step - 1) * B, pos + (size_t)(step - 1) * B, B, kc, vc, cap, logits,
+                        ws, g.dec, s);
+    if (st != SMOL_OK) return st;
+    if ((st = sample(step)) != SMOL_OK) return st;
+  }
+  return SMOL_OK;
 }
 
 smol_status check_model(const Dims &D, const smol_model_weights *w) {
@@ -438,6 +498,73 @@ smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w
   hipStream_t s = (hipStream_t)stream;
   return D.bf16 ? decode_impl<bf16>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay, s)
                 : decode_impl<float>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay, s);
+}
+
+smol_status smol_generate_workspace_size(const smol_config *cfg, int batch, int prompt_len, int max_new,
+                                         int cache_cap, size_t *bytes) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if (!bytes) return fail(SMOL_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || prompt_len < 1 || max_new < 1 || cache_cap < 1)
+    return fail(SMOL_ERR_INVALID_ARG, "batch, prompt_len, max_new and cache_cap must be >= 1");
+  *bytes = gen_layout(D, batch, prompt_len, max_new, cache_cap).total;
+  return SMOL_OK;
+}
+
+smol_status smol_generate(const smol_config *cfg, const smol_model_weights *w, const int32_t *prompt_ids, int batch,
+                          int prompt_len, int max_new, float temperature, int top_k, float top_p,
+                          const float *uniforms, int32_t *out_ids, void *k_cache, void *v_cache, int cache_cap,
+                          void *ws, size_t ws_bytes, void *stream) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if ((st = check_model(D, w)) != SMOL_OK) return st;
+  if (!prompt_ids || !out_ids) return fail(SMOL_ERR_INVALID_ARG, "prompt_ids / out_ids is NULL");
+  if (!k_cache || !v_cache) return fail(SMOL_ERR_INVALID_ARG, "generation needs k_cache and v_cache");
+  if (batch < 1 || prompt_len < 1 || max_new < 1)
+    return fail(SMOL_ERR_INVALID_ARG, "batch %d, prompt_len %d, max_new %d must be >= 1", batch, prompt_len, max_new);
+  const long last = (long)prompt_len + max_new - 1;  // positions fed: 0 .. last - 1
+  if (last > D.max_pos) return fail(SMOL_ERR_INVALID_ARG, "prompt_len + max_new - 1 = %ld exceeds max_pos %d", last, D.max_pos);
+  if (last > cache_cap) return fail(SMOL_ERR_INVALID_ARG, "prompt_len + max_new - 1 = %ld exceeds cache_cap %d", last, cache_cap);
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(SMOL_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (!(top_p >= 0.f)) return fail(SMOL_ERR_INVALID_ARG, "top_p must be >= 0");
+  if (top_k < 0) return fail(SMOL_ERR_INVALID_ARG, "top_k %d < 0", top_k);
+  if (temperature > 0.f && !uniforms) return fail(SMOL_ERR_INVALID_ARG, "uniforms is NULL");
+  if (!ws) return fail(SMOL_ERR_INVALID_ARG, "ws is NULL");
+  if ((uintptr_t)ws % ALIGN) return fail(SMOL_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  const GenWs g = gen_layout(D, batch, prompt_len, max_new, cache_cap);
+  if (ws_bytes < g.total) return fail(SMOL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, g.total);
+  hipStream_t s = (hipStream_t)stream;
+  return D.bf16 ? generate_impl<bf16>(D, w, prompt_ids, batch, prompt_len, max_new, temperature, top_k, top_p,
+                                      uniforms, out_ids, k_cache, v_cache, cache_cap, (char *)ws, g, s)
+                : generate_impl<float>(D, w, prompt_ids, batch, prompt_len, max_new, temperature, top_k, top_p,
+                                       uniforms, out_ids, k_cache, v_cache, cache_cap, (char *)ws, g, s);
+}
+
+smol_status smol_sample(const void *logits, int dtype, int batch, int vocab, int64_t row_stride, float temperature,
+                        int top_k, float top_p, const float *uniforms, int32_t *next_ids, void *stream) {
+  g_err.clear();
+  if (!logits || !next_ids) return fail(SMOL_ERR_INVALID_ARG, "logits / next_ids is NULL");
+  if (dtype != SMOL_F32 && dtype != SMOL_BF16) return fail(SMOL_ERR_INVALID_ARG, "dtype %d unknown", dtype);
+  if (batch < 1 || vocab < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d, vocab %d must be >= 1", batch, vocab);
+  if (batch > 1 && row_stride < vocab)
+    return fail(SMOL_ERR_INVALID_ARG, "row_stride %lld < vocab %d", (long long)row_stride, vocab);
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(SMOL_ERR_INVALID_ARG, "temperature must be finite and >= 0");
+  if (!(top_p >= 0.f)) return fail(SMOL_ERR_INVALID_ARG, "top_p must be >= 0");
+  if (top_k < 0) return fail(SMOL_ERR_INVALID_ARG, "top_k %d < 0", top_k);
+  if (temperature > 0.f && !uniforms) return fail(SMOL_ERR_INVALID_ARG, "uniforms is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  SMOL_LAUNCH(SMOL_K_SAMPLE, dtype == SMOL_BF16
+                                 ? smol::sample_next<bf16>((const bf16 *)logits, (long)row_stride, batch, vocab,
+                                                           temperature, top_k, top_p, uniforms, next_ids, s)
+                                 : smol::sample_next<float>((const float *)logits, (long)row_stride, batch, vocab,
+                                                            temperature, top_k, top_p, uniforms, next_ids, s));
+  return SMOL_OK;
 }
 
 const char *smol_status_string(smol_status s) {

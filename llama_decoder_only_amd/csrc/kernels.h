@@ -76,6 +76,13 @@ template <typename T>
 hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, float *ss_new, float *ss_old,
                    const T *w, Act<T> *xs, float eps, int M, int H, int V, const RopeIn &rope, hipStream_t s);
 
+// Generation: the last position of each sequence's prefill state (xs row and its two
+// sums-of-squares columns), and the per-step decode positions pos[j * B + b] = first + j.
+template <typename T>
+hipError_t gather_last(const Act<T> *xs, const float *ssp, const float *ssq, int B, int T_, int H, Act<T> *xs_out,
+                       float *ssp_out, float *ssq_out, hipStream_t s);
+hipError_t fill_positions(int32_t *pos, int B, int n, int first, hipStream_t s);
+
 // Causal GQA attention over a [B, n_kv, cap, d] key/value store. Query t of
 // sequence b sits at key index t + q_key_off; it sees key indices <= that.
 struct AttnArgs {
@@ -99,6 +106,11 @@ struct DecodeAttnArgs {
 template <typename T>
 hipError_t attention_decode(const DecodeAttnArgs &a, hipStream_t s);
 int decode_splits(int cap, int *chunk);
+
+// Next-token choice per row of logits (smol_sample in smol.h).
+template <typename T>
+hipError_t sample_next(const T *logits, long row_stride, int B, int V, float temperature, int top_k, float top_p,
+                       const float *uniforms, int32_t *next_ids, hipStream_t s);
 
 // Kernel-class timing (see smol_timing_begin). timing_before arms the next launch()
 // of that class with a start/stop event pair, which hipExtLaunchKernelGGL records at

@@ -434,6 +434,129 @@ def pin_brute_force_tiny():
     assert _rel(got, want) < 1e-12
 
 
+# ---------------------------------------------------------------- next-token choice
+# (oracle/generate.py; Sualeh77 model.py "7. Top-level", generate; abi96062 model.py,
+# SmolLM2Model.generate)
+
+import oracle.generate as G  # noqa: E402
+
+
+def _kept(logits, t=1.0, k=0, p=1.0):
+    return set(np.nonzero(G.next_token(np.asarray(logits, np.float64), t, k, p, 0.5).kept)[0].tolist())
+
+
+def pin_greedy_ties_and_nan():
+    """Greedy is the argmax, lowest index among equal maxima; NaN rows give -1."""
+    assert G.next_token([1.0, 3.0, 3.0, 2.0], 0.0).token == 1
+    assert G.next_token([-np.inf, np.inf, np.inf], 0.0).token == 1
+    assert G.next_token([0.0, np.nan, 1.0], 0.0).token == -1
+    assert G.next_token([0.0, np.nan, 1.0], 1.0, u=0.3).token == -1
+    assert G.next_token([0.0, np.inf, 1.0], 1.0, u=0.3).token == -1  # softmax undefined
+
+
+def pin_top_k_keeps_ties():
+    """Tokens below the k-th largest logit go; ties with it stay."""
+    l = [5.0, 4.0, 4.0, 1.0, 0.0]
+    assert _kept(l, k=1) == {0}
+    assert _kept(l, k=2) == {0, 1, 2}
+    assert _kept(l, k=3) == {0, 1, 2}
+    assert _kept(l, k=4) == {0, 1, 2, 3}
+    assert _kept(l, k=0) == _kept(l, k=5) == {0, 1, 2, 3, 4}
+
+
+def pin_top_p_hand_values():
+    """Probabilities 0.5, 0.3, 0.2 (cumulative 0.5, 0.8, 1.0): the nucleus keeps every
+    token up to and including the first whose cumulative probability exceeds p,
+    whatever the tokens' order in the vocabulary; equal logits rank by index."""
+    lp = np.log([0.5, 0.3, 0.2])
+    assert _kept(lp, p=0.45) == {0}
+    assert _kept(lp, p=0.6) == {0, 1}
+    assert _kept(lp, p=0.9) == {0, 1, 2}
+    perm = np.log([0.2, 0.5, 0.3])  # same distribution, other token order
+    assert _kept(perm, p=0.6) == {1, 2}
+    # logits 1, 2, 2, 0: probabilities e^2/Z twice (0.3995 each), e/Z, 1/Z
+    tie = [1.0, 2.0, 2.0, 0.0]
+    assert _kept(tie, p=0.3) == {1}
+    assert _kept(tie, p=0.5) == {1, 2}
+    assert _kept(tie, p=0.85) == {0, 1, 2}
+
+
+def pin_top_p_after_top_k():
+    """Top-p works on the distribution that top-k left (renormalised): probabilities
+    0.4, 0.3, 0.2, 0.1 with k = 2 become 4/7, 3/7, so p = 0.5 keeps one token; without
+    top-k (cumulative 0.4, 0.7) the same p keeps two."""
+    lp = np.log([0.4, 0.3, 0.2, 0.1])
+    assert _kept(lp, k=2, p=0.5) == {0}
+    assert _kept(lp, p=0.5) == {0, 1}
+
+
+def pin_inverse_cdf_stratified():
+    """With stratified uniforms u_i = (i + 1/2) / N the draw counts are N times the
+    probabilities exactly: 0.1, 0.2, 0.3, 0.4 at temperature 1, and p^2 / sum p^2
+    (= 1/30, 4/30, 9/30, 16/30) at temperature 1/2."""
+    lp = np.log([0.1, 0.2, 0.3, 0.4])
+    for t, n, want in ((1.0, 1000, [100, 200, 300, 400]), (0.5, 300, [10, 40, 90, 160])):
+        counts = np.zeros(4, int)
+        for i in range(n):
+            counts[G.next_token(lp, t, u=(i + 0.5) / n).token] += 1
+        assert counts.tolist() == want, (t, counts)
+
+
+def pin_inverse_cdf_steps():
+    """The draw is the first index whose cumulative probability exceeds u: with two
+    equal probabilities u = 0.5 picks index 1, u = 0 the first kept index and u just
+    below 1 the last kept index."""
+    assert G.next_token([0.0, 0.0], 1.0, u=0.5).token == 1
+    assert G.next_token([0.0, 0.0], 1.0, u=0.0).token == 0
+    l = [0.0, -np.inf, 3.0, 1.0, -np.inf]
+    assert G.next_token(l, 1.0, u=0.0).token == 0
+    assert G.next_token(l, 1.0, u=1.0 - 1e-12).token == 3
+    assert G.next_token(l, 1.0, top_k=1, u=0.0).token == 2
+
+
+def _brute_choice(l, t, k, p, u):
+    """The same choice by enumeration: sorted order by explicit comparisons, the
+    nucleus as the shortest sorted prefix whose mass exceeds p, the draw by a running
+    sum. Tiny V only."""
+    V = len(l)
+    order = sorted(range(V), key=lambda i: (-l[i], i))
+    kept = set(range(V))
+    if 0 < k < V:
+        kth = order[k - 1]
+        kept = {i for i in range(V) if l[i] >= l[kth]}
+    w = {i: math.exp((l[i] - max(l)) / t) for i in kept}
+    if p < 1.0:
+        ranked = [i for i in order if i in kept]
+        z = sum(w[i] for i in ranked)
+        for n in range(1, len(ranked) + 1):
+            if sum(w[i] for i in ranked[:n]) / z > p:
+                break
+        kept = set(ranked[:n])
+    z = sum(w[i] for i in kept)
+    acc = 0.0
+    for i in range(V):
+        if i in kept:
+            acc += w[i] / z
+            if acc > u:
+                return i
+    return max(kept)
+
+
+def pin_choice_brute_force():
+    rng = _rng(31)
+    for trial in range(300):
+        V = int(rng.integers(2, 7))
+        l = np.round(rng.normal(0, 1.5, V), 1)  # rounding makes ties common
+        t = float(rng.choice([0.3, 1.0, 2.5]))
+        k = int(rng.integers(0, V + 1))
+        p = float(rng.choice([1.0, 0.95, 0.7, 0.35]))
+        u = float(rng.random())
+        c = G.next_token(l, t, k, p, u)
+        if min(c.p_margin, c.u_margin) < 1e-9:
+            continue  # a cut within rounding of a boundary: either side is correct
+        assert c.token == _brute_choice(l.tolist(), t, k, p, u), (trial, l, t, k, p, u)
+
+
 ALL_PINS = [
     pin_rmsnorm_closed_forms,
     pin_rmsnorm_vs_torch,
@@ -452,4 +575,15 @@ ALL_PINS = [
     pin_gqa_mapping_smollm3,
     pin_decode_equals_prefill,
     pin_brute_force_tiny,
+    pin_greedy_ties_and_nan,
+    pin_top_k_keeps_ties,
+    pin_top_p_hand_values,
+    pin_top_p_after_top_k,
+    pin_inverse_cdf_stratified,
+    pin_inverse_cdf_steps,
+    pin_choice_brute_force,
 ]
+
+SAMPLER_PINS = [p for p in ALL_PINS if p.__name__ in (
+    "pin_greedy_ties_and_nan", "pin_top_k_keeps_ties", "pin_top_p_hand_values", "pin_top_p_after_top_k",
+    "pin_inverse_cdf_stratified", "pin_inverse_cdf_steps", "pin_choice_brute_force")]

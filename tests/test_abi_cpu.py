@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -153,6 +154,58 @@ def test_decode_step_rejects():
     assert call(b=0) == B.SMOL_ERR_INVALID_ARG
     assert call(cap=0) == B.SMOL_ERR_INVALID_ARG
     assert call(ws_bytes=need - 256) == B.SMOL_ERR_WORKSPACE
+
+
+def test_sample_rejects():
+    L = B.lib()
+    call = lambda **k: L.smol_sample(  # noqa: E731
+        k.get("logits", FAKE), k.get("dt", B.SMOL_BF16), k.get("b", 4), k.get("v", 49152), k.get("stride", 49152),
+        k.get("t", 1.0), k.get("k", 0), k.get("p", 1.0), k.get("u", FAKE), k.get("out", FAKE), None)
+    assert call(logits=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(out=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(dt=7) == B.SMOL_ERR_INVALID_ARG
+    assert call(b=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(v=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(stride=100) == B.SMOL_ERR_INVALID_ARG and "row_stride" in B.smol_last_error()
+    assert call(t=-1.0) == B.SMOL_ERR_INVALID_ARG
+    assert call(t=float("nan")) == B.SMOL_ERR_INVALID_ARG
+    assert call(t=float("inf")) == B.SMOL_ERR_INVALID_ARG
+    assert call(p=float("nan")) == B.SMOL_ERR_INVALID_ARG
+    assert call(k=-1) == B.SMOL_ERR_INVALID_ARG
+    assert call(u=None) == B.SMOL_ERR_INVALID_ARG and "uniforms" in B.smol_last_error()
+
+
+def test_generate_rejects():
+    cfg = _cfg()
+    m, keep = _model_struct(cfg)
+    L = B.lib()
+    n = ctypes.c_size_t(0)
+    assert L.smol_generate_workspace_size(ctypes.byref(cfg.c()), 4, 16, 8, 64, ctypes.byref(n)) == 0
+    need = n.value
+    assert need >= _ws(cfg, B.SMOL_OP_PREFILL, 4, 16)[1] and need >= _ws(cfg, B.SMOL_OP_DECODE, 4, 64)[1]
+    assert L.smol_generate_workspace_size(ctypes.byref(cfg.c()), 4, 0, 8, 64, ctypes.byref(n)) == B.SMOL_ERR_INVALID_ARG
+    call = lambda **k: L.smol_generate(  # noqa: E731
+        ctypes.byref(cfg.c()), ctypes.byref(m), k.get("ids", FAKE), 4, k.get("t", 16), k.get("n", 8),
+        k.get("temp", 0.0), 0, 1.0, k.get("u", None), k.get("out", FAKE), k.get("kc", FAKE), FAKE,
+        k.get("cap", 64), FAKE, k.get("ws_bytes", need), None)
+    assert call(ids=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(out=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(kc=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(n=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(t=60, n=6) == B.SMOL_ERR_INVALID_ARG and "cache_cap" in B.smol_last_error()  # 60 + 6 - 1 > 64
+    assert call(temp=0.7) == B.SMOL_ERR_INVALID_ARG and "uniforms" in B.smol_last_error()
+    assert call(ws_bytes=need - 256) == B.SMOL_ERR_WORKSPACE
+    cfg8 = _cfg(max_pos=20)
+    assert L.smol_generate(ctypes.byref(cfg8.c()), ctypes.byref(m), FAKE, 4, 16, 8, 0.0, 0, 1.0, None, FAKE, FAKE,
+                           FAKE, 64, FAKE, need, None) == B.SMOL_ERR_INVALID_ARG
+    assert "max_pos" in B.smol_last_error()
+
+
+def test_trim_at_eos():
+    out = np.array([[1, 2], [0, 3], [0, 0], [5, 0]])
+    assert B.trim_at_eos(out, 0).shape[0] == 3      # step 2: every sequence's new token is eos
+    assert B.trim_at_eos(out, 9).shape[0] == 4      # never
+    assert B.trim_at_eos(out[:1], 1).shape[0] == 1  # not all rows
 
 
 def test_timing_rejects():

@@ -169,3 +169,104 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught: {name}"
+
+
+# ---------------------------------------------------------------- planted mistakes in the sampler
+import oracle.generate as G  # noqa: E402
+
+
+def _top_k_exactly_k(logits, k):
+    V = logits.shape[0]
+    if k <= 0 or k >= V:
+        return np.ones(V, dtype=bool)
+    keep = np.zeros(V, dtype=bool)
+    keep[np.argsort(-logits, kind="stable")[:k]] = True
+    return keep
+
+
+def _top_p_without_crossing_token(logits, weights, keep, p):
+    if p >= 1.0:
+        return keep, np.inf
+    idx = np.nonzero(keep)[0]
+    order = idx[np.lexsort((idx, -logits[idx]))]
+    cum = np.cumsum(weights[order] / weights[order].sum())
+    new = np.zeros_like(keep)
+    new[order[cum <= p]] = True
+    new[order[0]] = True
+    return new, np.inf
+
+
+def _top_p_before_top_k(logits, weights, keep, p):
+    # the nucleus measured with the probabilities of every token, not of the top-k survivors
+    return _top_p_plain(logits, np.exp(logits - logits.max()), keep, p)
+
+
+def _top_p_plain(logits, full, keep, p):
+    if p >= 1.0:
+        return keep, np.inf
+    idx = np.nonzero(keep)[0]
+    order = idx[np.lexsort((idx, -logits[idx]))]
+    cum = np.cumsum(full[order] / full.sum())
+    over = np.nonzero(cum > p)[0]
+    s = int(over[0]) if over.size else len(order) - 1
+    new = np.zeros_like(keep)
+    new[order[: s + 1]] = True
+    return new, np.inf
+
+
+def _top_p_ties_by_descending_index(logits, weights, keep, p):
+    if p >= 1.0:
+        return keep, np.inf
+    idx = np.nonzero(keep)[0]
+    order = idx[np.lexsort((-idx, -logits[idx]))]
+    cum = np.cumsum(weights[order] / weights[order].sum())
+    over = np.nonzero(cum > p)[0]
+    s = int(over[0]) if over.size else len(order) - 1
+    new = np.zeros_like(keep)
+    new[order[: s + 1]] = True
+    return new, np.inf
+
+
+def _make_next_token(side="right", temp_mul=False, greedy_last=False):
+    def next_token(logits, temperature, top_k=0, top_p=1.0, u=0.0):
+        l = np.asarray(logits, dtype=np.float64)
+        if np.isnan(l).any():
+            return G.Choice(-1, None, np.inf, np.inf)
+        if temperature == 0:
+            j = len(l) - 1 - int(np.argmax(l[::-1])) if greedy_last else int(np.argmax(l))
+            return G.Choice(j, None, np.inf, np.inf)
+        if not np.isfinite(l.max()):
+            return G.Choice(-1, None, np.inf, np.inf)
+        keep = G.top_k_keep(l, top_k)
+        z = l * temperature if temp_mul else l / temperature
+        w = np.where(keep, np.exp(z - z.max()), 0.0)
+        keep, pm = G.top_p_keep(l, w, keep, top_p)
+        w = np.where(keep, w, 0.0)
+        cdf = np.cumsum(w / w.sum())
+        j = min(int(np.searchsorted(cdf, u, side=side)), len(l) - 1)
+        return G.Choice(j, keep, pm, np.inf)
+    return next_token
+
+
+GEN_MISTAKES = {
+    "top-k keeps exactly k tokens (drops ties)": ("top_k_keep", _top_k_exactly_k),
+    "top-p drops the token that crosses p": ("top_p_keep", _top_p_without_crossing_token),
+    "top-p measured before top-k renormalises": ("top_p_keep", _top_p_before_top_k),
+    "top-p ranks equal logits by descending index": ("top_p_keep", _top_p_ties_by_descending_index),
+    "draw takes the first cdf >= u": ("next_token", _make_next_token(side="left")),
+    "temperature multiplies the logits": ("next_token", _make_next_token(temp_mul=True)),
+    "greedy takes the last maximum": ("next_token", _make_next_token(greedy_last=True)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GEN_MISTAKES))
+def test_sampler_pins_catch_planted_mistake(name, monkeypatch):
+    attr, bad = GEN_MISTAKES[name]
+    monkeypatch.setattr(G, attr, bad)
+    failed = []
+    for pin in P.SAMPLER_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught: {name}"
