@@ -373,6 +373,38 @@ def main():
                          "traffic": None, "algorithmic_bytes_per_launch": db["decode_attention_per_launch"],
                          "avg_launch_us": round(att_s * 1e6, 2)},
         }
+        # next-token choice on the decode step's logits [64, 49152] (smol_sample), and the
+        # decode step + greedy choice captured together, timed cold like the step
+        nxt = torch.empty(sd.batch, dtype=torch.int32, device=dev)
+        uni = torch.rand(sd.batch, generator=gen, device=dev, dtype=torch.float32)
+        samp = {}
+        for label, (t, k, p) in (("greedy", (0.0, 0, 1.0)), ("t0.8_topk50_topp0.9", (0.8, 50, 0.9)),
+                                 ("t1.0_topp0.9", (1.0, 0, 0.9))):
+            with torch.cuda.stream(stream):
+                ms, n = _kernel_time(B, "sample", lambda: [B.smol_sample(dlog, nxt, t, k, p, uni, stream=stream)
+                                                           for _ in range(5)], torch)
+            samp[label] = round(1e3 * ms / max(n, 1), 2)
+
+        def gstep():
+            dstep()
+            B.smol_sample(dlog, nxt, 0.0, 0, 1.0, uni, stream=stream)
+
+        gfn = gstep
+        if not args.no_graph:
+            gg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gg, stream=stream):
+                gstep()
+            gfn = gg.replay
+        flush = torch.empty(1 << 27, dtype=torch.float32, device=dev)
+        gen_ms = _rep_ms(gfn, args.decode_steps, torch, stream, before=lambda: flush.fill_(1.0))
+        del flush
+        g_s = float(np.median(gen_ms)) * 1e-3
+        out["generate"] = {
+            "workload": "one greedy generation step at the decode workload: decode step + smol_sample",
+            "ms_per_token_step": round(g_s * 1e3, 4),
+            "tokens_per_s": round(sd.batch / g_s, 1),
+            "sample_us": samp,
+        }
         del kc, vc
 
     if not args.no_decode:

@@ -122,6 +122,14 @@ __host__ __device__ inline int xcd_mode(int M, int N, int BN) {
   return 0;
 }
 
+// A store to global memory through a global-address-space pointer: the compiler
+// then emits global_store, never a flat store (the pointers here are loaded from the
+// kernel's parameter struct, where it cannot infer the address space itself).
+template <typename V>
+__device__ __forceinline__ void gstore(void *dst, const V &v) {
+  *reinterpret_cast<__attribute__((address_space(1))) V *>(reinterpret_cast<uintptr_t>(dst)) = v;
+}
+
 // Store N (4 or 8) consecutive floats as type O.
 template <typename O, int N>
 __device__ __forceinline__ void store_vec(O *dst, const float *v) {
@@ -131,7 +139,7 @@ __device__ __forceinline__ void store_vec(O *dst, const float *v) {
     for (int i = 0; i < 4; ++i)
       c[i] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i])) |
              ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i + 1])) << 16);
-    st16(dst, c);
+    gstore(dst, c);
   } else if constexpr (sizeof(O) == 2 && N == 4) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     u32x2 c;
@@ -139,12 +147,11 @@ __device__ __forceinline__ void store_vec(O *dst, const float *v) {
     for (int i = 0; i < 2; ++i)
       c[i] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i])) |
              ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i + 1])) << 16);
-    *reinterpret_cast<u32x2 *>(dst) = c;
+    gstore(dst, c);
   } else {
     static_assert(sizeof(O) == 4, "float output");
 #pragma unroll
-    for (int i = 0; i < N; i += 4)
-      *reinterpret_cast<f32x4 *>((float *)dst + i) = (f32x4){v[i], v[i + 1], v[i + 2], v[i + 3]};
+    for (int i = 0; i < N; i += 4) gstore((float *)dst + i, (f32x4){v[i], v[i + 1], v[i + 2], v[i + 3]});
   }
 }
 
@@ -762,8 +769,11 @@ static hipError_t launch_split(GemmParams p, int ks, hipStream_t s) {
 
 // Tile choice, from sweeps on MI355X over the model's shapes (2-stage rings were
 // never slower than deeper ones; 256-byte stages did not pay):
+//   * a plain store with >= 512 tiles of 256 x 256 (lm_head): 256 x 256 in 4 x 4 waves,
+//     which halves the L2 -> LDS bytes per FLOP of 128 x 128 (lm_head at batch 4 x seq
+//     512: 160 us against 200);
 //   * >= 512 tiles of 128 x 128: 128 x 128 with the four waves side by side along N,
-//     so each converted weight fragment feeds four MFMAs (lm_head);
+//     so each converted weight fragment feeds four MFMAs;
 //   * >= 512 tiles of 64 x 128: the same 1 x 4 wave layout (gate/up);
 //   * otherwise 64 x 64 in a 2 x 2 wave layout, for parallelism on small N (o_proj,
 //     down, QKV and every decode GEMM); 64 x 128 when a 128-wide head must stay in one
@@ -781,6 +791,8 @@ static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
     if (ks > 1) return launch_split<T, EPI>(p, ks, s);
   }
   const long tm128 = (p.M + 127) / 128, tm64 = (p.M + 63) / 64;
+  if (EPI == EPI_STORE && p.N % 256 == 0 && ((p.M + 255) / 256) * (long)(p.N / 256) >= 512)
+    return launch_cfg<T, 256, 256, 4, 4, 128, EPI, 2, 1>(p, s);
   if (EPI != EPI_QKV_ROPE || p.head_dim == 64)
     if (tm64 * (p.N / 64) < 128 && p.N % 64 == 0) return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 4, 2>(p, s);
   if (p.N % 128 == 0 && tm128 * (p.N / 128) >= 512) return launch_cfg<T, 128, 128, 1, 4, 128, EPI, 2, 2>(p, s);
