@@ -176,6 +176,7 @@ def gqa_attention(
     v: np.ndarray,
     q_pos: np.ndarray,
     k_pos: np.ndarray,
+    key_mask: Optional[np.ndarray] = None,
 ) -> np.ndarray:
     """Causal grouped-query attention by its definition.
 
@@ -185,10 +186,15 @@ def gqa_attention(
     with k_pos_j <= p go through softmax and weight v_j. Returns [B, n_heads, T, d].
 
     Sualeh77 model.py, "4. Attention" (scores / sqrt(d), triu(1) mask, softmax,
-    probs @ v; with a cache a single new token sees every cached key);
+    probs @ v; with a cache a single new token sees every cached key; an optional
+    padding mask is added to the scores as 0 / -inf per key);
     abi96062 components.py, GroupedQueryAttention (repeat_interleave + causal SDPA);
     nnterp SmolLM3, "Grouped-query attention" (head h reads kv head h // group,
-    scale head_dim ** -0.5)."""
+    scale head_dim ** -0.5).
+
+    key_mask: optional bool [B, S], False = key j of sequence b gets -inf added to
+    its score for every query and head. A query left with no visible key gets the
+    softmax of all -inf, NaN."""
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
     v = np.asarray(v, F64)
@@ -199,11 +205,13 @@ def gqa_attention(
     out = np.empty((B, nq, T, d), F64)
     scale = 1.0 / np.sqrt(d)
     for b in range(B):
+        vis = visible if key_mask is None else visible & np.asarray(key_mask[b], bool)[None, :]
         for h in range(nq):
             g = h // group
             s = (q[b, h] @ k[b, g].T) * scale  # [T, S]
-            s = np.where(visible, s, -np.inf)
-            out[b, h] = softmax(s, axis=-1) @ v[b, g]
+            s = np.where(vis, s, -np.inf)
+            with np.errstate(invalid="ignore"):
+                out[b, h] = softmax(s, axis=-1) @ v[b, g]
     return out
 
 
@@ -226,12 +234,14 @@ def swiglu_mlp(u: np.ndarray, w_gate, w_up, w_down) -> np.ndarray:
 # ---------------------------------------------------------------- the block
 
 
-def attention_sublayer(x, lw: LayerWeights, cfg: Config, positions, past_k=None, past_v=None, past_pos=None):
+def attention_sublayer(x, lw: LayerWeights, cfg: Config, positions, past_k=None, past_v=None, past_pos=None,
+                       key_mask=None):
     """self_attn(input_layernorm(x)) for x [B, T, H].
 
     Returns (attn_out [B,T,H], k_rot [B,n_kv,T,d], v [B,n_kv,T,d]); the cache
     holds keys after RoPE and before any head repetition (Sualeh77 model.py,
-    "4. Attention", the stored k_cache / v_cache)."""
+    "4. Attention", the stored k_cache / v_cache). key_mask: optional bool
+    [B, >= last position + 1] over absolute key positions (False: masked)."""
     x = np.asarray(x, F64)
     B, T, H = x.shape
     d = cfg.head_dim
@@ -248,7 +258,8 @@ def attention_sublayer(x, lw: LayerWeights, cfg: Config, positions, past_k=None,
         k_pos = np.concatenate([np.asarray(past_pos), positions])
     else:
         k_all, v_all, k_pos = k, v, positions
-    o = gqa_attention(q, k_all, v_all, positions, k_pos)  # [B, nq, T, d]
+    km = None if key_mask is None else np.asarray(key_mask, bool)[:, np.asarray(k_pos)]
+    o = gqa_attention(q, k_all, v_all, positions, k_pos, km)  # [B, nq, T, d]
     o = o.transpose(0, 2, 1, 3).reshape(B, T, cfg.n_heads * d)  # column h*d + e
     return o @ np.asarray(lw.wo, F64).T, k, v
 
@@ -259,17 +270,18 @@ def mlp_sublayer(h, lw: LayerWeights, cfg: Config):
     return swiglu_mlp(w, lw.w_gate, lw.w_up, lw.w_down)
 
 
-def block_forward(x, lw: LayerWeights, cfg: Config, pos0: int = 0, return_parts: bool = False):
+def block_forward(x, lw: LayerWeights, cfg: Config, pos0: int = 0, return_parts: bool = False, key_mask=None):
     """Pre-norm block: h = x + attn(norm1(x)); out = h + mlp(norm2(h)).
 
     nnterp SmolLM3, "The block, in order"; tohio block.py, SLMDecoderBlock.forward;
     abi96062 components.py, TransformerBlock.forward; Sualeh77 model.py,
-    "6. Transformer Block". Positions are pos0 .. pos0+T-1.
+    "6. Transformer Block". Positions are pos0 .. pos0+T-1; key_mask as in
+    attention_sublayer.
     Returns out (and, with return_parts, a dict with attn, mlp, k, v)."""
     x = np.asarray(x, F64)
     T = x.shape[1]
     positions = np.arange(pos0, pos0 + T)
-    attn, k, v = attention_sublayer(x, lw, cfg, positions)
+    attn, k, v = attention_sublayer(x, lw, cfg, positions, key_mask=key_mask)
     h = x + attn
     mlp = mlp_sublayer(h, lw, cfg)
     out = h + mlp
@@ -293,12 +305,16 @@ def lm_head(x: np.ndarray, final_norm, E, cfg: Config) -> np.ndarray:
     return z @ np.asarray(E, F64).T
 
 
-def model_prefill(ids, mw: ModelWeights, cfg: Config, logit_rows: Optional[Sequence[int]] = None, keep_cache: bool = False):
+def model_prefill(ids, mw: ModelWeights, cfg: Config, logit_rows: Optional[Sequence[int]] = None, keep_cache: bool = False,
+                  key_mask=None):
     """embed -> n_layers blocks -> final norm -> tied lm_head, positions 0..T-1.
 
     abi96062 model.py, SmolLM2Model.forward; Sualeh77 model.py, "7. Top-level".
     logit_rows, if given, selects the flattened rows (b*T + t) whose logits are
     returned (the head is row-wise, so this only skips outputs).
+    key_mask: optional bool [B, T] padding mask over key positions (False: the key
+    gets -inf added to its scores; Sualeh77 model.py, "4. Attention",
+    attention_mask).
     Returns logits [B, T, V] (or [len(rows), V]) and, with keep_cache, the list of
     per-layer (k_rot, v) each [B, n_kv, T, d]."""
     ids = np.asarray(ids)
@@ -308,7 +324,7 @@ def model_prefill(ids, mw: ModelWeights, cfg: Config, logit_rows: Optional[Seque
     x = embed(ids, mw.embed)
     cache = []
     for lw in mw.layers:
-        x, parts = block_forward(x, lw, cfg, 0, return_parts=True)
+        x, parts = block_forward(x, lw, cfg, 0, return_parts=True, key_mask=key_mask)
         if keep_cache:
             cache.append((parts["k"], parts["v"]))
     xf = x.reshape(B * T, cfg.hidden)
@@ -320,13 +336,14 @@ def model_prefill(ids, mw: ModelWeights, cfg: Config, logit_rows: Optional[Seque
     return (logits, cache) if keep_cache else logits
 
 
-def decode_step(ids, cache_len: int, mw: ModelWeights, cfg: Config, k_cache, v_cache):
+def decode_step(ids, cache_len: int, mw: ModelWeights, cfg: Config, k_cache, v_cache, key_mask=None):
     """One new token per sequence at position P = cache_len.
 
     k_cache / v_cache: per layer arrays [B, n_kv, >=P, d] holding keys after RoPE
     and values for positions 0..P-1. The new token's q, k are rotated at P, its
-    k', v appended, and it attends over keys 0..P with no mask (Sualeh77 model.py,
-    "7. Top-level" forward with past_key_values, and generate).
+    k', v appended, and it attends over keys 0..P (Sualeh77 model.py, "7. Top-level"
+    forward with past_key_values, and generate); key_mask, optional bool [B, >= P+1]
+    over key positions, masks keys as in gqa_attention.
     Returns (logits [B, V], new_k [L][B, n_kv, d], new_v [L][B, n_kv, d])."""
     ids = np.asarray(ids).reshape(-1, 1)
     B = ids.shape[0]
@@ -339,7 +356,7 @@ def decode_step(ids, cache_len: int, mw: ModelWeights, cfg: Config, k_cache, v_c
     for li, lw in enumerate(mw.layers):
         pk = np.asarray(k_cache[li])[:, :, :P]
         pv = np.asarray(v_cache[li])[:, :, :P]
-        attn, k, v = attention_sublayer(x, lw, cfg, positions, pk, pv, np.arange(P))
+        attn, k, v = attention_sublayer(x, lw, cfg, positions, pk, pv, np.arange(P), key_mask=key_mask)
         h = x + attn
         x = h + mlp_sublayer(h, lw, cfg)
         new_k.append(k[:, :, 0])

@@ -361,8 +361,10 @@ def pin_decode_equals_prefill():
         assert np.allclose(nv[li], cache_full[li][1][:, :, P], rtol=1e-12)
 
 
-def _brute_force_logits(cfg, mw, ids):
-    """Scalar pure-Python evaluation of the whole forward (for tiny sizes only)."""
+def _brute_force_logits(cfg, mw, ids, mask=None):
+    """Scalar pure-Python evaluation of the whole forward (for tiny sizes only).
+    mask[b][j] False: key j of sequence b gets weight 0 (its value still enters the
+    sum times 0, as in probs @ v); a query with no unmasked key gets NaN."""
     H, d, nq, nkv = cfg.hidden, cfg.head_dim, cfg.n_heads, cfg.n_kv_heads
     G = nq // nkv
     B, T = len(ids), len(ids[0])
@@ -399,15 +401,20 @@ def _brute_force_logits(cfg, mw, ids):
                 for h in range(nq):
                     g = h // G
                     qh = rot(qs[t][h * d:(h + 1) * d], t)
-                    sc = []
-                    for j in range(t + 1):
+                    seen = [j for j in range(t + 1) if mask is None or mask[b][j]]
+                    if not seen:
+                        for e in range(d):
+                            att[h * d + e] = float("nan")
+                        continue
+                    sc = {}
+                    for j in seen:
                         kj = rot(ks[j][g * d:(g + 1) * d], j)
-                        sc.append(sum(qh[e] * kj[e] for e in range(d)) / math.sqrt(d))
-                    mx = max(sc)
-                    ex = [math.exp(s - mx) for s in sc]
-                    z = sum(ex)
+                        sc[j] = sum(qh[e] * kj[e] for e in range(d)) / math.sqrt(d)
+                    mx = max(sc.values())
+                    ex = {j: math.exp(s - mx) for j, s in sc.items()}
+                    z = sum(ex.values())
                     for e in range(d):
-                        att[h * d + e] = sum(ex[j] / z * vs[j][g * d + e] for j in range(t + 1))
+                        att[h * d + e] = sum((ex[j] / z if j in ex else 0.0) * vs[j][g * d + e] for j in range(t + 1))
                 xs[t] = [xs[t][i] + o for i, o in enumerate(lin(att, W["wo"]))]
             for t in range(T):
                 w = norm(xs[t], lw.mlp_norm.tolist())
@@ -432,6 +439,39 @@ def pin_brute_force_tiny():
     want = _brute_force_logits(cfg, mw, ids.tolist())
     got = O.model_prefill(ids, mw, cfg)
     assert _rel(got, want) < 1e-12
+
+
+def pin_padding_mask():
+    """The pages' attention_mask adds 0 / -inf per key (Sualeh77 model.py, "4.
+    Attention"): an all-True mask changes nothing; a scalar evaluation with masked
+    keys agrees (a query whose every key is masked comes out NaN in both); a masked
+    token's embedding cannot reach any other position's logits; masking keys is not
+    masking queries."""
+    cfg = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=2, vocab=16, max_pos=32,
+                   rms_eps=1e-5, rope_theta=1e5)
+    rng = _rng(41)
+    mw = _rand_model(cfg, rng, std=0.5, norm_jitter=0.3)
+    ids = rng.integers(0, cfg.vocab, size=(2, 6))
+    full = np.ones((2, 6), bool)
+    assert np.array_equal(O.model_prefill(ids, mw, cfg, key_mask=full), O.model_prefill(ids, mw, cfg))
+    mask = np.array([[True, False, True, False, True, True], [True, True, False, True, False, True]])
+    want = _brute_force_logits(cfg, mw, ids.tolist(), mask.tolist())
+    got = O.model_prefill(ids, mw, cfg, key_mask=mask)
+    assert np.isfinite(got).all() and _rel(got, want) < 1e-12
+    # a query with every key masked: NaN at that position of the block's output only
+    x = O.embed(ids, mw.embed)
+    none0 = mask.copy()
+    none0[0, :2] = [False, True]  # query 0 of sequence 0 sees no key; query 1 sees key 1
+    out = O.block_forward(x, mw.layers[0], cfg, key_mask=none0)
+    assert np.isnan(out[0, 0]).all() and np.isfinite(out[0, 1:]).all() and np.isfinite(out[1]).all()
+    bf = _brute_force_logits(cfg, O.ModelWeights(mw.embed, mw.layers[:1], mw.final_norm), ids.tolist(), none0.tolist())
+    assert np.isnan(bf[0, 0]).all() and np.isfinite(bf[0, 1:]).all()
+    ids2 = ids.copy()
+    ids2[0, 3] = (ids2[0, 3] + 5) % cfg.vocab  # a masked token of sequence 0
+    got2 = O.model_prefill(ids2, mw, cfg, key_mask=mask)
+    keep = [t for t in range(6) if t != 3]
+    a, b_ = got[0, keep], got2[0, keep]
+    assert np.array_equal(np.isnan(a), np.isnan(b_)) and np.array_equal(a[~np.isnan(a)], b_[~np.isnan(b_)])
 
 
 # ---------------------------------------------------------------- next-token choice
@@ -575,6 +615,7 @@ ALL_PINS = [
     pin_gqa_mapping_smollm3,
     pin_decode_equals_prefill,
     pin_brute_force_tiny,
+    pin_padding_mask,
     pin_greedy_ties_and_nan,
     pin_top_k_keeps_ties,
     pin_top_p_hand_values,

@@ -59,8 +59,8 @@ def _rope_sign_flipped(z, positions, theta):
     return np.concatenate([a * c + b * s, b * c - a * s], axis=-1)
 
 
-def _make_attention(mapping="div", scale="sqrt", strict=False):
-    def attn(q, k, v, q_pos, k_pos):
+def _make_attention(mapping="div", scale="sqrt", strict=False, mask="keys"):
+    def attn(q, k, v, q_pos, k_pos, key_mask=None):
         q, k, v = (np.asarray(a, F64) for a in (q, k, v))
         B, nq, T, d = q.shape
         nkv = k.shape[1]
@@ -70,10 +70,16 @@ def _make_attention(mapping="div", scale="sqrt", strict=False):
         sc = 1.0 / np.sqrt(d) if scale == "sqrt" else 1.0 / d
         out = np.empty((B, nq, T, d))
         for b in range(B):
+            vb = vis
+            if key_mask is not None and mask == "keys":
+                vb = vis & np.asarray(key_mask[b], bool)[None, :]
+            elif key_mask is not None and mask == "queries":  # the mask applied to query rows
+                vb = vis & np.asarray(key_mask[b], bool)[-T:][:, None]
             for h in range(nq):
                 g = h // G if mapping == "div" else h % nkv
-                s = np.where(vis, (q[b, h] @ k[b, g].T) * sc, -np.inf)
-                out[b, h] = O.softmax(s) @ v[b, g]
+                s = np.where(vb, (q[b, h] @ k[b, g].T) * sc, -np.inf)
+                with np.errstate(invalid="ignore"):
+                    out[b, h] = O.softmax(s) @ v[b, g]
         return out
     return attn
 
@@ -88,10 +94,10 @@ def _silu_sigmoid(z):
     return 1.0 / (1.0 + np.exp(-np.asarray(z, F64)))
 
 
-def _block_no_mlp_residual(x, lw, cfg, pos0=0, return_parts=False):
+def _block_no_mlp_residual(x, lw, cfg, pos0=0, return_parts=False, key_mask=None):
     x = np.asarray(x, F64)
     positions = np.arange(pos0, pos0 + x.shape[1])
-    attn, k, v = O.attention_sublayer(x, lw, cfg, positions)
+    attn, k, v = O.attention_sublayer(x, lw, cfg, positions, key_mask=key_mask)
     h = x + attn
     mlp = O.mlp_sublayer(h, lw, cfg)
     out = mlp + attn  # the first residual's x is dropped
@@ -107,8 +113,8 @@ def _mlp_reads_stream_not_norm(h, lw, cfg):
 _orig_attention_sublayer = O.attention_sublayer
 
 
-def _attention_rotates_v(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None):
-    out, k, v = _orig_attention_sublayer(x, lw, cfg, positions, past_k, past_v, past_pos)
+def _attention_rotates_v(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None, key_mask=None):
+    out, k, v = _orig_attention_sublayer(x, lw, cfg, positions, past_k, past_v, past_pos, key_mask)
     vr = O.rope_rotate(v, np.asarray(positions), cfg.rope_theta)
     # recompute the output with rotated values
     B, T, H = np.asarray(x).shape
@@ -122,15 +128,16 @@ def _attention_rotates_v(x, lw, cfg, positions, past_k=None, past_v=None, past_p
         kp = np.concatenate([past_pos, positions])
     else:
         k_all, v_all, kp = k, vr, positions
-    o = O.gqa_attention(q, k_all, v_all, positions, kp).transpose(0, 2, 1, 3).reshape(B, T, -1)
+    km = None if key_mask is None else np.asarray(key_mask, bool)[:, np.asarray(kp)]
+    o = O.gqa_attention(q, k_all, v_all, positions, kp, km).transpose(0, 2, 1, 3).reshape(B, T, -1)
     return o @ np.asarray(lw.wo, F64).T, k, vr
 
 
-def _attention_wo_transposed(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None):
+def _attention_wo_transposed(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None, key_mask=None):
     import copy
     lw2 = copy.copy(lw)
     lw2.wo = np.asarray(lw.wo).T
-    return _orig_attention_sublayer(x, lw2, cfg, positions, past_k, past_v, past_pos)
+    return _orig_attention_sublayer(x, lw2, cfg, positions, past_k, past_v, past_pos, key_mask)
 
 
 def _lm_head_no_final_norm(x, final_norm, E, cfg):
@@ -147,6 +154,8 @@ MISTAKES = {
     "gqa head h % n_kv": ("gqa_attention", _make_attention(mapping="mod")),
     "attention scale 1/d": ("gqa_attention", _make_attention(scale="d")),
     "causal mask excludes the diagonal": ("gqa_attention", _make_attention(strict=True)),
+    "padding mask ignored": ("gqa_attention", _make_attention(mask="ignored")),
+    "padding mask applied to queries": ("gqa_attention", _make_attention(mask="queries")),
     "swiglu gate and up swapped": ("swiglu_mlp", _swiglu_swapped),
     "silu is the sigmoid": ("silu", _silu_sigmoid),
     "block drops the residual x": ("block_forward", _block_no_mlp_residual),
