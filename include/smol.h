@@ -155,13 +155,16 @@ smol_status smol_sample(const void *logits, int dtype, int batch, int vocab, int
 
 /* Generation (the loop of Sualeh77 model.py, "7. Top-level SmolLM2-135M Model
  * Architecture", generate: the prompt once, then one cached decode step per new
- * token). prompt_ids [batch, prompt_len] int32; the prompt fills the caches
- * [n_layers, batch, n_kv, cache_cap, head_dim] at 0 .. prompt_len-1 and the logits
- * of its last position give token 0 through smol_sample's rule (temperature, top_k,
- * top_p; uniforms [max_new, batch] device, row j for token j, NULL when temperature
- * is 0). Token j >= 1 comes from a decode step that feeds token j-1 at position
- * prompt_len + j - 1. out_ids [max_new, batch] int32 (device, written; token j of
- * sequence b at j * batch + b). All max_new tokens are produced: a caller that stops
+ * token). prompt_ids [batch, prompt_len] int32, right-padded when the prompts differ
+ * in length: prompt_lens NULL (every prompt has prompt_len tokens) or int32 [batch]
+ * (device), sequence b's length L_b = prompt_lens[b] clamped to [1, prompt_len]. The
+ * prompt fills the caches [n_layers, batch, n_kv, cache_cap, head_dim] at
+ * 0 .. prompt_len-1 (causality keeps the padding out of the real tokens) and the
+ * logits of position L_b - 1 give token 0 through smol_sample's rule (temperature,
+ * top_k, top_p; uniforms [max_new, batch] device, row j for token j, NULL when
+ * temperature is 0). Token j >= 1 comes from a decode step that feeds token j-1 at
+ * position L_b + j - 1 (overwriting the padding's cache entries). out_ids
+ * [max_new, batch] int32 (device, written; token j of sequence b at j * batch + b). All max_new tokens are produced: a caller that stops
  * at an end-of-sequence id trims afterwards. Requires prompt_len + max_new - 1 <=
  * min(cache_cap, max_pos). ws: smol_generate_workspace_size() bytes, 256-byte
  * aligned. Everything is enqueued on `stream`; nothing synchronises, so the whole
@@ -169,9 +172,39 @@ smol_status smol_sample(const void *logits, int dtype, int batch, int vocab, int
 smol_status smol_generate_workspace_size(const smol_config *cfg, int batch, int prompt_len, int max_new,
                                          int cache_cap, size_t *bytes);
 smol_status smol_generate(const smol_config *cfg, const smol_model_weights *w, const int32_t *prompt_ids,
-                          int batch, int prompt_len, int max_new, float temperature, int top_k, float top_p,
-                          const float *uniforms, int32_t *out_ids, void *k_cache, void *v_cache,
-                          int cache_cap, void *ws, size_t ws_bytes, void *stream);
+                          const int32_t *prompt_lens, int batch, int prompt_len, int max_new,
+                          float temperature, int top_k, float top_p, const float *uniforms,
+                          int32_t *out_ids, void *k_cache, void *v_cache, int cache_cap, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Prefill of a chunk, with an optional padding mask (Sualeh77 model.py, "4.
+ * Attention": the attention_mask added to the scores as 0 / -inf per key).
+ *   pos0: the chunk's tokens sit at positions pos0 .. pos0 + seq - 1. pos0 > 0
+ *     needs k_cache / v_cache, whose indices 0 .. pos0 - 1 hold the earlier tokens
+ *     (keys after RoPE); the chunk's k and v are written at pos0 .. pos0 + seq - 1
+ *     and each query attends to every key index <= its own position (absolute-
+ *     position causality; the pages leave T > 1 with a cache undefined).
+ *   key_mask: NULL, or uint8 [batch, cache_cap] (with caches) / [batch, seq]
+ *     (without), indexed by key position: 0 removes that key from every query of
+ *     its sequence; a query that is left with no key gets NaN outputs (the softmax
+ *     of all -inf), which then reach that sequence's later positions through the
+ *     residual stream only where they attend to it.
+ * Everything else as smol_model_prefill (which is this call with pos0 0 and no
+ * mask); requires pos0 + seq <= max_pos and, with caches, <= cache_cap. */
+smol_status smol_model_prefill_ex(const smol_config *cfg, const smol_model_weights *w,
+                                  const int32_t *ids, int batch, int seq, int pos0,
+                                  const uint8_t *key_mask, void *logits, void *k_cache,
+                                  void *v_cache, int cache_cap, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/* A decode step with an optional padding mask: key_mask NULL or uint8
+ * [batch, cache_cap] over key positions (0: the key is ignored by the new token).
+ * Everything else as smol_decode_step (which is this call with no mask). */
+smol_status smol_decode_step_ex(const smol_config *cfg, const smol_model_weights *w,
+                                const int32_t *ids, const int32_t *cache_len, int batch,
+                                const uint8_t *key_mask, void *k_cache, void *v_cache,
+                                int cache_cap, void *logits, void *ws, size_t ws_bytes,
+                                void *stream);
 
 /* Static text for a status code. */
 const char *smol_status_string(smol_status s);

@@ -25,6 +25,7 @@ SMOL_OP_BLOCK, SMOL_OP_PREFILL, SMOL_OP_DECODE = 0, 1, 2
 KERNELS = ["embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head",
            "decode_attention", "decode_combine", "sample"]
 EXPORTED = ["smol_workspace_size", "smol_block_forward", "smol_model_prefill", "smol_decode_step",
+            "smol_model_prefill_ex", "smol_decode_step_ex",
             "smol_sample", "smol_generate_workspace_size", "smol_generate",
             "smol_status_string", "smol_last_error", "smol_timing_begin", "smol_timing_end"]
 
@@ -75,8 +76,12 @@ def lib() -> ctypes.CDLL:
         f32, i64 = ctypes.c_float, ctypes.c_int64
         L.smol_sample.argtypes = [vp, i32, i32, i32, i64, f32, i32, f32, vp, vp, vp]
         L.smol_generate_workspace_size.argtypes = [cfgp, i32, i32, i32, i32, ctypes.POINTER(sz)]
-        L.smol_generate.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, i32, i32, i32, f32, i32, f32, vp,
-                                    vp, vp, vp, i32, vp, sz, vp]
+        L.smol_generate.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, vp, i32, i32, i32, f32, i32, f32,
+                                    vp, vp, vp, vp, i32, vp, sz, vp]
+        L.smol_model_prefill_ex.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, i32, i32, i32, vp, vp, vp,
+                                            vp, i32, vp, sz, vp]
+        L.smol_decode_step_ex.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, vp, i32, vp, vp, vp, i32,
+                                          vp, vp, sz, vp]
         L.smol_status_string.argtypes = [i32]
         L.smol_status_string.restype = ctypes.c_char_p
         L.smol_last_error.argtypes = []
@@ -271,15 +276,17 @@ def smol_generate_workspace_size(cfg: Config, batch: int, prompt_len: int, max_n
 def smol_generate(cfg: Config, w: ModelWeights, prompt_ids: torch.Tensor, max_new: int, k_cache: torch.Tensor,
                   v_cache: torch.Tensor, out_ids: torch.Tensor, temperature: float = 0.0, top_k: int = 0,
                   top_p: float = 1.0, uniforms: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                  stream=None) -> torch.Tensor:
-    """prompt_ids int32 [B, T]; caches [L, B, n_kv, cap, d]; out_ids int32 [max_new, B] (written);
-    uniforms float32 [max_new, B] when temperature > 0."""
+                  stream=None, prompt_lens: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """prompt_ids int32 [B, T] (right-padded); prompt_lens int32 [B] or None; caches
+    [L, B, n_kv, cap, d]; out_ids int32 [max_new, B] (written); uniforms float32
+    [max_new, B] when temperature > 0."""
     B, T = prompt_ids.shape
     cap = k_cache.shape[3]
     if ws is None:
         ws = torch.empty(smol_generate_workspace_size(cfg, B, T, max_new, cap), dtype=torch.uint8,
                          device=prompt_ids.device)
-    _check(lib().smol_generate(ctypes.byref(cfg.c()), ctypes.byref(w.c), _ptr(prompt_ids), B, T, max_new,
+    _check(lib().smol_generate(ctypes.byref(cfg.c()), ctypes.byref(w.c), _ptr(prompt_ids), _ptr(prompt_lens), B, T,
+                               max_new,
                                float(temperature), int(top_k), float(top_p), _ptr(uniforms), _ptr(out_ids),
                                _ptr(k_cache), _ptr(v_cache), cap, _ptr(ws), ws.numel(), _stream(stream)))
     return out_ids
@@ -292,6 +299,40 @@ def trim_at_eos(out_ids: np.ndarray, eos_id: int) -> np.ndarray:
         if (out_ids[j] == eos_id).all():
             return out_ids[: j + 1]
     return out_ids
+
+
+def smol_model_prefill_ex(cfg: Config, w: ModelWeights, ids: torch.Tensor, logits: torch.Tensor, pos0: int = 0,
+                          key_mask: Optional[torch.Tensor] = None, k_cache: Optional[torch.Tensor] = None,
+                          v_cache: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """ids int32 [B, T] at positions pos0 ..; key_mask uint8 [B, cap] (with caches) or [B, T]."""
+    B, T = ids.shape
+    if ws is None:
+        ws = workspace(cfg, SMOL_OP_PREFILL, B, T, ids.device)
+    cap = k_cache.shape[3] if k_cache is not None else 0
+    if key_mask is not None and (key_mask.dtype != torch.uint8 or tuple(key_mask.shape) != (B, cap if k_cache is not None else T)):
+        raise ValueError("key_mask must be uint8 [B, cache_cap] (with caches) or [B, seq]")
+    _check(lib().smol_model_prefill_ex(ctypes.byref(cfg.c()), ctypes.byref(w.c), _ptr(ids), B, T, pos0,
+                                       _ptr(key_mask), _ptr(logits), _ptr(k_cache), _ptr(v_cache), cap, _ptr(ws),
+                                       ws.numel(), _stream(stream)))
+    return logits
+
+
+def smol_decode_step_ex(cfg: Config, w: ModelWeights, ids: torch.Tensor, cache_len: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, logits: torch.Tensor,
+                        key_mask: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """As smol_decode_step, with key_mask uint8 [B, cap] (or None)."""
+    B = ids.shape[0]
+    cap = k_cache.shape[3]
+    if key_mask is not None and (key_mask.dtype != torch.uint8 or tuple(key_mask.shape) != (B, cap)):
+        raise ValueError("key_mask must be uint8 [B, cache_cap]")
+    if ws is None:
+        ws = workspace(cfg, SMOL_OP_DECODE, B, cap, ids.device)
+    _check(lib().smol_decode_step_ex(ctypes.byref(cfg.c()), ctypes.byref(w.c), _ptr(ids), _ptr(cache_len), B,
+                                     _ptr(key_mask), _ptr(k_cache), _ptr(v_cache), cap, _ptr(logits), _ptr(ws),
+                                     ws.numel(), _stream(stream)))
+    return logits
 
 
 def smol_timing_begin(kernel: str, max_launches: int):

@@ -182,6 +182,8 @@ struct LayerCtx {
   void *kc, *vc;
   int cap, kv_off, q_key_off;
   const int *cache_len;  // decode only
+  const uint8_t *key_mask;  // [B, mask_ld] over key indices, or nullptr
+  int mask_ld;
   float inv_freq[64];
   hipStream_t s;
 };
@@ -212,11 +214,11 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, 
     int chunk;
     const int splits = smol::decode_splits(std::min(c.cap, D.max_pos), &chunk);
     smol::DecodeAttnArgs da{q, c.kc, c.vc, o, c.cache_len, c.B, D.nq, D.nkv, D.d, c.cap, D.max_pos, splits, chunk,
-                            (float *)(c.ws + c.lay.part)};
+                            (float *)(c.ws + c.lay.part), c.key_mask, c.mask_ld};
     hipError_t e = smol::attention_decode<T>(da, s);
     if (e != hipSuccess) return fail(SMOL_ERR_HIP, "attention_decode: %s", hipGetErrorString(e));
   } else {
-    smol::AttnArgs aa{q, c.kc, c.vc, o, c.B, c.T, D.nq, D.nkv, D.d, c.cap, c.q_key_off};
+    smol::AttnArgs aa{q, c.kc, c.vc, o, c.B, c.T, D.nq, D.nkv, D.d, c.cap, c.q_key_off, c.key_mask, c.mask_ld};
     SMOL_LAUNCH(SMOL_K_ATTENTION, smol::attention_prefill<T>(aa, s));
   }
   // x += o W_o^T; leaves xs for mlp_norm, the new sums in ss_q (ss_p: the old ones)
@@ -291,9 +293,12 @@ smol_status block_impl(const Dims &D, const smol_layer_weights *w, const float *
   return run_layer<T>(c, w, x_out, nullptr);
 }
 
+// Tokens at positions pos0 .. pos0 + T_ - 1 (pos0 > 0 needs the caches, which then
+// hold positions 0 .. pos0 - 1 already: a chunk of a longer prefill).
 template <typename T>
 smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32_t *ids, int B, int T_, void *logits,
-                         void *kc, void *vc, int cap, char *ws, const Ws &lay, hipStream_t s) {
+                         void *kc, void *vc, int cap, char *ws, const Ws &lay, hipStream_t s, int pos0 = 0,
+                         const uint8_t *key_mask = nullptr) {
   float *x = (float *)(ws + lay.x);
   const int M = B * T_;
   LayerCtx c{};
@@ -302,7 +307,9 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
   c.lay = lay;
   c.B = B;
   c.T = T_;
-  c.pos0 = 0;
+  c.pos0 = pos0;
+  c.key_mask = key_mask;
+  c.mask_ld = kc ? cap : T_;
   c.s = s;
   fill_inv_freq(D, c.inv_freq);
   smol_status st0 = prologue<T>(c, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, M);
@@ -312,7 +319,7 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
     if (kc) {
       c.kc = (char *)kc + l * layer_elems * D.esz;
       c.vc = (char *)vc + l * layer_elems * D.esz;
-      c.cap = cap; c.kv_off = 0; c.q_key_off = 0;
+      c.cap = cap; c.kv_off = 0; c.q_key_off = pos0;
     } else {
       c.kc = ws + lay.k; c.vc = ws + lay.v; c.cap = T_; c.kv_off = 0; c.q_key_off = 0;
     }
@@ -326,7 +333,8 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
 
 template <typename T>
 smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_t *ids, const int32_t *cache_len,
-                        int B, void *kc, void *vc, int cap, void *logits, char *ws, const Ws &lay, hipStream_t s) {
+                        int B, void *kc, void *vc, int cap, void *logits, char *ws, const Ws &lay, hipStream_t s,
+                        const uint8_t *key_mask = nullptr) {
   float *x = (float *)(ws + lay.x);
   LayerCtx c{};
   c.D = &D;
@@ -336,6 +344,8 @@ smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_
   c.T = 1;
   c.cap = cap;
   c.cache_len = cache_len;
+  c.key_mask = key_mask;
+  c.mask_ld = cap;
   c.s = s;
   fill_inv_freq(D, c.inv_freq);
   smol_status st0 = prologue<T>(c, ids, (const T *)w->embed, x, x, (const T *)w->layers[0].attn_norm, B);
@@ -375,9 +385,10 @@ GenWs gen_layout(const Dims &D, int B, int T, int max_new, int cap) {
 }
 
 template <typename T>
-smol_status generate_impl(const Dims &D, const smol_model_weights *w, const int32_t *prompt, int B, int T_,
-                          int max_new, float temperature, int top_k, float top_p, const float *uniforms,
-                          int32_t *out_ids, void *kc, void *vc, int cap, char *ws, const GenWs &g, hipStream_t s) {
+smol_status generate_impl(const Dims &D, const smol_model_weights *w, const int32_t *prompt, const int32_t *lens,
+                          int B, int T_, int max_new, float temperature, int top_k, float top_p,
+                          const float *uniforms, int32_t *out_ids, void *kc, void *vc, int cap, char *ws,
+                          const GenWs &g, hipStream_t s) {
   smol_status st = prefill_impl<T>(D, w, prompt, B, T_, nullptr, kc, vc, cap, ws, g.pre, s);
   if (st != SMOL_OK) return st;
   using A = Act<T>;
@@ -386,7 +397,7 @@ smol_status generate_impl(const Dims &D, const smol_model_weights *w, const int3
   T *logits = (T *)(ws + g.logits);
   int32_t *pos = (int32_t *)(ws + g.pos);
   hipError_t e = smol::gather_last<T>((const A *)(ws + g.pre.xs), (const float *)(ws + g.pre.ss_p),
-                                      (const float *)(ws + g.pre.ss_q), B, T_, D.H, xs_last, ssp, ssq, s);
+                                      (const float *)(ws + g.pre.ss_q), B, T_, D.H, lens, xs_last, ssp, ssq, s);
   if (e != hipSuccess) return fail(SMOL_ERR_HIP, "gather_last: %s", hipGetErrorString(e));
   SMOL_LAUNCH(SMOL_K_LM_HEAD, smol::gemm_store<T>(xs_last, smol::NormIn{ssp, ssq, D.eps}, (const T *)w->embed, B, D.V,
                                                   D.H, logits, 0, nullptr, s));
@@ -398,7 +409,7 @@ smol_status generate_impl(const Dims &D, const smol_model_weights *w, const int3
   };
   if ((st = sample(0)) != SMOL_OK) return st;
   if (max_new > 1) {
-    e = smol::fill_positions(pos, B, max_new - 1, T_, s);
+    e = smol::fill_positions(pos, B, max_new - 1, T_, lens, s);
     if (e != hipSuccess) return fail(SMOL_ERR_HIP, "fill_positions: %s", hipGetErrorString(e));
   }
   for (int step = 1; step < max_new; ++step) {
@@ -461,9 +472,9 @@ smol_status smol_block_forward(const smol_config *cfg, const smol_layer_weights 
                 : block_impl<float>(D, w, x_in, x_out, batch, seq, pos0, k_cache, v_cache, cache_cap, (char *)ws, lay, s);
 }
 
-smol_status smol_model_prefill(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids, int batch,
-                               int seq, void *logits, void *k_cache, void *v_cache, int cache_cap, void *ws,
-                               size_t ws_bytes, void *stream) {
+smol_status smol_model_prefill_ex(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids, int batch,
+                                  int seq, int pos0, const uint8_t *key_mask, void *logits, void *k_cache,
+                                  void *v_cache, int cache_cap, void *ws, size_t ws_bytes, void *stream) {
   g_err.clear();
   Dims D;
   smol_status st = check_config(cfg, &D);
@@ -471,19 +482,39 @@ smol_status smol_model_prefill(const smol_config *cfg, const smol_model_weights 
   if ((st = check_model(D, w)) != SMOL_OK) return st;
   if (!ids || !logits) return fail(SMOL_ERR_INVALID_ARG, "ids / logits is NULL");
   if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d, seq %d must be >= 1", batch, seq);
-  if (seq > D.max_pos) return fail(SMOL_ERR_INVALID_ARG, "seq %d exceeds max_pos %d", seq, D.max_pos);
+  if (pos0 < 0) return fail(SMOL_ERR_INVALID_ARG, "pos0 %d < 0", pos0);
+  if ((long)pos0 + seq > D.max_pos)
+    return fail(SMOL_ERR_INVALID_ARG, "pos0 + seq = %ld exceeds max_pos %d", (long)pos0 + seq, D.max_pos);
   if (!k_cache != !v_cache) return fail(SMOL_ERR_INVALID_ARG, "k_cache and v_cache must both be set or both NULL");
-  if (k_cache && cache_cap < seq) return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d < seq %d", cache_cap, seq);
+  if (pos0 > 0 && !k_cache) return fail(SMOL_ERR_INVALID_ARG, "pos0 %d > 0 needs the caches of positions before it", pos0);
+  if (k_cache && cache_cap < pos0 + seq)
+    return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d < pos0 + seq = %d", cache_cap, pos0 + seq);
   Ws lay;
   if ((st = check_ws(D, SMOL_OP_PREFILL, batch, seq, ws, ws_bytes, &lay)) != SMOL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  return D.bf16 ? prefill_impl<bf16>(D, w, ids, batch, seq, logits, k_cache, v_cache, cache_cap, (char *)ws, lay, s)
-                : prefill_impl<float>(D, w, ids, batch, seq, logits, k_cache, v_cache, cache_cap, (char *)ws, lay, s);
+  return D.bf16 ? prefill_impl<bf16>(D, w, ids, batch, seq, logits, k_cache, v_cache, cache_cap, (char *)ws, lay, s,
+                                     pos0, key_mask)
+                : prefill_impl<float>(D, w, ids, batch, seq, logits, k_cache, v_cache, cache_cap, (char *)ws, lay, s,
+                                      pos0, key_mask);
+}
+
+smol_status smol_model_prefill(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids, int batch,
+                               int seq, void *logits, void *k_cache, void *v_cache, int cache_cap, void *ws,
+                               size_t ws_bytes, void *stream) {
+  return smol_model_prefill_ex(cfg, w, ids, batch, seq, 0, nullptr, logits, k_cache, v_cache, cache_cap, ws, ws_bytes,
+                               stream);
 }
 
 smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids,
                              const int32_t *cache_len, int batch, void *k_cache, void *v_cache, int cache_cap,
                              void *logits, void *ws, size_t ws_bytes, void *stream) {
+  return smol_decode_step_ex(cfg, w, ids, cache_len, batch, nullptr, k_cache, v_cache, cache_cap, logits, ws, ws_bytes,
+                             stream);
+}
+
+smol_status smol_decode_step_ex(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids,
+                                const int32_t *cache_len, int batch, const uint8_t *key_mask, void *k_cache,
+                                void *v_cache, int cache_cap, void *logits, void *ws, size_t ws_bytes, void *stream) {
   g_err.clear();
   Dims D;
   smol_status st = check_config(cfg, &D);
@@ -496,8 +527,10 @@ smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w
   Ws lay;
   if ((st = check_ws(D, SMOL_OP_DECODE, batch, cache_cap, ws, ws_bytes, &lay)) != SMOL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  return D.bf16 ? decode_impl<bf16>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay, s)
-                : decode_impl<float>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay, s);
+  return D.bf16 ? decode_impl<bf16>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay, s,
+                                    key_mask)
+                : decode_impl<float>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay,
+                                     s, key_mask);
 }
 
 smol_status smol_generate_workspace_size(const smol_config *cfg, int batch, int prompt_len, int max_new,
@@ -513,8 +546,9 @@ smol_status smol_generate_workspace_size(const smol_config *cfg, int batch, int 
   return SMOL_OK;
 }
 
-smol_status smol_generate(const smol_config *cfg, const smol_model_weights *w, const int32_t *prompt_ids, int batch,
-                          int prompt_len, int max_new, float temperature, int top_k, float top_p,
+smol_status smol_generate(const smol_config *cfg, const smol_model_weights *w, const int32_t *prompt_ids,
+                          const int32_t *prompt_lens, int batch, int prompt_len, int max_new, float temperature,
+                          int top_k, float top_p,
                           const float *uniforms, int32_t *out_ids, void *k_cache, void *v_cache, int cache_cap,
                           void *ws, size_t ws_bytes, void *stream) {
   g_err.clear();
@@ -539,10 +573,10 @@ smol_status smol_generate(const smol_config *cfg, const smol_model_weights *w, c
   const GenWs g = gen_layout(D, batch, prompt_len, max_new, cache_cap);
   if (ws_bytes < g.total) return fail(SMOL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, g.total);
   hipStream_t s = (hipStream_t)stream;
-  return D.bf16 ? generate_impl<bf16>(D, w, prompt_ids, batch, prompt_len, max_new, temperature, top_k, top_p,
-                                      uniforms, out_ids, k_cache, v_cache, cache_cap, (char *)ws, g, s)
-                : generate_impl<float>(D, w, prompt_ids, batch, prompt_len, max_new, temperature, top_k, top_p,
-                                       uniforms, out_ids, k_cache, v_cache, cache_cap, (char *)ws, g, s);
+  return D.bf16 ? generate_impl<bf16>(D, w, prompt_ids, prompt_lens, batch, prompt_len, max_new, temperature, top_k,
+                                      top_p, uniforms, out_ids, k_cache, v_cache, cache_cap, (char *)ws, g, s)
+                : generate_impl<float>(D, w, prompt_ids, prompt_lens, batch, prompt_len, max_new, temperature, top_k,
+                                       top_p, uniforms, out_ids, k_cache, v_cache, cache_cap, (char *)ws, g, s);
 }
 
 smol_status smol_sample(const void *logits, int dtype, int batch, int vocab, int64_t row_stride, float temperature,

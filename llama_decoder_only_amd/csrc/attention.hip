@@ -19,8 +19,10 @@
 // converted to the fp16 operand type once per staged round, in LDS, when waves walk
 // many rounds; with a 4-way key split (short key ranges, one or two rounds) each wave
 // converts the fragments it reads instead, which spares the extra barrier per round.
-// Keys come in tiles in increasing order, so tile 0 (always visible) fixes a
-// finite running max before any fully masked tile can occur.
+// Keys come in tiles in increasing order, so without a key mask tile 0 (always
+// visible) fixes a finite running max before any fully masked tile can occur; with
+// one, a row may see no key yet (or ever): its max stays -inf, its probabilities 0,
+// and a row that never sees a key ends as 0/0 = NaN.
 #include "common.h"
 #include "kernels.h"
 
@@ -46,7 +48,10 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const char *p) {
 }
 
 
-template <typename W, int D, int G, int QW, int KS, int S>
+// MASKED: the launch has a key mask. A separate instantiation: the mask's byte
+// loads inside the ring loop make the compiler drain every outstanding load (it
+// cannot see the ring's direct-to-LDS copies), which the unmasked kernel must not pay.
+template <typename W, int D, int G, int QW, int KS, int S, bool MASKED>
 __global__ void __launch_bounds__(64 * G * QW * KS)
 attn_prefill_kernel(const AttnArgs a) {
   using T = Act<W>;  // operand type of q, p and o; cached k, v (type W) convert as they leave LDS
@@ -218,6 +223,16 @@ attn_prefill_kernel(const AttnArgs a) {
       // split may meet tiles where some of its queries see no key yet: their max stays
       // -inf and their probabilities 0.
       const bool need_mask = k0 + BKV - 1 > q0 + a.q_key_off;
+      if constexpr (MASKED) {  // bit j of kb: key k0 + j may be attended (lane j loads its byte)
+        const int kj = k0 + lane;
+        const bool kok = kj < nkeys && a.key_mask[(size_t)b * a.mask_ld + kj] != 0;
+        const unsigned long long kb = __ballot(kok);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (!((kb >> (32 * i + acc_row(rr, lane))) & 1ull)) s[i][rr] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -228,7 +243,7 @@ attn_prefill_kernel(const AttnArgs a) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx * c_log2);
-      const float m_use = (KS > 1 && m_new == -INFINITY) ? 0.f : m_new;
+      const float m_use = ((KS > 1 || MASKED) && m_new == -INFINITY) ? 0.f : m_new;  // no key seen yet: p = 0
       float ls = 0.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -285,7 +300,8 @@ attn_prefill_kernel(const AttnArgs a) {
 
   if constexpr (KS > 1) {
     // ---- merge the key splits: splits 1..KS-1 park (o, m, l) in LDS, split 0 folds
-    // them into its own state. Split 0 saw tile 0, so its max is finite.
+    // them into its own state. A split that saw no key has max -inf and weight 0
+    // (split 0 saw tile 0, so without a mask its max is finite).
     __syncthreads();  // every wave is done with the ring
     float *part = reinterpret_cast<float *>(smem);
     if (ks > 0) {
@@ -302,7 +318,7 @@ attn_prefill_kernel(const AttnArgs a) {
     float m_tot = m_run;
 #pragma unroll
     for (int k = 1; k < KS; ++k) m_tot = fmaxf(m_tot, part[(((k - 1) * G * QW + hq) * PSTATE + DT * 16) * 64 + lane]);
-    const float f0 = __builtin_amdgcn_exp2f(m_run - m_tot);
+    const float f0 = (MASKED && m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_tot);
     l_run *= f0;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] *= f0;
@@ -335,7 +351,9 @@ static hipError_t launch_attn_cfg(const AttnArgs &a, hipStream_t s) {
   constexpr int ROUND = KS * 2 * 64 * D * (int)sizeof(T);
   constexpr int S = (3 * ROUND <= 98304) ? 3 : 2;
   const int nqb = (a.T + 32 * QW - 1) / (32 * QW);
-  return launch(attn_prefill_kernel<T, D, G, QW, KS, S>, dim3(nqb * a.B * a.n_kv), dim3(64 * G * QW * KS), s, a);
+  const dim3 grid(nqb * a.B * a.n_kv), block(64 * G * QW * KS);
+  if (a.key_mask) return launch(attn_prefill_kernel<T, D, G, QW, KS, S, true>, grid, block, s, a);
+  return launch(attn_prefill_kernel<T, D, G, QW, KS, S, false>, grid, block, s, a);
 }
 
 template <typename T, int D, int G>

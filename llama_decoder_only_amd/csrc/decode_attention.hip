@@ -2,9 +2,10 @@
 // split along the keys so that the whole cache streams through every CU.
 //
 // The new token of sequence b sits at position P = cache_len[b] and sees keys
-// 0 .. P with no mask (Sualeh77 model.py, "4. Attention": with a cache the single
-// new token attends to all past keys and itself). This step is bound by HBM:
-// every cached key and value is read once.
+// 0 .. P (Sualeh77 model.py, "4. Attention": with a cache the single new token
+// attends to all past keys and itself), minus those an optional key mask removes
+// (the pages' additive padding mask). This step is bound by HBM: every cached key
+// and value is read once.
 //
 // Kernel 1, grid (splits, n_kv, B), 256 threads: a workgroup takes `chunk`
 // consecutive keys of kv head g and serves all G query heads of the group.
@@ -77,10 +78,12 @@ decode_attn_kernel(const DecodeAttnArgs a) {
   constexpr int PASSES = CHUNK / KPP;
   {
     Chunk16 kc[PASSES];
+    bool keep[PASSES];
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
       const int j = min(kk + it * KPP, n - 1);  // rows past the chunk re-read its last key
       kc[it] = ld16(kb + (size_t)j * D);
+      keep[it] = !a.key_mask || a.key_mask[(size_t)b * a.mask_ld + k_begin + j] != 0;
     }
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
@@ -99,7 +102,7 @@ decode_attn_kernel(const DecodeAttnArgs a) {
         for (int hh = 0; hh < G; ++hh) dot[hh] += __shfl_xor(dot[hh], o, 64);
       if (dl == 0 && j < n)
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) S[hh][j] = dot[hh] * c_log2;
+        for (int hh = 0; hh < G; ++hh) S[hh][j] = keep[it] ? dot[hh] * c_log2 : -INFINITY;
     }
   }
   __syncthreads();
@@ -110,9 +113,10 @@ decode_attn_kernel(const DecodeAttnArgs a) {
     float m = -INFINITY;
     for (int j = lane; j < n; j += 64) m = fmaxf(m, S[hh][j]);
     m = wave_max(m);
+    const float mu = m == -INFINITY ? 0.f : m;  // every key of the chunk masked: p = 0
     float l = 0.f;
     for (int j = lane; j < n; j += 64) {
-      const float p = exp2f(S[hh][j] - m);
+      const float p = exp2f(S[hh][j] - mu);
       S[hh][j] = p;
       l += p;
     }
@@ -200,13 +204,13 @@ decode_combine_kernel(const DecodeAttnArgs a) {
 #pragma unroll
     for (int i = 0; i < R; ++i)
       if (s0 + i < used) mr = fmaxf(mr, ms[i]);
-    const float f = exp2f(m - mr);  // split 0 makes mr finite
+    const float f = m == -INFINITY ? 0.f : exp2f(m - mr);  // a split with no key weighs 0
     l *= f;
     acc *= f;
 #pragma unroll
     for (int i = 0; i < R; ++i)
       if (s0 + i < used) {
-        const float fi = exp2f(ms[i] - mr);
+        const float fi = ms[i] == -INFINITY ? 0.f : exp2f(ms[i] - mr);
         l += fi * ls[i];
         acc += fi * os[i];
       }

@@ -76,25 +76,31 @@ template <typename T>
 hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, float *ss_new, float *ss_old,
                    const T *w, Act<T> *xs, float eps, int M, int H, int V, const RopeIn &rope, hipStream_t s);
 
-// Generation: the last position of each sequence's prefill state (xs row and its two
-// sums-of-squares columns), and the per-step decode positions pos[j * B + b] = first + j.
+// Generation: the last prompt position of each sequence's prefill state (xs row and
+// its two sums-of-squares columns), and the per-step decode positions
+// pos[j * B + b] = len_b + j, with len_b = lens[b] clamped to [1, T] (T: no lens).
 template <typename T>
-hipError_t gather_last(const Act<T> *xs, const float *ssp, const float *ssq, int B, int T_, int H, Act<T> *xs_out,
-                       float *ssp_out, float *ssq_out, hipStream_t s);
-hipError_t fill_positions(int32_t *pos, int B, int n, int first, hipStream_t s);
+hipError_t gather_last(const Act<T> *xs, const float *ssp, const float *ssq, int B, int T_, int H, const int32_t *lens,
+                       Act<T> *xs_out, float *ssp_out, float *ssq_out, hipStream_t s);
+hipError_t fill_positions(int32_t *pos, int B, int n, int T, const int32_t *lens, hipStream_t s);
 
 // Causal GQA attention over a [B, n_kv, cap, d] key/value store. Query t of
-// sequence b sits at key index t + q_key_off; it sees key indices <= that.
+// sequence b sits at key index t + q_key_off; it sees key indices <= that, except
+// those whose key_mask byte is 0 (key_mask: [B, mask_ld] uint8 over key indices, or
+// nullptr). A query left with no key comes out NaN.
 struct AttnArgs {
   const void *q;  // [B*T, n_heads*d] operand type; k, v, o: storage / operand types
   const void *k, *v;
   void *o;        // [B*T, n_heads*d]
   int B, T, n_heads, n_kv, head_dim, cap, q_key_off;
+  const uint8_t *key_mask;
+  int mask_ld;
 };
 template <typename T>
 hipError_t attention_prefill(const AttnArgs &a, hipStream_t s);
 
 // Decode: one query per sequence at key index cache_len[b]; split-K partials in ws.
+// key_mask as in AttnArgs ([B, mask_ld], or nullptr).
 struct DecodeAttnArgs {
   const void *q;  // [B, n_heads*d]
   const void *k, *v;
@@ -102,6 +108,8 @@ struct DecodeAttnArgs {
   const int *cache_len;
   int B, n_heads, n_kv, head_dim, cap, max_pos, splits, chunk;
   float *part;    // [B, n_heads, splits, head_dim + 2]
+  const uint8_t *key_mask;
+  int mask_ld;
 };
 template <typename T>
 hipError_t attention_decode(const DecodeAttnArgs &a, hipStream_t s);

@@ -60,15 +60,21 @@ hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, f
                 V, rope);
 }
 
-// Generation helpers. gather_last: row b of xs_out and of the two sums-of-squares
-// buffers ([H/64, B]) takes row b*T + T-1 of the prefill's ([H/64, B*T]), so that the
-// head runs on each sequence's last position only.
+// Generation helpers. The prompt length of sequence b is lens[b] clamped to
+// [1, T] (T when lens is nullptr): right-padded prompts of different lengths.
+__device__ __forceinline__ int prompt_len_of(const int32_t *lens, int b, int T) {
+  return lens ? min(max(lens[b], 1), T) : T;
+}
+
+// gather_last: row b of xs_out and of the two sums-of-squares buffers ([H/64, B])
+// takes row b*T + len_b - 1 of the prefill's ([H/64, B*T]), so that the head runs
+// on each sequence's last prompt position only.
 template <typename A>
 __global__ void __launch_bounds__(256)
-gather_last_kernel(const A *xs, const float *ssp, const float *ssq, int B, int T, int H, A *xs_out, float *ssp_out,
-                   float *ssq_out) {
+gather_last_kernel(const A *xs, const float *ssp, const float *ssq, int B, int T, int H, const int32_t *lens,
+                   A *xs_out, float *ssp_out, float *ssq_out) {
   const int b = blockIdx.x;
-  const size_t row = (size_t)b * T + T - 1, M = (size_t)B * T;
+  const size_t row = (size_t)b * T + prompt_len_of(lens, b, T) - 1, M = (size_t)B * T;
   for (int i = threadIdx.x; i < H; i += 256) xs_out[(size_t)b * H + i] = xs[row * H + i];
   for (int j = threadIdx.x; j < H / 64; j += 256) {
     ssp_out[(size_t)j * B + b] = ssp[j * M + row];
@@ -77,27 +83,28 @@ gather_last_kernel(const A *xs, const float *ssp, const float *ssq, int B, int T
 }
 
 template <typename T>
-hipError_t gather_last(const Act<T> *xs, const float *ssp, const float *ssq, int B, int T_, int H, Act<T> *xs_out,
-                       float *ssp_out, float *ssq_out, hipStream_t s) {
+hipError_t gather_last(const Act<T> *xs, const float *ssp, const float *ssq, int B, int T_, int H, const int32_t *lens,
+                       Act<T> *xs_out, float *ssp_out, float *ssq_out, hipStream_t s) {
   if (H % 64 != 0 || B < 1 || T_ < 1) return hipErrorInvalidValue;
-  return launch(gather_last_kernel<Act<T>>, dim3(B), dim3(256), s, xs, ssp, ssq, B, T_, H, xs_out, ssp_out, ssq_out);
+  return launch(gather_last_kernel<Act<T>>, dim3(B), dim3(256), s, xs, ssp, ssq, B, T_, H, lens, xs_out, ssp_out,
+                ssq_out);
 }
 
-// pos[j * B + b] = first + j for j < n: the cache length of every decode step.
-__global__ void __launch_bounds__(256) fill_positions_kernel(int32_t *pos, int B, int n, int first) {
+// pos[j * B + b] = len_b + j for j < n: the cache length of every decode step.
+__global__ void __launch_bounds__(256) fill_positions_kernel(int32_t *pos, int B, int n, int T, const int32_t *lens) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < B * n) pos[i] = first + i / B;
+  if (i < B * n) pos[i] = prompt_len_of(lens, i % B, T) + i / B;
 }
 
-hipError_t fill_positions(int32_t *pos, int B, int n, int first, hipStream_t s) {
+hipError_t fill_positions(int32_t *pos, int B, int n, int T, const int32_t *lens, hipStream_t s) {
   if (B * n == 0) return hipSuccess;
-  return launch(fill_positions_kernel, dim3((B * n + 255) / 256), dim3(256), s, pos, B, n, first);
+  return launch(fill_positions_kernel, dim3((B * n + 255) / 256), dim3(256), s, pos, B, n, T, lens);
 }
 
-template hipError_t gather_last<float>(const float *, const float *, const float *, int, int, int, float *, float *,
-                                       float *, hipStream_t);
-template hipError_t gather_last<bf16>(const f16 *, const float *, const float *, int, int, int, f16 *, float *,
-                                      float *, hipStream_t);
+template hipError_t gather_last<float>(const float *, const float *, const float *, int, int, int, const int32_t *,
+                                       float *, float *, float *, hipStream_t);
+template hipError_t gather_last<bf16>(const f16 *, const float *, const float *, int, int, int, const int32_t *, f16 *,
+                                      float *, float *, hipStream_t);
 
 template hipError_t rows_ss<float>(const int32_t *, const float *, const float *, float *, float *, float *,
                                    const float *, float *, float, int, int, int, const RopeIn &, hipStream_t);

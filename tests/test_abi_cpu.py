@@ -185,7 +185,7 @@ def test_generate_rejects():
     assert need >= _ws(cfg, B.SMOL_OP_PREFILL, 4, 16)[1] and need >= _ws(cfg, B.SMOL_OP_DECODE, 4, 64)[1]
     assert L.smol_generate_workspace_size(ctypes.byref(cfg.c()), 4, 0, 8, 64, ctypes.byref(n)) == B.SMOL_ERR_INVALID_ARG
     call = lambda **k: L.smol_generate(  # noqa: E731
-        ctypes.byref(cfg.c()), ctypes.byref(m), k.get("ids", FAKE), 4, k.get("t", 16), k.get("n", 8),
+        ctypes.byref(cfg.c()), ctypes.byref(m), k.get("ids", FAKE), None, 4, k.get("t", 16), k.get("n", 8),
         k.get("temp", 0.0), 0, 1.0, k.get("u", None), k.get("out", FAKE), k.get("kc", FAKE), FAKE,
         k.get("cap", 64), FAKE, k.get("ws_bytes", need), None)
     assert call(ids=None) == B.SMOL_ERR_INVALID_ARG
@@ -196,9 +196,23 @@ def test_generate_rejects():
     assert call(temp=0.7) == B.SMOL_ERR_INVALID_ARG and "uniforms" in B.smol_last_error()
     assert call(ws_bytes=need - 256) == B.SMOL_ERR_WORKSPACE
     cfg8 = _cfg(max_pos=20)
-    assert L.smol_generate(ctypes.byref(cfg8.c()), ctypes.byref(m), FAKE, 4, 16, 8, 0.0, 0, 1.0, None, FAKE, FAKE,
-                           FAKE, 64, FAKE, need, None) == B.SMOL_ERR_INVALID_ARG
+    assert L.smol_generate(ctypes.byref(cfg8.c()), ctypes.byref(m), FAKE, None, 4, 16, 8, 0.0, 0, 1.0, None, FAKE,
+                           FAKE, FAKE, 64, FAKE, need, None) == B.SMOL_ERR_INVALID_ARG
     assert "max_pos" in B.smol_last_error()
+
+
+def test_prefill_ex_rejects():
+    cfg = _cfg()
+    m, keep = _model_struct(cfg)
+    need = _ws(cfg, B.SMOL_OP_PREFILL, 2, 16)[1]
+    call = lambda **k: B.lib().smol_model_prefill_ex(  # noqa: E731
+        ctypes.byref(cfg.c()), ctypes.byref(m), FAKE, 2, 16, k.get("pos0", 0), k.get("mask", None), FAKE,
+        k.get("kc", FAKE), k.get("vc", FAKE), k.get("cap", 64), FAKE, need, None)
+    assert call(pos0=-1) == B.SMOL_ERR_INVALID_ARG
+    assert call(pos0=8, kc=None, vc=None, cap=0) == B.SMOL_ERR_INVALID_ARG and "pos0" in B.smol_last_error()
+    assert call(pos0=50) == B.SMOL_ERR_INVALID_ARG and "cache_cap" in B.smol_last_error()  # 50 + 16 > 64
+    assert call(pos0=8190, cap=9000) == B.SMOL_ERR_INVALID_ARG and "max_pos" in B.smol_last_error()
+    assert call(kc=None) == B.SMOL_ERR_INVALID_ARG  # one cache without the other
 
 
 def test_trim_at_eos():
