@@ -57,6 +57,19 @@ class Config:
     max_pos: int = 8192
     rms_eps: float = 1e-5
     rope_theta: float = 100000.0
+    # SmolLM3 variants (nnterp SmolLM3, "NoPE blocks" and "A sliding window the 3B
+    # checkpoints leave off"): with no_rope_interval k > 0, block l applies no rotary
+    # when (l + 1) % k == 0; with sliding_window W > 0 those blocks attend only to
+    # the W most recent positions (their own included).
+    no_rope_interval: int = 0
+    sliding_window: int = 0
+
+    def rope_on(self, layer: int) -> bool:
+        k = self.no_rope_interval
+        return not (k > 0 and (layer + 1) % k == 0)
+
+    def window(self, layer: int) -> int:
+        return self.sliding_window if (self.sliding_window > 0 and not self.rope_on(layer)) else 0
 
     @property
     def head_dim(self) -> int:
@@ -177,6 +190,7 @@ def gqa_attention(
     q_pos: np.ndarray,
     k_pos: np.ndarray,
     key_mask: Optional[np.ndarray] = None,
+    window: int = 0,
 ) -> np.ndarray:
     """Causal grouped-query attention by its definition.
 
@@ -193,7 +207,8 @@ def gqa_attention(
     scale head_dim ** -0.5).
 
     key_mask: optional bool [B, S], False = key j of sequence b gets -inf added to
-    its score for every query and head. A query left with no visible key gets the
+    its score for every query and head. window W > 0: a query at position p sees
+    only keys with p - W < position <= p. A query left with no visible key gets the
     softmax of all -inf, NaN."""
     q = np.asarray(q, F64)
     k = np.asarray(k, F64)
@@ -202,6 +217,8 @@ def gqa_attention(
     nkv = k.shape[1]
     group = nq // nkv
     visible = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]  # [T, S]
+    if window > 0:
+        visible &= np.asarray(k_pos)[None, :] > np.asarray(q_pos)[:, None] - window
     out = np.empty((B, nq, T, d), F64)
     scale = 1.0 / np.sqrt(d)
     for b in range(B):
@@ -235,13 +252,14 @@ def swiglu_mlp(u: np.ndarray, w_gate, w_up, w_down) -> np.ndarray:
 
 
 def attention_sublayer(x, lw: LayerWeights, cfg: Config, positions, past_k=None, past_v=None, past_pos=None,
-                       key_mask=None):
+                       key_mask=None, layer: int = 0):
     """self_attn(input_layernorm(x)) for x [B, T, H].
 
     Returns (attn_out [B,T,H], k_rot [B,n_kv,T,d], v [B,n_kv,T,d]); the cache
     holds keys after RoPE and before any head repetition (Sualeh77 model.py,
     "4. Attention", the stored k_cache / v_cache). key_mask: optional bool
-    [B, >= last position + 1] over absolute key positions (False: masked)."""
+    [B, >= last position + 1] over absolute key positions (False: masked). layer:
+    the block's index, which decides the rotary and the window (Config)."""
     x = np.asarray(x, F64)
     B, T, H = x.shape
     d = cfg.head_dim
@@ -250,8 +268,9 @@ def attention_sublayer(x, lw: LayerWeights, cfg: Config, positions, past_k=None,
     k = (u @ np.asarray(lw.wk, F64).T).reshape(B, T, cfg.n_kv_heads, d).transpose(0, 2, 1, 3)
     v = (u @ np.asarray(lw.wv, F64).T).reshape(B, T, cfg.n_kv_heads, d).transpose(0, 2, 1, 3)
     positions = np.asarray(positions)
-    q = rope_rotate(q, positions, cfg.rope_theta)
-    k = rope_rotate(k, positions, cfg.rope_theta)
+    if cfg.rope_on(layer):  # a NoPE block keeps q and k as projected (nnterp SmolLM3)
+        q = rope_rotate(q, positions, cfg.rope_theta)
+        k = rope_rotate(k, positions, cfg.rope_theta)
     if past_k is not None:
         k_all = np.concatenate([np.asarray(past_k, F64), k], axis=2)
         v_all = np.concatenate([np.asarray(past_v, F64), v], axis=2)
@@ -259,7 +278,7 @@ def attention_sublayer(x, lw: LayerWeights, cfg: Config, positions, past_k=None,
     else:
         k_all, v_all, k_pos = k, v, positions
     km = None if key_mask is None else np.asarray(key_mask, bool)[:, np.asarray(k_pos)]
-    o = gqa_attention(q, k_all, v_all, positions, k_pos, km)  # [B, nq, T, d]
+    o = gqa_attention(q, k_all, v_all, positions, k_pos, km, cfg.window(layer))  # [B, nq, T, d]
     o = o.transpose(0, 2, 1, 3).reshape(B, T, cfg.n_heads * d)  # column h*d + e
     return o @ np.asarray(lw.wo, F64).T, k, v
 
@@ -270,7 +289,8 @@ def mlp_sublayer(h, lw: LayerWeights, cfg: Config):
     return swiglu_mlp(w, lw.w_gate, lw.w_up, lw.w_down)
 
 
-def block_forward(x, lw: LayerWeights, cfg: Config, pos0: int = 0, return_parts: bool = False, key_mask=None):
+def block_forward(x, lw: LayerWeights, cfg: Config, pos0: int = 0, return_parts: bool = False, key_mask=None,
+                  layer: int = 0):
     """Pre-norm block: h = x + attn(norm1(x)); out = h + mlp(norm2(h)).
 
     nnterp SmolLM3, "The block, in order"; tohio block.py, SLMDecoderBlock.forward;
@@ -281,7 +301,7 @@ def block_forward(x, lw: LayerWeights, cfg: Config, pos0: int = 0, return_parts:
     x = np.asarray(x, F64)
     T = x.shape[1]
     positions = np.arange(pos0, pos0 + T)
-    attn, k, v = attention_sublayer(x, lw, cfg, positions, key_mask=key_mask)
+    attn, k, v = attention_sublayer(x, lw, cfg, positions, key_mask=key_mask, layer=layer)
     h = x + attn
     mlp = mlp_sublayer(h, lw, cfg)
     out = h + mlp
@@ -323,8 +343,8 @@ def model_prefill(ids, mw: ModelWeights, cfg: Config, logit_rows: Optional[Seque
         raise ValueError("sequence longer than max_position_embeddings")
     x = embed(ids, mw.embed)
     cache = []
-    for lw in mw.layers:
-        x, parts = block_forward(x, lw, cfg, 0, return_parts=True, key_mask=key_mask)
+    for li, lw in enumerate(mw.layers):
+        x, parts = block_forward(x, lw, cfg, 0, return_parts=True, key_mask=key_mask, layer=li)
         if keep_cache:
             cache.append((parts["k"], parts["v"]))
     xf = x.reshape(B * T, cfg.hidden)
@@ -356,7 +376,7 @@ def decode_step(ids, cache_len: int, mw: ModelWeights, cfg: Config, k_cache, v_c
     for li, lw in enumerate(mw.layers):
         pk = np.asarray(k_cache[li])[:, :, :P]
         pv = np.asarray(v_cache[li])[:, :, :P]
-        attn, k, v = attention_sublayer(x, lw, cfg, positions, pk, pv, np.arange(P), key_mask=key_mask)
+        attn, k, v = attention_sublayer(x, lw, cfg, positions, pk, pv, np.arange(P), key_mask=key_mask, layer=li)
         h = x + attn
         x = h + mlp_sublayer(h, lw, cfg)
         new_k.append(k[:, :, 0])

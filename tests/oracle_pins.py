@@ -361,7 +361,7 @@ def pin_decode_equals_prefill():
         assert np.allclose(nv[li], cache_full[li][1][:, :, P], rtol=1e-12)
 
 
-def _brute_force_logits(cfg, mw, ids, mask=None):
+def _brute_force_logits(cfg, mw, ids, mask=None):  # noqa: C901
     """Scalar pure-Python evaluation of the whole forward (for tiny sizes only).
     mask[b][j] False: key j of sequence b gets weight 0 (its value still enters the
     sum times 0, as in probs @ v); a query with no unmasked key gets NaN."""
@@ -388,9 +388,13 @@ def _brute_force_logits(cfg, mw, ids, mask=None):
 
     E = mw.embed.tolist()
     logits = []
+    rope_every = getattr(cfg, "no_rope_interval", 0)
+    win = getattr(cfg, "sliding_window", 0)
     for b in range(B):
         xs = [list(E[ids[b][t]]) for t in range(T)]
-        for lw in mw.layers:
+        for li, lw in enumerate(mw.layers):
+            nope = rope_every > 0 and (li + 1) % rope_every == 0  # blocks rope_every-1, 2 rope_every-1, ...
+            w_l = win if (nope and win > 0) else 0
             W = {n: getattr(lw, n).tolist() for n in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")}
             us = [norm(x, lw.attn_norm.tolist()) for x in xs]
             qs = [lin(u, W["wq"]) for u in us]
@@ -400,15 +404,15 @@ def _brute_force_logits(cfg, mw, ids, mask=None):
                 att = [0.0] * (nq * d)
                 for h in range(nq):
                     g = h // G
-                    qh = rot(qs[t][h * d:(h + 1) * d], t)
-                    seen = [j for j in range(t + 1) if mask is None or mask[b][j]]
+                    qh = qs[t][h * d:(h + 1) * d] if nope else rot(qs[t][h * d:(h + 1) * d], t)
+                    seen = [j for j in range(t + 1) if (mask is None or mask[b][j]) and (w_l == 0 or j > t - w_l)]
                     if not seen:
                         for e in range(d):
                             att[h * d + e] = float("nan")
                         continue
                     sc = {}
                     for j in seen:
-                        kj = rot(ks[j][g * d:(g + 1) * d], j)
+                        kj = ks[j][g * d:(g + 1) * d] if nope else rot(ks[j][g * d:(g + 1) * d], j)
                         sc[j] = sum(qh[e] * kj[e] for e in range(d)) / math.sqrt(d)
                     mx = max(sc.values())
                     ex = {j: math.exp(s - mx) for j, s in sc.items()}
@@ -472,6 +476,45 @@ def pin_padding_mask():
     keep = [t for t in range(6) if t != 3]
     a, b_ = got[0, keep], got2[0, keep]
     assert np.array_equal(np.isnan(a), np.isnan(b_)) and np.array_equal(a[~np.isnan(a)], b_[~np.isnan(b_)])
+
+
+def pin_nope_blocks_and_window():
+    """SmolLM3 variants (nnterp SmolLM3, "NoPE blocks" and the sliding-window
+    section): every 4th block is NoPE, which on 36 blocks gives the page's list 3, 7,
+    ..., 35; a NoPE block's queries and keys are the bare projections, so its output
+    does not move when the whole sequence shifts position; a window at least the
+    sequence long changes nothing; a window of 1 leaves each query its own value; and
+    a scalar evaluation with a NoPE block and a window agrees. (A rotary block is
+    shift-invariant too, since its scores depend on position offsets only; what tells
+    the two apart is that its keys differ from the projections past position 0.)"""
+    cfg4 = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=36, vocab=16, max_pos=256,
+                    rms_eps=1e-5, rope_theta=5e6, no_rope_interval=4)
+    assert [l for l in range(36) if not cfg4.rope_on(l)] == [3, 7, 11, 15, 19, 23, 27, 31, 35]
+    rng = _rng(43)
+    cfg1 = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=1, vocab=16, max_pos=256,
+                    rms_eps=1e-5, rope_theta=5e6, no_rope_interval=1)
+    lw = _rand_layer(cfg1, rng, std=0.5, norm_jitter=0.3)
+    x = rng.normal(0, 1, (2, 7, 12))
+    a = O.block_forward(x, lw, cfg1, pos0=0)
+    assert np.array_equal(a, O.block_forward(x, lw, cfg1, pos0=123))
+    _, parts = O.block_forward(x, lw, cfg1, return_parts=True)
+    u = O.rms_norm(x, lw.attn_norm, cfg1.rms_eps)
+    raw_k = (u @ lw.wk.T).reshape(2, 7, 1, 4).transpose(0, 2, 1, 3)
+    assert np.array_equal(parts["k"], raw_k)
+    rope = O.Config(**{**cfg1.__dict__, "no_rope_interval": 0})  # a rotary block rotates them
+    _, parts_r = O.block_forward(x, lw, rope, return_parts=True)
+    assert np.array_equal(parts_r["k"][:, :, 0], raw_k[:, :, 0]) and not np.allclose(parts_r["k"][:, :, 1:], raw_k[:, :, 1:])
+    wide = O.Config(**{**cfg1.__dict__, "sliding_window": 7})
+    assert np.array_equal(O.block_forward(x, lw, wide), a)
+    one = O.Config(**{**cfg1.__dict__, "sliding_window": 1})
+    attn, k, v = O.attention_sublayer(x, lw, one, np.arange(7))
+    want = np.repeat(v, 3, axis=1).transpose(0, 2, 1, 3).reshape(2, 7, 12) @ lw.wo.T
+    assert _rel(attn, want) < 1e-12
+    cfg2 = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=2, vocab=16, max_pos=32,
+                    rms_eps=1e-5, rope_theta=5e6, no_rope_interval=2, sliding_window=2)
+    mw = _rand_model(cfg2, rng, std=0.5, norm_jitter=0.3)
+    ids = rng.integers(0, cfg2.vocab, size=(2, 6))
+    assert _rel(O.model_prefill(ids, mw, cfg2), _brute_force_logits(cfg2, mw, ids.tolist())) < 1e-12
 
 
 # ---------------------------------------------------------------- next-token choice
@@ -616,6 +659,7 @@ ALL_PINS = [
     pin_decode_equals_prefill,
     pin_brute_force_tiny,
     pin_padding_mask,
+    pin_nope_blocks_and_window,
     pin_greedy_ties_and_nan,
     pin_top_k_keeps_ties,
     pin_top_p_hand_values,

@@ -59,14 +59,16 @@ def _rope_sign_flipped(z, positions, theta):
     return np.concatenate([a * c + b * s, b * c - a * s], axis=-1)
 
 
-def _make_attention(mapping="div", scale="sqrt", strict=False, mask="keys"):
-    def attn(q, k, v, q_pos, k_pos, key_mask=None):
+def _make_attention(mapping="div", scale="sqrt", strict=False, mask="keys", window_off=0):
+    def attn(q, k, v, q_pos, k_pos, key_mask=None, window=0):
         q, k, v = (np.asarray(a, F64) for a in (q, k, v))
         B, nq, T, d = q.shape
         nkv = k.shape[1]
         G = nq // nkv
         qp, kp = np.asarray(q_pos), np.asarray(k_pos)
         vis = (kp[None, :] < qp[:, None]) if strict else (kp[None, :] <= qp[:, None])
+        if window > 0:
+            vis = vis & (kp[None, :] > qp[:, None] - window - window_off)
         sc = 1.0 / np.sqrt(d) if scale == "sqrt" else 1.0 / d
         out = np.empty((B, nq, T, d))
         for b in range(B):
@@ -94,10 +96,10 @@ def _silu_sigmoid(z):
     return 1.0 / (1.0 + np.exp(-np.asarray(z, F64)))
 
 
-def _block_no_mlp_residual(x, lw, cfg, pos0=0, return_parts=False, key_mask=None):
+def _block_no_mlp_residual(x, lw, cfg, pos0=0, return_parts=False, key_mask=None, layer=0):
     x = np.asarray(x, F64)
     positions = np.arange(pos0, pos0 + x.shape[1])
-    attn, k, v = O.attention_sublayer(x, lw, cfg, positions, key_mask=key_mask)
+    attn, k, v = O.attention_sublayer(x, lw, cfg, positions, key_mask=key_mask, layer=layer)
     h = x + attn
     mlp = O.mlp_sublayer(h, lw, cfg)
     out = mlp + attn  # the first residual's x is dropped
@@ -113,15 +115,16 @@ def _mlp_reads_stream_not_norm(h, lw, cfg):
 _orig_attention_sublayer = O.attention_sublayer
 
 
-def _attention_rotates_v(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None, key_mask=None):
-    out, k, v = _orig_attention_sublayer(x, lw, cfg, positions, past_k, past_v, past_pos, key_mask)
+def _attention_rotates_v(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None, key_mask=None, layer=0):
+    out, k, v = _orig_attention_sublayer(x, lw, cfg, positions, past_k, past_v, past_pos, key_mask, layer)
     vr = O.rope_rotate(v, np.asarray(positions), cfg.rope_theta)
     # recompute the output with rotated values
     B, T, H = np.asarray(x).shape
     d = cfg.head_dim
     u = O.rms_norm(x, lw.attn_norm, cfg.rms_eps)
     q = (u @ np.asarray(lw.wq, F64).T).reshape(B, T, cfg.n_heads, d).transpose(0, 2, 1, 3)
-    q = O.rope_rotate(q, np.asarray(positions), cfg.rope_theta)
+    if cfg.rope_on(layer):
+        q = O.rope_rotate(q, np.asarray(positions), cfg.rope_theta)
     if past_k is not None:
         k_all = np.concatenate([past_k, k], 2)
         v_all = np.concatenate([past_v, vr], 2)
@@ -129,15 +132,15 @@ def _attention_rotates_v(x, lw, cfg, positions, past_k=None, past_v=None, past_p
     else:
         k_all, v_all, kp = k, vr, positions
     km = None if key_mask is None else np.asarray(key_mask, bool)[:, np.asarray(kp)]
-    o = O.gqa_attention(q, k_all, v_all, positions, kp, km).transpose(0, 2, 1, 3).reshape(B, T, -1)
+    o = O.gqa_attention(q, k_all, v_all, positions, kp, km, cfg.window(layer)).transpose(0, 2, 1, 3).reshape(B, T, -1)
     return o @ np.asarray(lw.wo, F64).T, k, vr
 
 
-def _attention_wo_transposed(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None, key_mask=None):
+def _attention_wo_transposed(x, lw, cfg, positions, past_k=None, past_v=None, past_pos=None, key_mask=None, layer=0):
     import copy
     lw2 = copy.copy(lw)
     lw2.wo = np.asarray(lw.wo).T
-    return _orig_attention_sublayer(x, lw2, cfg, positions, past_k, past_v, past_pos, key_mask)
+    return _orig_attention_sublayer(x, lw2, cfg, positions, past_k, past_v, past_pos, key_mask, layer)
 
 
 def _lm_head_no_final_norm(x, final_norm, E, cfg):
@@ -156,6 +159,8 @@ MISTAKES = {
     "causal mask excludes the diagonal": ("gqa_attention", _make_attention(strict=True)),
     "padding mask ignored": ("gqa_attention", _make_attention(mask="ignored")),
     "padding mask applied to queries": ("gqa_attention", _make_attention(mask="queries")),
+    "sliding window one key too wide": ("gqa_attention", _make_attention(window_off=1)),
+    "NoPE on blocks 0, 4, 8, ...": ("Config.rope_on", lambda self, layer: not (self.no_rope_interval > 0 and layer % self.no_rope_interval == 0)),
     "swiglu gate and up swapped": ("swiglu_mlp", _swiglu_swapped),
     "silu is the sigmoid": ("silu", _silu_sigmoid),
     "block drops the residual x": ("block_forward", _block_no_mlp_residual),
@@ -170,7 +175,10 @@ MISTAKES = {
 @pytest.mark.parametrize("name", sorted(MISTAKES))
 def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, bad = MISTAKES[name]
-    monkeypatch.setattr(O, attr, bad)
+    if attr.startswith("Config."):
+        monkeypatch.setattr(O.Config, attr.split(".", 1)[1], bad)
+    else:
+        monkeypatch.setattr(O, attr, bad)
     failed = []
     for pin in P.ALL_PINS:
         try:
