@@ -72,6 +72,12 @@ typedef struct {
   int32_t hidden, n_heads, n_kv_heads, head_dim, intermediate, n_layers, vocab, max_pos;
   float rms_eps, rope_theta;
   int32_t dtype; /* smol_dtype */
+  /* SmolLM3 variants (nnterp "SmolLM3", NoPE blocks and sliding window): with
+   * no_rope_interval k > 0, block l (0-based) applies no rotary to q and k when
+   * (l + 1) % k == 0 (k = 4: blocks 3, 7, 11, ...); with sliding_window W > 0 those
+   * blocks attend only to keys at positions p - W < pos <= p. 0 and 0: every block
+   * rotary with full causal attention (SmolLM2). */
+  int32_t no_rope_interval, sliding_window;
 } smol_config;
 
 /* One block's weights (host struct of device pointers), element type config.dtype. */

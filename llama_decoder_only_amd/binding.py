@@ -33,7 +33,8 @@ EXPORTED = ["smol_workspace_size", "smol_block_forward", "smol_model_prefill", "
 class smol_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("hidden", "n_heads", "n_kv_heads", "head_dim", "intermediate",
                                               "n_layers", "vocab", "max_pos")] + [
-        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32)]
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("no_rope_interval", ctypes.c_int32), ("sliding_window", ctypes.c_int32)]
 
 
 LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
@@ -111,11 +112,13 @@ class Config:
     rms_eps: float
     rope_theta: float
     dtype: str  # "f32" | "bf16"
+    no_rope_interval: int = 0  # SmolLM3 NoPE blocks: (l + 1) % k == 0 has no rotary
+    sliding_window: int = 0    # window of those blocks (0: none)
 
     @classmethod
     def from_shape(cls, s) -> "Config":
         """From a synthetic.Shape (or anything with the same attribute names)."""
-        return cls(**{k: getattr(s, k) for k in cls.__dataclass_fields__})
+        return cls(**{k: getattr(s, k) for k in cls.__dataclass_fields__ if hasattr(s, k)})
 
     def c(self) -> smol_config:
         d = asdict(self)

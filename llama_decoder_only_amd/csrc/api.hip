@@ -41,6 +41,7 @@ smol_status fail(smol_status s, const char *fmt, ...) {
 
 struct Dims {
   int H, nq, nkv, d, I, L, V, max_pos, G;
+  int nope_every, window;  // SmolLM3 variants (smol_config)
   float eps, theta;
   bool bf16;
   size_t esz;
@@ -64,6 +65,10 @@ smol_status check_config(const smol_config *c, Dims *o) {
   if (c->hidden % 64 || c->intermediate % 64 || c->vocab % 64)
     return fail(SMOL_ERR_UNSUPPORTED, "hidden, intermediate and vocab must be multiples of 64");
   if (c->hidden > 4096) return fail(SMOL_ERR_UNSUPPORTED, "hidden %d (supported: up to 4096)", c->hidden);
+  if (c->no_rope_interval < 0 || c->sliding_window < 0)
+    return fail(SMOL_ERR_INVALID_ARG, "no_rope_interval and sliding_window must be >= 0");
+  o->nope_every = c->no_rope_interval;
+  o->window = c->sliding_window;
   o->H = c->hidden;
   o->nq = c->n_heads;
   o->nkv = c->n_kv_heads;
@@ -181,6 +186,7 @@ struct LayerCtx {
   int B, T, pos0;
   void *kc, *vc;
   int cap, kv_off, q_key_off;
+  int layer;             // block index: decides the rotary and the window
   const int *cache_len;  // decode only
   const uint8_t *key_mask;  // [B, mask_ld] over key indices, or nullptr
   int mask_ld;
@@ -205,20 +211,24 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, 
   float *ss_p = (float *)(c.ws + c.lay.ss_p), *ss_q = (float *)(c.ws + c.lay.ss_q);
   float *gpart = (float *)(c.ws + c.lay.gpart);
 
+  // SmolLM3 variants: no rotary on every nope_every-th block, the window on those
+  const bool rope_on = !(D.nope_every > 0 && (c.layer + 1) % D.nope_every == 0);
+  const int window = (!rope_on && D.window > 0) ? D.window : 0;
   smol::QkvOut qo{M, D.H, D.nq * D.d, D.nkv * D.d, D.d, q, c.kc, c.vc,
                   decode ? 1 : c.T, c.cap, D.nkv, c.pos0, c.kv_off, D.max_pos, c.cache_len,
-                  (const float2 *)(c.ws + c.lay.rope)};
+                  (const float2 *)(c.ws + c.lay.rope), rope_on ? 1 : 0};
   SMOL_LAUNCH(SMOL_K_QKV_ROPE, smol::gemm_qkv_rope<T>(xs, smol::NormIn{ss_p, ss_q, D.eps}, (const T *)w->wq,
                                                       (const T *)w->wk, (const T *)w->wv, qo, gpart, s));
   if (decode) {
     int chunk;
     const int splits = smol::decode_splits(std::min(c.cap, D.max_pos), &chunk);
     smol::DecodeAttnArgs da{q, c.kc, c.vc, o, c.cache_len, c.B, D.nq, D.nkv, D.d, c.cap, D.max_pos, splits, chunk,
-                            (float *)(c.ws + c.lay.part), c.key_mask, c.mask_ld};
+                            (float *)(c.ws + c.lay.part), c.key_mask, c.mask_ld, window};
     hipError_t e = smol::attention_decode<T>(da, s);
     if (e != hipSuccess) return fail(SMOL_ERR_HIP, "attention_decode: %s", hipGetErrorString(e));
   } else {
-    smol::AttnArgs aa{q, c.kc, c.vc, o, c.B, c.T, D.nq, D.nkv, D.d, c.cap, c.q_key_off, c.key_mask, c.mask_ld};
+    smol::AttnArgs aa{q, c.kc, c.vc, o, c.B, c.T, D.nq, D.nkv, D.d, c.cap, c.q_key_off, c.key_mask, c.mask_ld,
+                      window};
     SMOL_LAUNCH(SMOL_K_ATTENTION, smol::attention_prefill<T>(aa, s));
   }
   // x += o W_o^T; leaves xs for mlp_norm, the new sums in ss_q (ss_p: the old ones)
@@ -324,6 +334,7 @@ smol_status prefill_impl(const Dims &D, const smol_model_weights *w, const int32
       c.kc = ws + lay.k; c.vc = ws + lay.v; c.cap = T_; c.kv_off = 0; c.q_key_off = 0;
     }
     const void *next = l + 1 < D.L ? w->layers[l + 1].attn_norm : w->final_norm;
+    c.layer = l;
     smol_status st = run_layer<T>(c, &w->layers[l], x, next);
     if (st != SMOL_OK) return st;
   }
@@ -355,6 +366,7 @@ smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_
     c.kc = (char *)kc + l * layer_elems * D.esz;
     c.vc = (char *)vc + l * layer_elems * D.esz;
     const void *next = l + 1 < D.L ? w->layers[l + 1].attn_norm : w->final_norm;
+    c.layer = l;
     smol_status st = run_layer<T>(c, &w->layers[l], x, next);
     if (st != SMOL_OK) return st;
   }

@@ -48,9 +48,11 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const char *p) {
 }
 
 
-// MASKED: the launch has a key mask. A separate instantiation: the mask's byte
-// loads inside the ring loop make the compiler drain every outstanding load (it
-// cannot see the ring's direct-to-LDS copies), which the unmasked kernel must not pay.
+// MASKED: the launch has a key mask or a sliding window (a query at key index i then
+// sees only indices > i - window; rounds wholly before the block's first window are
+// skipped). A separate instantiation: the mask's byte loads inside the ring loop make
+// the compiler drain every outstanding load (it cannot see the ring's direct-to-LDS
+// copies), which the unmasked kernel must not pay.
 template <typename W, int D, int G, int QW, int KS, int S, bool MASKED>
 __global__ void __launch_bounds__(64 * G * QW * KS)
 attn_prefill_kernel(const AttnArgs a) {
@@ -170,12 +172,16 @@ attn_prefill_kernel(const AttnArgs a) {
   for (int i = 0; i < DT; ++i) o[i] = (f32x16){};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // first round that holds a key some query of the block may see (0 without a window)
+  const int rf = (MASKED && a.window > 0) ? max(0, qb * BQ + a.q_key_off - a.window + 1) / (KS * BKV) : 0;
+  const int nr = nrounds - rf;  // rounds walked; walk step `step` is round rf + step, in slot step % S
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
-    if (st < nrounds) issue(st, st);
+    if (st < nr) issue(rf + st, st);
 
-  for (int r = 0; r < nrounds; ++r) {
-    if (r + S - 2 < nrounds)
+  for (int step = 0; step < nr; ++step) {
+    const int r = rf + step;
+    if (step + S - 2 < nr)
       wait_vmcnt<(S - 2) * IPW>();
     else
       wait_vmcnt<0>();
@@ -185,14 +191,14 @@ attn_prefill_kernel(const AttnArgs a) {
       // place (same width, same swizzled layout), instead of in every wave that reads
       // them. The barrier waits for the LDS writes only: the DMA of a later round may
       // still be in flight.
-      Chunk16 *t = reinterpret_cast<Chunk16 *>(smem + (r % S) * STAGE_BYTES);
+      Chunk16 *t = reinterpret_cast<Chunk16 *>(smem + (step % S) * STAGE_BYTES);
       for (int i = tid; i < STAGE_BYTES / 16; i += NW * 64) t[i] = to_operand<W>(t[i]);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
     }
-    if (r + S - 1 < nrounds) issue(r + S - 1, (r + S - 1) % S);
+    if (step + S - 1 < nr) issue(r + S - 1, (step + S - 1) % S);
     const int kt = r * KS + ks;  // this wave's tile
-    const char *ks_ptr = smem + (r % S) * STAGE_BYTES + ks * 2 * TILE_BYTES;
+    const char *ks_ptr = smem + (step % S) * STAGE_BYTES + ks * 2 * TILE_BYTES;
     const char *vs = ks_ptr + TILE_BYTES;
     const int k0 = kt * BKV;
     if (wave_live && kt < ntiles && k0 <= wave_kmax) {
@@ -223,15 +229,20 @@ attn_prefill_kernel(const AttnArgs a) {
       // split may meet tiles where some of its queries see no key yet: their max stays
       // -inf and their probabilities 0.
       const bool need_mask = k0 + BKV - 1 > q0 + a.q_key_off;
-      if constexpr (MASKED) {  // bit j of kb: key k0 + j may be attended (lane j loads its byte)
-        const int kj = k0 + lane;
-        const bool kok = kj < nkeys && a.key_mask[(size_t)b * a.mask_ld + kj] != 0;
-        const unsigned long long kb = __ballot(kok);
+      if constexpr (MASKED) {
+        unsigned long long kb = ~0ull;  // bit j: key k0 + j may be attended (lane j loads its byte)
+        if (a.key_mask) {
+          const int kj = k0 + lane;
+          kb = __ballot(kj < nkeys && a.key_mask[(size_t)b * a.mask_ld + kj] != 0);
+        }
+        const int kmin = a.window > 0 ? my_kmax - a.window + 1 : 0;  // this query's window
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            if (!((kb >> (32 * i + acc_row(rr, lane))) & 1ull)) s[i][rr] = -INFINITY;
+          for (int e = 0; e < 16; ++e) {
+            const int j = 32 * i + acc_row(e, lane);
+            if (!((kb >> j) & 1ull) || k0 + j < kmin) s[i][e] = -INFINITY;
+          }
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -352,7 +363,7 @@ static hipError_t launch_attn_cfg(const AttnArgs &a, hipStream_t s) {
   constexpr int S = (3 * ROUND <= 98304) ? 3 : 2;
   const int nqb = (a.T + 32 * QW - 1) / (32 * QW);
   const dim3 grid(nqb * a.B * a.n_kv), block(64 * G * QW * KS);
-  if (a.key_mask) return launch(attn_prefill_kernel<T, D, G, QW, KS, S, true>, grid, block, s, a);
+  if (a.key_mask || a.window > 0) return launch(attn_prefill_kernel<T, D, G, QW, KS, S, true>, grid, block, s, a);
   return launch(attn_prefill_kernel<T, D, G, QW, KS, S, false>, grid, block, s, a);
 }
 

@@ -4,8 +4,8 @@
 // The new token of sequence b sits at position P = cache_len[b] and sees keys
 // 0 .. P (Sualeh77 model.py, "4. Attention": with a cache the single new token
 // attends to all past keys and itself), minus those an optional key mask removes
-// (the pages' additive padding mask). This step is bound by HBM: every cached key
-// and value is read once.
+// (the pages' additive padding mask) and, on a windowed block, those at or before
+// P - window. This step is bound by HBM: every cached key and value is read once.
 //
 // Kernel 1, grid (splits, n_kv, B), 256 threads: a workgroup takes `chunk`
 // consecutive keys of kv head g and serves all G query heads of the group.
@@ -52,7 +52,8 @@ decode_attn_kernel(const DecodeAttnArgs a) {
 
   const int k_begin = sp * CHUNK;
   const int k_end = decode_pos_ok(P, a.cap, a.max_pos) ? min(k_begin + CHUNK, P + 1) : 0;
-  const int n = k_end - k_begin;
+  const int k_lo = a.window > 0 ? P - a.window + 1 : 0;  // first key inside the window
+  const int n = k_end <= k_lo ? 0 : k_end - k_begin;     // a chunk wholly before it is empty
   if (n <= 0) {  // empty split: neutral partial
     if (tid < G) {
       part[tid * head_stride + 0] = -INFINITY;
@@ -83,7 +84,7 @@ decode_attn_kernel(const DecodeAttnArgs a) {
     for (int it = 0; it < PASSES; ++it) {
       const int j = min(kk + it * KPP, n - 1);  // rows past the chunk re-read its last key
       kc[it] = ld16(kb + (size_t)j * D);
-      keep[it] = !a.key_mask || a.key_mask[(size_t)b * a.mask_ld + k_begin + j] != 0;
+      keep[it] = (!a.key_mask || a.key_mask[(size_t)b * a.mask_ld + k_begin + j] != 0) && k_begin + j >= k_lo;
     }
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {

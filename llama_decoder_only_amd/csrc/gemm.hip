@@ -32,7 +32,8 @@
 //   EPI_SWIGLU    Y = silu(gate) * up              gate/up projection: tile columns
 //                                                  [0, BN/2) read gate rows and
 //                                                  [BN/2, BN) the matching up rows
-//   EPI_QKV_ROPE  q, k rotated at their position, q stored [M, n_heads*d]; k, v
+//   EPI_QKV_ROPE  q, k rotated at their position (not on a NoPE block), q stored
+//                 [M, n_heads*d]; k, v
 //                 stored into the [B, n_kv, cap, d] cache at their index.
 // Projection math: abi96062 components.py (GroupedQueryAttention, SwiGLU_FFN);
 // RoPE pairs (i, i + d/2): Sualeh77 model.py, "3. RoPE".
@@ -55,6 +56,7 @@ struct GemmParams {
   int seq, cap, n_kv, pos0, kv_off, max_pos;
   const int *cache_len;
   const float2 *rope;  // [M, head_dim / 2] (cos, sin) of each row's RoPE angles
+  int rope_on;         // 0: a NoPE block, q and k are stored as projected
   // Row sums of squares of the residual stream, H/64 partials per row:
   // ss[j * M + row] over columns [64 j, 64 j + 64).
   //   A GEMM on xs (EPI != EPI_RESIDUAL, ss_new != nullptr): output row scaled by
@@ -338,7 +340,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams &p, const float *
         lo[e] = t[e0 + e] * f;
         up[e] = t[HALF + e0 + e] * f;
       }
-      if (kind != 2) {
+      if (kind != 2 && p.rope_on) {
         f32x4 cs0, cs1;  // (cos, sin) of frequencies e0 .. e0 + 3
         if (cs_pre) {
           cs0 = cs_pre[0];
@@ -852,6 +854,7 @@ hipError_t gemm_qkv_rope(const Act<T> *A, const NormIn &nrm, const T *Wq, const 
   p.seq = o.seq; p.cap = o.cap; p.n_kv = o.n_kv; p.pos0 = o.pos0; p.kv_off = o.kv_off; p.max_pos = o.max_pos;
   p.cache_len = o.cache_len;
   p.rope = o.rope;
+  p.rope_on = o.rope_on;
   if (!o.rope || o.head_dim % 8 != 0) return hipErrorInvalidValue;
   return launch_gemm<T, EPI_QKV_ROPE>(p, s);
 }

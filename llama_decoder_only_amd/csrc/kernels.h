@@ -21,6 +21,7 @@ struct QkvOut {
   int seq, cap, n_kv, pos0, kv_off, max_pos;
   const int *cache_len;
   const float2 *rope;     // [M, head_dim / 2] (cos, sin) of each row's angles (RopeIn)
+  int rope_on;            // 0: a NoPE block (q and k stay as projected)
 };
 
 // The deferred RMSNorm u = w * x * r, r = 1 / sqrt(mean(x^2) + eps) per row of the
@@ -95,6 +96,7 @@ struct AttnArgs {
   int B, T, n_heads, n_kv, head_dim, cap, q_key_off;
   const uint8_t *key_mask;
   int mask_ld;
+  int window;  // > 0: a query at key index i sees only indices > i - window
 };
 template <typename T>
 hipError_t attention_prefill(const AttnArgs &a, hipStream_t s);
@@ -110,6 +112,7 @@ struct DecodeAttnArgs {
   float *part;    // [B, n_heads, splits, head_dim + 2]
   const uint8_t *key_mask;
   int mask_ld;
+  int window;     // > 0: the new token sees only key indices > cache_len - window
 };
 template <typename T>
 hipError_t attention_decode(const DecodeAttnArgs &a, hipStream_t s);

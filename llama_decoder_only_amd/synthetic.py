@@ -45,6 +45,8 @@ class Shape:
     workload_id: int
     cache_len: int = 0  # decode: positions already in the cache
     norm_jitter: float = 0.0  # >0: RMSNorm weights 1 + N(0, jitter^2) instead of 1
+    no_rope_interval: int = 0  # SmolLM3 variants: NoPE on blocks (l + 1) % k == 0
+    sliding_window: int = 0    # and a window on those blocks
 
 
 SMOLLM2 = dict(hidden=576, n_heads=9, n_kv_heads=3, head_dim=64, intermediate=1536, n_layers=30,

@@ -29,7 +29,7 @@ def rel(g, o) -> float:
 def ocfg(s: S.Shape) -> O.Config:
     return O.Config(hidden=s.hidden, n_heads=s.n_heads, n_kv_heads=s.n_kv_heads, intermediate=s.intermediate,
                     n_layers=s.n_layers, vocab=s.vocab, max_pos=s.max_pos, rms_eps=s.rms_eps,
-                    rope_theta=s.rope_theta)
+                    rope_theta=s.rope_theta, no_rope_interval=s.no_rope_interval, sliding_window=s.sliding_window)
 
 
 def olayer(l: S.Layer) -> O.LayerWeights:
