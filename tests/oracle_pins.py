@@ -640,6 +640,136 @@ def pin_choice_brute_force():
         assert c.token == _brute_choice(l.tolist(), t, k, p, u), (trial, l, t, k, p, u)
 
 
+# ---------------------------------------------------------------- block backward
+# (oracle/backward.py: the chain rule through the block of oracle/smol.py)
+
+import oracle.backward as BW  # noqa: E402
+
+GRAD_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")
+
+
+def _block_loss(x, lw, cfg, dy, pos0, layer, mask):
+    return float(np.sum(dy * O.block_forward(x, lw, cfg, pos0=pos0, key_mask=mask, layer=layer)))
+
+
+def _finite_difference_check(cfg, lw, x, dy, pos0=0, layer=0, mask=None, seed=0, n_elem=10):
+    """Central differences of L = sum(dy * block_forward(...)) in float64: for every
+    gradient, n_elem single entries and one random direction over the whole tensor.
+    With step 1e-5 the truncation and rounding errors are ~1e-9 relative."""
+    g = BW.block_backward(x, lw, cfg, dy, pos0=pos0, layer=layer, key_mask=mask)
+    rng = _rng(seed)
+    h = 1e-5
+    tensors = {"x": x, **{n: getattr(lw, n) for n in GRAD_NAMES}}
+    for name, base in tensors.items():
+        assert g[name].shape == np.shape(base), (name, g[name].shape, np.shape(base))
+
+        def loss_at(delta):
+            if name == "x":
+                return _block_loss(x + delta, lw, cfg, dy, pos0, layer, mask)
+            lw2 = O.LayerWeights(**{**lw.__dict__, name: getattr(lw, name) + delta})
+            return _block_loss(x, lw2, cfg, dy, pos0, layer, mask)
+
+        scale = max(np.max(np.abs(g[name])), 1e-12)
+        flat_idx = rng.choice(np.size(base), size=min(n_elem, np.size(base)), replace=False)
+        for fi in flat_idx:
+            e = np.zeros(np.shape(base))
+            e.flat[fi] = h
+            fd = (loss_at(e) - loss_at(-e)) / (2 * h)
+            assert abs(fd - g[name].flat[fi]) <= 1e-6 * scale, (name, int(fi), fd, g[name].flat[fi])
+        r = rng.standard_normal(np.shape(base))
+        fd = (loss_at(h * r) - loss_at(-h * r)) / (2 * h)
+        an = float(np.sum(g[name] * r))
+        assert abs(fd - an) <= 1e-6 * max(abs(fd), scale), (name, "direction", fd, an)
+
+
+def pin_backward_finite_differences():
+    """The block's gradients (input and all nine weights) against central finite
+    differences of the forward oracle: rotary block at positions 3.., grouped heads
+    (6 query heads over 2 kv heads), unit-scale activations."""
+    cfg = _tiny_cfg()
+    rng = _rng(51)
+    lw = _rand_layer(cfg, rng, std=0.3, norm_jitter=0.3)
+    x = rng.standard_normal((2, 5, cfg.hidden))
+    dy = rng.standard_normal((2, 5, cfg.hidden))
+    _finite_difference_check(cfg, lw, x, dy, pos0=3, seed=1)
+
+
+def pin_backward_variants_finite_differences():
+    """The same check on a NoPE block with a sliding window of 2 and a padding mask
+    (nnterp SmolLM3 variants; Sualeh77 model.py, "4. Attention", attention_mask):
+    masked and out-of-window keys receive no gradient through the scores; one kv
+    head shared by 3 query heads."""
+    cfg = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=2, vocab=16, max_pos=32,
+                   rms_eps=1e-5, rope_theta=5e6, no_rope_interval=2, sliding_window=2)
+    rng = _rng(52)
+    lw = _rand_layer(cfg, rng, std=0.5, norm_jitter=0.3)
+    x = rng.standard_normal((2, 6, cfg.hidden))
+    dy = rng.standard_normal((2, 6, cfg.hidden))
+    mask = np.array([[True, True, True, False, True, True, False, True],
+                     [True, False, True, True, False, True, True, True]])  # no two masked keys in a row
+    assert not cfg.rope_on(1) and cfg.window(1) == 2
+    _finite_difference_check(cfg, lw, x, dy, pos0=2, layer=1, mask=mask, seed=2)
+    _finite_difference_check(cfg, lw, x, dy, pos0=0, layer=0, mask=mask, seed=3)  # rotary block, no window
+
+
+def pin_backward_vs_transformers_autograd():
+    """The gradients equal torch autograd through transformers' Llama decoder layer
+    (float64 weights; its RoPE angles are built in float32, hence ~1e-6 relative) at
+    a SmolLM2-like head layout (9 query heads over 3 kv heads of 8)."""
+    import torch
+
+    cfg = O.Config(hidden=72, n_heads=9, n_kv_heads=3, intermediate=64, n_layers=1, vocab=32, max_pos=64,
+                   rms_eps=1e-5, rope_theta=1e5)
+    rng = _rng(53)
+    lw = _rand_layer(cfg, rng, std=0.15, norm_jitter=0.2)
+    mw = O.ModelWeights(embed=rng.standard_normal((cfg.vocab, cfg.hidden)), layers=[lw],
+                        final_norm=np.ones(cfg.hidden))
+    m = _hf_model(cfg, mw)
+    T, pos0 = 11, 4
+    x = rng.standard_normal((2, T, cfg.hidden))
+    dy = rng.standard_normal((2, T, cfg.hidden))
+    xt = torch.from_numpy(x).requires_grad_(True)
+    pos = torch.arange(pos0, pos0 + T)[None]
+    cos_sin = m.model.rotary_emb(xt, pos)
+    mask = torch.full((T, T), -torch.inf, dtype=torch.float64).triu(1)[None, None]
+    L = m.model.layers[0]
+    L.zero_grad()
+    out = L(xt, attention_mask=mask, position_ids=pos, position_embeddings=cos_sin)
+    out = out[0] if isinstance(out, tuple) else out
+    (out * torch.from_numpy(dy)).sum().backward()
+    g = BW.block_backward(x, lw, cfg, dy, pos0=pos0)
+    hf = {"x": xt.grad, "attn_norm": L.input_layernorm.weight.grad, "wq": L.self_attn.q_proj.weight.grad,
+          "wk": L.self_attn.k_proj.weight.grad, "wv": L.self_attn.v_proj.weight.grad,
+          "wo": L.self_attn.o_proj.weight.grad, "mlp_norm": L.post_attention_layernorm.weight.grad,
+          "w_gate": L.mlp.gate_proj.weight.grad, "w_up": L.mlp.up_proj.weight.grad,
+          "w_down": L.mlp.down_proj.weight.grad}
+    for name, want in hf.items():
+        assert _rel(g[name], want.detach().numpy()) < 1e-5, (name, _rel(g[name], want.detach().numpy()))
+
+
+def pin_backward_special_cases():
+    """Closed forms: with w_down = 0 and wo = 0 the block is the identity, so dx = dy
+    and only w_down and wo get gradients (the sublayers' other weights sit behind a
+    zero map); the w_down gradient is then dy^T silu(gate) * up of the normed input;
+    with dy = 0 every gradient is 0."""
+    cfg = _tiny_cfg()
+    rng = _rng(54)
+    lw = _rand_layer(cfg, rng, std=0.3, norm_jitter=0.3)
+    lw0 = O.LayerWeights(**{**lw.__dict__, "w_down": np.zeros_like(lw.w_down), "wo": np.zeros_like(lw.wo)})
+    x = rng.standard_normal((2, 4, cfg.hidden))
+    dy = rng.standard_normal((2, 4, cfg.hidden))
+    g = BW.block_backward(x, lw0, cfg, dy)
+    assert np.array_equal(g["x"], dy)
+    for n in ("attn_norm", "wq", "wk", "wv", "mlp_norm", "w_gate", "w_up"):
+        assert not np.any(g[n]), n
+    w = O.rms_norm(x, lw.mlp_norm, cfg.rms_eps).reshape(-1, cfg.hidden)
+    y = O.silu(w @ lw.w_gate.T) * (w @ lw.w_up.T)
+    assert _rel(g["w_down"], dy.reshape(-1, cfg.hidden).T @ y) < 1e-12
+    assert np.any(g["wo"])
+    z = BW.block_backward(x, lw, cfg, np.zeros_like(dy))
+    assert all(not np.any(v) for v in z.values())
+
+
 ALL_PINS = [
     pin_rmsnorm_closed_forms,
     pin_rmsnorm_vs_torch,
@@ -667,8 +797,14 @@ ALL_PINS = [
     pin_inverse_cdf_stratified,
     pin_inverse_cdf_steps,
     pin_choice_brute_force,
+    pin_backward_finite_differences,
+    pin_backward_variants_finite_differences,
+    pin_backward_vs_transformers_autograd,
+    pin_backward_special_cases,
 ]
 
 SAMPLER_PINS = [p for p in ALL_PINS if p.__name__ in (
     "pin_greedy_ties_and_nan", "pin_top_k_keeps_ties", "pin_top_p_hand_values", "pin_top_p_after_top_k",
     "pin_inverse_cdf_stratified", "pin_inverse_cdf_steps", "pin_choice_brute_force")]
+
+BACKWARD_PINS = [p for p in ALL_PINS if p.__name__.startswith("pin_backward")]

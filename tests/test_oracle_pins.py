@@ -287,3 +287,57 @@ def test_sampler_pins_catch_planted_mistake(name, monkeypatch):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             failed.append(pin.__name__)
     assert failed, f"no pin caught: {name}"
+
+
+# ---------------------------------------------------------------- planted mistakes in the backward
+import oracle.backward as BW  # noqa: E402
+
+
+def _rms_backward_no_mean(du, n, r, w):
+    return r * (du * w), np.sum((du * n).reshape(-1, n.shape[-1]), axis=0)
+
+
+def _rms_backward_no_r(du, n, r, w):
+    dn = du * w
+    return dn - n * np.mean(dn * n, axis=-1, keepdims=True), np.sum((du * n).reshape(-1, n.shape[-1]), axis=0)
+
+
+def _rotate_forward_only(z, positions, theta, sign):
+    return O.rope_rotate(z, positions, theta)
+
+
+def _make_attention_backward(row_sum=True, dk_scale=True, dv_transposed=False):
+    def attention_backward(P, do, q, k, v, scale):
+        dv = (P @ do) if dv_transposed else (P.T @ do)
+        dp = do @ v.T
+        ds = P * (dp - np.sum(dp * P, axis=-1, keepdims=True)) if row_sum else P * dp
+        return (ds @ k) * scale, (ds.T @ q) * (scale if dk_scale else 1.0), dv
+    return attention_backward
+
+
+def _silu_grad_sigmoid(g):
+    return 1.0 / (1.0 + np.exp(-g))
+
+
+BW_MISTAKES = {
+    "rmsnorm backward drops the mean term": ("_rms_backward", _rms_backward_no_mean),
+    "rmsnorm backward drops the 1/rms factor": ("_rms_backward", _rms_backward_no_r),
+    "rotary carried back by +angle": ("_rotate", _rotate_forward_only),
+    "softmax backward without the row sum": ("_attention_backward", _make_attention_backward(row_sum=False)),
+    "dk without the 1/sqrt(d) scale": ("_attention_backward", _make_attention_backward(dk_scale=False)),
+    "dv from P, not its transpose": ("_attention_backward", _make_attention_backward(dv_transposed=True)),
+    "silu derivative taken as the sigmoid": ("_silu_grad", _silu_grad_sigmoid),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BW_MISTAKES))
+def test_backward_pins_catch_planted_mistake(name, monkeypatch):
+    attr, bad = BW_MISTAKES[name]
+    monkeypatch.setattr(BW, attr, bad)
+    failed = []
+    for pin in P.BACKWARD_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught: {name}"
