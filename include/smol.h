@@ -212,6 +212,39 @@ smol_status smol_decode_step_ex(const smol_config *cfg, const smol_model_weights
                                 int cache_cap, void *logits, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* Gradient buffers of one block (host struct of device pointers, float32, shaped
+ * like the weights of smol_layer_weights). */
+typedef struct {
+  float *attn_norm, *wq, *wk, *wv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} smol_layer_grads;
+
+/* Backward of one decoder block (the block of smol_block_forward, trained in the
+ * pages: Sualeh77 model.py trains it on TinyShakespeare, abi96062 model.py sets it
+ * up for training; the chain rule through nnterp "SmolLM3", "The block, in order",
+ * and abi96062 components.py, RMSNorm / GroupedQueryAttention / SwiGLU_FFN).
+ * For L = sum(dy * block(x)):
+ *   x [batch, seq, H] float32: the block's input, tokens at positions pos0 .. pos0 +
+ *     seq - 1 (RoPE angles; the queries attend to the seq tokens of the call only, as
+ *     smol_block_forward without a cache);
+ *   layer: the block's index in its model (decides the SmolLM3 NoPE rotary and the
+ *     sliding window; 0 for a SmolLM2 block);
+ *   key_mask: NULL or uint8 [batch, seq] by token index (0: the key is hidden from
+ *     every query of its sequence; a query must keep at least one key);
+ *   dy [batch, seq, H] float32: dL/d(block output);
+ *   dx [batch, seq, H] float32 (written): dL/dx; may not alias x or dy;
+ *   grads: the nine weight gradients, written (accumulate == 0) or added to what the
+ *     buffers hold (accumulate == 1: gradient accumulation over micro-batches).
+ * The forward is recomputed inside (activations are not taken from a forward call).
+ * Supports config.dtype SMOL_F32 only (float32 weights; every contraction is a
+ * float32 MFMA); SMOL_BF16 returns SMOL_ERR_UNSUPPORTED. Requires pos0 >= 0, pos0 +
+ * seq <= max_pos, 0 <= layer < n_layers. ws: smol_block_backward_workspace_size()
+ * bytes, 256-byte aligned. Deterministic: no atomics, every sum in a fixed order. */
+smol_status smol_block_backward_workspace_size(const smol_config *cfg, int batch, int seq, size_t *bytes);
+smol_status smol_block_backward(const smol_config *cfg, const smol_layer_weights *w, int layer,
+                                const float *x, const float *dy, int batch, int seq, int pos0,
+                                const uint8_t *key_mask, float *dx, const smol_layer_grads *grads,
+                                int accumulate, void *ws, size_t ws_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *smol_status_string(smol_status s);
 
@@ -231,7 +264,10 @@ const char *smol_last_error(void);
 typedef enum {
   SMOL_K_EMBED = 0, SMOL_K_RMSNORM = 1, SMOL_K_QKV_ROPE = 2, SMOL_K_ATTENTION = 3,
   SMOL_K_O_PROJ = 4, SMOL_K_GATE_UP = 5, SMOL_K_DOWN = 6, SMOL_K_LM_HEAD = 7,
-  SMOL_K_DECODE_ATTENTION = 8, SMOL_K_DECODE_COMBINE = 9, SMOL_K_SAMPLE = 10, SMOL_K_COUNT = 11
+  SMOL_K_DECODE_ATTENTION = 8, SMOL_K_DECODE_COMBINE = 9, SMOL_K_SAMPLE = 10,
+  /* smol_block_backward: its GEMMs, attention forward / dQ / dK-dV, row kernels */
+  SMOL_K_BW_GEMM = 11, SMOL_K_BW_ATTN_FWD = 12, SMOL_K_BW_ATTN_DQ = 13, SMOL_K_BW_ATTN_DKDV = 14,
+  SMOL_K_BW_ROWS = 15, SMOL_K_COUNT = 16
 } smol_kernel;
 smol_status smol_timing_begin(int kernel, int max_launches);
 smol_status smol_timing_end(float *total_ms, int *launches);

@@ -23,10 +23,12 @@ SMOL_OK, SMOL_ERR_INVALID_ARG, SMOL_ERR_UNSUPPORTED, SMOL_ERR_WORKSPACE, SMOL_ER
 SMOL_F32, SMOL_BF16 = 0, 1
 SMOL_OP_BLOCK, SMOL_OP_PREFILL, SMOL_OP_DECODE = 0, 1, 2
 KERNELS = ["embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head",
-           "decode_attention", "decode_combine", "sample"]
+           "decode_attention", "decode_combine", "sample",
+           "bw_gemm", "bw_attn_fwd", "bw_attn_dq", "bw_attn_dkdv", "bw_rows"]
 EXPORTED = ["smol_workspace_size", "smol_block_forward", "smol_model_prefill", "smol_decode_step",
             "smol_model_prefill_ex", "smol_decode_step_ex",
             "smol_sample", "smol_generate_workspace_size", "smol_generate",
+            "smol_block_backward_workspace_size", "smol_block_backward",
             "smol_status_string", "smol_last_error", "smol_timing_begin", "smol_timing_end"]
 
 
@@ -41,6 +43,10 @@ LAYER_FIELDS = ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up
 
 
 class smol_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
+
+
+class smol_layer_grads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
 
 
@@ -83,6 +89,9 @@ def lib() -> ctypes.CDLL:
                                             vp, i32, vp, sz, vp]
         L.smol_decode_step_ex.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, vp, i32, vp, vp, vp, i32,
                                           vp, vp, sz, vp]
+        L.smol_block_backward_workspace_size.argtypes = [cfgp, i32, i32, ctypes.POINTER(sz)]
+        L.smol_block_backward.argtypes = [cfgp, ctypes.POINTER(smol_layer_weights), i32, vp, vp, i32, i32, i32, vp,
+                                          vp, ctypes.POINTER(smol_layer_grads), i32, vp, sz, vp]
         L.smol_status_string.argtypes = [i32]
         L.smol_status_string.restype = ctypes.c_char_p
         L.smol_last_error.argtypes = []
@@ -336,6 +345,46 @@ def smol_decode_step_ex(cfg: Config, w: ModelWeights, ids: torch.Tensor, cache_l
                                      _ptr(key_mask), _ptr(k_cache), _ptr(v_cache), cap, _ptr(logits), _ptr(ws),
                                      ws.numel(), _stream(stream)))
     return logits
+
+
+def smol_block_backward_workspace_size(cfg: Config, batch: int, seq: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().smol_block_backward_workspace_size(ctypes.byref(cfg.c()), batch, seq, ctypes.byref(n)))
+    return int(n.value)
+
+
+class LayerGrads:
+    """Float32 gradient buffers shaped like one block's weights, plus the C struct."""
+
+    def __init__(self, tensors: Sequence[torch.Tensor]):
+        self.tensors = list(tensors)
+        for t in self.tensors:
+            if t.dtype != torch.float32:
+                raise ValueError("gradients are float32")
+        self.c = smol_layer_grads(*[_ptr(t) for t in self.tensors])
+
+    @classmethod
+    def zeros_like(cls, w: LayerWeights) -> "LayerGrads":
+        return cls([torch.zeros(t.shape, dtype=torch.float32, device=t.device) for t in w.tensors])
+
+    def as_dict(self):
+        return dict(zip(LAYER_FIELDS, self.tensors))
+
+
+def smol_block_backward(cfg: Config, w: LayerWeights, x: torch.Tensor, dy: torch.Tensor, dx: torch.Tensor,
+                        grads: LayerGrads, layer: int = 0, pos0: int = 0, key_mask: Optional[torch.Tensor] = None,
+                        accumulate: bool = False, ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """x, dy, dx float32 [B, T, H] (dx written); grads: LayerGrads (written, or added to
+    with accumulate); key_mask uint8 [B, T] or None."""
+    B, T, _ = x.shape
+    if key_mask is not None and (key_mask.dtype != torch.uint8 or tuple(key_mask.shape) != (B, T)):
+        raise ValueError("key_mask must be uint8 [B, seq]")
+    if ws is None:
+        ws = torch.empty(smol_block_backward_workspace_size(cfg, B, T), dtype=torch.uint8, device=x.device)
+    _check(lib().smol_block_backward(ctypes.byref(cfg.c()), ctypes.byref(w.c), layer, _ptr(x), _ptr(dy), B, T, pos0,
+                                     _ptr(key_mask), _ptr(dx), ctypes.byref(grads.c), int(bool(accumulate)),
+                                     _ptr(ws), ws.numel(), _stream(stream)))
+    return dx
 
 
 def smol_timing_begin(kernel: str, max_launches: int):

@@ -445,6 +445,167 @@ smol_status check_model(const Dims &D, const smol_model_weights *w) {
   return SMOL_OK;
 }
 
+
+// ------------------------------------------------------------------ backward
+// smol_block_backward: the forward recomputed with its activations kept, then the
+// chain rule in reverse (backward.hip). M = B*T rows; C3 = (nq + 2 nkv) d.
+struct BwWs {
+  size_t u, r1, qkv, o, lse, h, wn, r2, gu, dgu, y, dwn, dh, dO, dsum, dqkv, part, du, npart, total;
+};
+
+BwWs bw_layout(const Dims &D, int B, int T) {
+  BwWs w{};
+  const size_t M = (size_t)B * T, H = D.H, C3 = (size_t)(D.nq + 2 * D.nkv) * D.d, QD = (size_t)D.nq * D.d;
+  size_t off = 0;
+  auto take = [&](size_t floats) { size_t at = off; off += up(floats * 4); return at; };
+  w.u = take(M * H);
+  w.r1 = take(M);
+  w.qkv = take(M * C3);
+  w.o = take(M * QD);
+  w.lse = take((size_t)B * D.nq * T);
+  w.h = take(M * H);
+  w.wn = take(M * H);
+  w.r2 = take(M);
+  w.gu = take(M * 2 * D.I);
+  w.dgu = take(M * 2 * D.I);
+  w.y = take(M * D.I);
+  w.dwn = take(M * H);
+  w.dh = take(M * H);
+  w.dO = take(M * QD);
+  w.dsum = take((size_t)B * D.nq * T);
+  w.dqkv = take(M * C3);
+  w.part = take(2 * (size_t)D.nq * M * D.d);
+  w.du = take(M * H);
+  w.npart = take((size_t)smol::bw_rms_part_rows((int)M) * H);
+  w.total = off;
+  return w;
+}
+
+smol::BwOperand operand(const float *p0, int ld, const float *p1 = nullptr, int seg0 = 1 << 30,
+                        const float *p2 = nullptr, int seg1 = 1 << 30) {
+  return smol::BwOperand{p0, p1, p2, seg0, seg1, ld};
+}
+
+smol::BwGemm gemm_args(const smol::BwOperand &a, const smol::BwOperand &b, int M, int N, int K, float *C, int ldc) {
+  smol::BwGemm g{};
+  g.a = a;
+  g.b = b;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+smol_status backward_impl(const Dims &D, const smol_layer_weights *w, int layer, const float *x, const float *dy,
+                          int B, int T, int pos0, const uint8_t *key_mask, float *dx, const smol_layer_grads *gr,
+                          int accumulate, char *ws, const BwWs &L, hipStream_t s) {
+  const int M = B * T, H = D.H, I = D.I, d = D.d, QD = D.nq * d, KD = D.nkv * d, C3 = QD + 2 * KD;
+  const bool rope_on = !(D.nope_every > 0 && (layer + 1) % D.nope_every == 0);
+  const int window = (!rope_on && D.window > 0) ? D.window : 0;
+  auto F = [&](size_t off) { return (float *)(ws + off); };
+  float *u = F(L.u), *r1 = F(L.r1), *qkv = F(L.qkv), *o = F(L.o), *h = F(L.h), *wn = F(L.wn), *r2 = F(L.r2);
+  float *gu = F(L.gu), *dgu = F(L.dgu), *y = F(L.y), *dwn = F(L.dwn), *dh = F(L.dh), *dO = F(L.dO);
+  float *dqkv = F(L.dqkv), *du = F(L.du), *npart = F(L.npart);
+  const float *Wq = (const float *)w->wq, *Wk = (const float *)w->wk, *Wv = (const float *)w->wv;
+  const float *Wo = (const float *)w->wo, *Wg = (const float *)w->w_gate, *Wu = (const float *)w->w_up;
+  const float *Wd = (const float *)w->w_down;
+  const int wgrad = accumulate ? smol::BW_ACCUM : smol::BW_STORE;
+  using smol::BW_NN;
+  using smol::BW_NT;
+  using smol::BW_TN;
+
+  // ---- forward, keeping what the backward reads
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_fwd(x, (const float *)w->attn_norm, u, r1, M, H, D.eps, s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NT, smol::BW_STORE,
+                                            gemm_args(operand(u, H), operand(Wq, H, Wk, QD, Wv, QD + KD), M, C3, H,
+                                                      qkv, C3), s));
+  smol::InvFreq inv{};
+  fill_inv_freq(D, inv.v);
+  if (rope_on)
+    SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rope(qkv, M, T, C3, D.nq + D.nkv, d, pos0, inv, s));
+  smol::BwAttn at{};
+  at.qkv = qkv;
+  at.ld = C3;
+  at.B = B;
+  at.T = T;
+  at.nq = D.nq;
+  at.nkv = D.nkv;
+  at.G = D.G;
+  at.D = d;
+  at.key_mask = key_mask;
+  at.window = window;
+  at.scale = 1.0f / std::sqrt((float)d);
+  at.scale2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  at.o = o;
+  at.lse = F(L.lse);
+  at.dO = dO;
+  at.dsum = F(L.dsum);
+  at.dqkv = dqkv;
+  at.part = F(L.part);
+  at.rope_on = rope_on ? 1 : 0;
+  at.pos0 = pos0;
+  for (int i = 0; i < 64; ++i) at.inv_freq[i] = inv.v[i];
+  SMOL_LAUNCH(SMOL_K_BW_ATTN_FWD, smol::bw_attention(0, at, s));
+  {  // h = x + o W_o^T
+    smol::BwGemm g = gemm_args(operand(o, QD), operand(Wo, QD), M, H, QD, h, H);
+    g.R = x;
+    g.ldr = H;
+    SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NT, smol::BW_RESID, g, s));
+  }
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_fwd(h, (const float *)w->mlp_norm, wn, r2, M, H, D.eps, s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NT, smol::BW_STORE,
+                                            gemm_args(operand(wn, H), operand(Wg, H, Wu, I), M, 2 * I, H, gu, 2 * I),
+                                            s));
+
+  // ---- MLP: dy_mlp = dy W_d, through SwiGLU into d(gate | up), and y = silu(g) u
+  {
+    smol::BwGemm g = gemm_args(operand(dy, H), operand(Wd, I), M, I, H, dgu, 2 * I);
+    g.G = gu;
+    g.ldg = 2 * I;
+    g.half = I;
+    g.Y = y;
+    g.ldy = I;
+    SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_SWIGLU, g, s));
+  }
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dy, H), operand(y, I), H, I, M,
+                                                                    gr->w_down, I), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_STORE,
+                                            gemm_args(operand(dgu, 2 * I), operand(Wg, H, Wu, I), M, H, 2 * I, dwn, H),
+                                            s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dgu, 2 * I), operand(wn, H), I, H, M,
+                                                                    gr->w_gate, H), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dgu + I, 2 * I), operand(wn, H), I, H, M,
+                                                                    gr->w_up, H), s));
+  // dh = dy + RMSNorm_m backward
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_bwd(dwn, h, r2, (const float *)w->mlp_norm, dy, dh, npart, M, H, s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_colsum(npart, smol::bw_rms_part_rows(M), H, gr->mlp_norm, accumulate, s));
+
+  // ---- attention
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dh, H), operand(o, QD), H, QD, M,
+                                                                    gr->wo, QD), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_STORE, gemm_args(operand(dh, H), operand(Wo, QD), M, QD,
+                                                                             H, dO, QD), s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rowdot(dO, o, F(L.dsum), M, T, D.nq, d, s));
+  SMOL_LAUNCH(SMOL_K_BW_ATTN_DQ, smol::bw_attention(1, at, s));
+  SMOL_LAUNCH(SMOL_K_BW_ATTN_DKDV, smol::bw_attention(2, at, s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_kv_reduce(F(L.part), dqkv, M, D.nq, D.nkv, D.G, d, C3, s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dqkv, C3), operand(u, H), QD, H, M,
+                                                                    gr->wq, H), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dqkv + QD, C3), operand(u, H), KD, H, M,
+                                                                    gr->wk, H), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dqkv + QD + KD, C3), operand(u, H), KD,
+                                                                    H, M, gr->wv, H), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_STORE,
+                                            gemm_args(operand(dqkv, C3), operand(Wq, H, Wk, QD, Wv, QD + KD), M, H, C3,
+                                                      du, H), s));
+  // dx = dh + RMSNorm_a backward
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_bwd(du, x, r1, (const float *)w->attn_norm, dh, dx, npart, M, H, s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_colsum(npart, smol::bw_rms_part_rows(M), H, gr->attn_norm, accumulate, s));
+  return SMOL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -611,6 +772,56 @@ smol_status smol_sample(const void *logits, int dtype, int batch, int vocab, int
                                  : smol::sample_next<float>((const float *)logits, (long)row_stride, batch, vocab,
                                                             temperature, top_k, top_p, uniforms, next_ids, s));
   return SMOL_OK;
+}
+
+
+smol_status smol_block_backward_workspace_size(const smol_config *cfg, int batch, int seq, size_t *bytes) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if (!bytes) return fail(SMOL_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch and seq must be >= 1");
+  *bytes = bw_layout(D, batch, seq).total;
+  return SMOL_OK;
+}
+
+smol_status smol_block_backward(const smol_config *cfg, const smol_layer_weights *w, int layer, const float *x,
+                                const float *dy, int batch, int seq, int pos0, const uint8_t *key_mask, float *dx,
+                                const smol_layer_grads *grads, int accumulate, void *ws, size_t ws_bytes,
+                                void *stream) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if (D.bf16) return fail(SMOL_ERR_UNSUPPORTED, "smol_block_backward supports dtype SMOL_F32 only");
+  if ((st = check_layer(w, layer)) != SMOL_OK) return st;
+  if (layer < 0 || layer >= D.L) return fail(SMOL_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, D.L);
+  if (!x || !dy || !dx) return fail(SMOL_ERR_INVALID_ARG, "x / dy / dx is NULL");
+  if (dx == x || dx == dy) return fail(SMOL_ERR_INVALID_ARG, "dx may not alias x or dy");
+  if (!grads) return fail(SMOL_ERR_INVALID_ARG, "grads is NULL");
+  {
+    float *const g[9] = {grads->attn_norm, grads->wq, grads->wk, grads->wv, grads->wo,
+                         grads->mlp_norm, grads->w_gate, grads->w_up, grads->w_down};
+    for (int i = 0; i < 9; ++i)
+      if (!g[i]) return fail(SMOL_ERR_INVALID_ARG, "grads: gradient %d is NULL", i);
+  }
+  if (accumulate != 0 && accumulate != 1) return fail(SMOL_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d, seq %d must be >= 1", batch, seq);
+  if (pos0 < 0) return fail(SMOL_ERR_INVALID_ARG, "pos0 %d < 0", pos0);
+  if ((long)pos0 + seq > D.max_pos)
+    return fail(SMOL_ERR_INVALID_ARG, "pos0 + seq = %ld exceeds max_pos %d", (long)pos0 + seq, D.max_pos);
+  if ((long)batch * seq * std::max(2 * D.I, (D.nq + 2 * D.nkv) * D.d) > INT32_MAX)
+    return fail(SMOL_ERR_UNSUPPORTED, "batch * seq too large");
+  const void *aligned[3] = {x, dy, dx};
+  for (const void *p : aligned)
+    if ((uintptr_t)p % 16) return fail(SMOL_ERR_INVALID_ARG, "x, dy and dx must be 16-byte aligned");
+  const BwWs lay = bw_layout(D, batch, seq);
+  if (!ws) return fail(SMOL_ERR_INVALID_ARG, "ws is NULL");
+  if (ws_bytes < lay.total) return fail(SMOL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, lay.total);
+  if ((uintptr_t)ws % ALIGN) return fail(SMOL_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  return backward_impl(D, w, layer, x, dy, batch, seq, pos0, key_mask, dx, grads, accumulate, (char *)ws, lay,
+                       (hipStream_t)stream);
 }
 
 const char *smol_status_string(smol_status s) {

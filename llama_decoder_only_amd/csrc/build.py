@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsmol.so")
 
-SOURCES = ["api.hip", "gemm.hip", "attention.hip", "decode_attention.hip", "norm_embed.hip", "sample.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attention.hip", "decode_attention.hip", "norm_embed.hip", "sample.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 

@@ -123,6 +123,71 @@ template <typename T>
 hipError_t sample_next(const T *logits, long row_stride, int B, int V, float temperature, int top_k, float top_p,
                        const float *uniforms, int32_t *next_ids, hipStream_t s);
 
+// ------------------------------------------------------------------ backward (float32)
+// backward.hip: the kernels of smol_block_backward.
+
+// A GEMM operand: up to three row-major matrices stacked along their rows (rows
+// [0, seg0) from p0, [seg0, seg1) from p1, the rest from p2), row length ld.
+struct BwOperand {
+  const float *p0, *p1, *p2;
+  int seg0, seg1, ld;
+};
+// C[M, N] = sum_k A(m, k) B(k, n), float32 MFMA. layout:
+//   BW_NT  A [M, K] and B [N, K] (K-contiguous): y = x W^T
+//   BW_NN  A [M, K], B [K, N]: dx = dy W
+//   BW_TN  A [K, M] and B [K, N] (contraction down the columns): dW = dy^T x
+// epi: BW_STORE C = acc; BW_ACCUM C += acc; BW_RESID C = R + acc; BW_SWIGLU, the
+// SwiGLU backward: with g = G[m, n], u = G[m, half + n] (the forward's gate and up)
+// and acc = dL/d(silu(g) u): C[m, n] = acc u silu'(g), C[m, half + n] = acc silu(g),
+// Y[m, n] = silu(g) u.
+enum { BW_NT = 0, BW_NN = 1, BW_TN = 2 };
+enum { BW_STORE = 0, BW_ACCUM = 1, BW_RESID = 2, BW_SWIGLU = 3 };
+struct BwGemm {
+  BwOperand a, b;
+  int M, N, K;
+  float *C;
+  int ldc;
+  const float *R;
+  int ldr;
+  const float *G;
+  int ldg, half;
+  float *Y;
+  int ldy;
+};
+hipError_t bw_gemm(int layout, int epi, const BwGemm &p, hipStream_t s);
+
+struct InvFreq {
+  float v[64];
+};
+// Attention of the block being differentiated: qkv [B*T, ld] holds q | k | v (q and
+// k rotated), query head h reads kv head h / G; key_mask [B, T] (token index) or
+// nullptr; window > 0: a query at t sees keys t - window < t' <= t.
+struct BwAttn {
+  const float *qkv;
+  int ld;
+  int B, T, nq, nkv, G, D;
+  const uint8_t *key_mask;
+  int window;
+  float scale, scale2;  // 1/sqrt(D), log2(e)/sqrt(D)
+  float *o;             // [B*T, nq*D]            (forward)
+  float *lse;           // [B, nq, T], base 2     (forward; read by dq, dkdv)
+  const float *dO;      // [B*T, nq*D]
+  const float *dsum;    // [B, nq, T]
+  float *dqkv;          // [B*T, ld]: dq written by dq; dk, dv by bw_kv_reduce
+  float *part;          // [2, nq, B*T, D]: per-query-head dk, dv partials (dkdv)
+  int rope_on, pos0;
+  float inv_freq[64];
+};
+hipError_t bw_attention(int which, const BwAttn &a, hipStream_t s);  // 0 forward, 1 dq, 2 dk/dv
+hipError_t bw_rowdot(const float *dO, const float *O, float *dsum, int M, int T, int nq, int D, hipStream_t s);
+hipError_t bw_kv_reduce(const float *part, float *dqkv, int M, int nq, int nkv, int G, int D, int ld, hipStream_t s);
+hipError_t bw_rope(float *qkv, int M, int T, int ld, int heads, int D, int pos0, const InvFreq &f, hipStream_t s);
+hipError_t bw_rms_fwd(const float *x, const float *w, float *u, float *r, int M, int H, float eps, hipStream_t s);
+int bw_rms_part_rows(int M);  // rows of the column partials bw_rms_bwd writes
+hipError_t bw_rms_bwd(const float *du, const float *x, const float *r, const float *w, const float *resid, float *dx,
+                      float *part, int M, int H, hipStream_t s);
+hipError_t bw_colsum(const float *part, int nrows, int H, float *dw, int accumulate, hipStream_t s);
+
 // Kernel-class timing (see smol_timing_begin). timing_before arms the next launch()
 // of that class with a start/stop event pair, which hipExtLaunchKernelGGL records at
 // the dispatch itself: the pair brackets the kernel's own execution, not the queue

@@ -21,7 +21,7 @@ import numpy as np
 # tensor ids of the seed tree
 T_EMBED, T_WQ, T_WK, T_WV, T_WO, T_WG, T_WU, T_WD = 0, 1, 2, 3, 4, 5, 6, 7
 T_ATTN_NORM, T_MLP_NORM, T_FINAL_NORM = 8, 9, 10
-T_HIDDEN, T_IDS, T_KCACHE, T_VCACHE, T_DECODE_IDS = 100, 101, 102, 103, 104
+T_HIDDEN, T_IDS, T_KCACHE, T_VCACHE, T_DECODE_IDS, T_DY = 100, 101, 102, 103, 104, 105
 
 
 @dataclass(frozen=True)
@@ -66,6 +66,9 @@ WORKLOADS: Dict[str, Shape] = {
     "long_prefill_bf16": Shape(**SMOLLM2, dtype="bf16", batch=1, seq=8192, std=INIT_STD, workload_id=3),
     # decode: batch 64, 2047 cached positions, one new token each
     "decode_bf16": Shape(**SMOLLM2, dtype="bf16", batch=64, seq=1, std=INIT_STD, workload_id=4, cache_len=2047),
+    # backward of one SmolLM2-135M block in float32 at the prefill's batch 4 x seq 512
+    "block_backward_f32": Shape(**{**SMOLLM2, "n_layers": 1}, dtype="f32", batch=4, seq=512, std=INIT_STD,
+                                workload_id=6, norm_jitter=0.1),
     # SmolLM3-3B-shaped prefill, bfloat16, batch 2 x seq 4096
     "smollm3_prefill_bf16": Shape(**SMOLLM3_SHAPE, dtype="bf16", batch=2, seq=4096, std=0.02, workload_id=5),
 }
@@ -190,6 +193,12 @@ def model_weights(s: Shape, seed: int = 0) -> Model:
 def hidden_states(s: Shape, seed: int = 0) -> Tensor:
     """Block input [B, T, H] ~ N(0, 1)."""
     return normal(s, seed, 0, T_HIDDEN, (s.batch, s.seq, s.hidden), 1.0)
+
+
+def output_grad(s: Shape, seed: int = 0) -> Tensor:
+    """Gradient arriving at a block's output [B, T, H] ~ N(0, 1), float32."""
+    x = _rng(s, seed, 0, T_DY).standard_normal(size=(s.batch, s.seq, s.hidden))
+    return _store(x, "f32")
 
 
 def token_ids(s: Shape, seed: int = 0, tensor_id: int = T_IDS) -> np.ndarray:

@@ -215,6 +215,49 @@ def test_prefill_ex_rejects():
     assert call(kc=None) == B.SMOL_ERR_INVALID_ARG  # one cache without the other
 
 
+def _grads_struct(null=None):
+    return B.smol_layer_grads(*[None if n == null else FAKE for n in B.LAYER_FIELDS])
+
+
+def _backward(cfg, w, g=None, layer=0, x=FAKE, dy=FAKE + 4096, dx=FAKE + 8192, batch=1, seq=8, pos0=0, acc=0,
+              ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        n = ctypes.c_size_t(0)
+        assert B.lib().smol_block_backward_workspace_size(ctypes.byref(cfg.c()), batch if batch > 0 else 1,
+                                                          seq if seq > 0 else 1, ctypes.byref(n)) == 0
+        ws_bytes = n.value
+    g = _grads_struct() if g is None else g
+    return B.lib().smol_block_backward(ctypes.byref(cfg.c()), ctypes.byref(w), layer, x, dy, batch, seq, pos0, None,
+                                       dx, ctypes.byref(g), acc, ws, ws_bytes, None)
+
+
+def test_block_backward_rejects():
+    f32 = _cfg(dtype="f32")
+    w = _layer_struct()
+    n = ctypes.c_size_t(0)
+    assert B.lib().smol_block_backward_workspace_size(ctypes.byref(f32.c()), 4, 512, ctypes.byref(n)) == 0
+    assert n.value > 4 * 512 * (576 * 8 + 1536 * 5) * 4
+    assert _backward(_cfg(), w) == B.SMOL_ERR_UNSUPPORTED and "F32" in B.smol_last_error()  # bf16 config
+    assert _backward(f32, _layer_struct(null="wo")) == B.SMOL_ERR_INVALID_ARG and "wo" in B.smol_last_error()
+    assert _backward(f32, w, g=_grads_struct(null="w_up")) == B.SMOL_ERR_INVALID_ARG
+    assert _backward(f32, w, layer=30) == B.SMOL_ERR_INVALID_ARG and "layer" in B.smol_last_error()
+    assert _backward(f32, w, layer=-1) == B.SMOL_ERR_INVALID_ARG
+    assert _backward(f32, w, x=None) == B.SMOL_ERR_INVALID_ARG
+    assert _backward(f32, w, dx=FAKE) == B.SMOL_ERR_INVALID_ARG and "alias" in B.smol_last_error()
+    assert _backward(f32, w, dx=FAKE + 8196) == B.SMOL_ERR_INVALID_ARG and "aligned" in B.smol_last_error()
+    assert _backward(f32, w, acc=2) == B.SMOL_ERR_INVALID_ARG
+    assert _backward(f32, w, batch=0) == B.SMOL_ERR_INVALID_ARG
+    assert _backward(f32, w, pos0=8190, seq=8) == B.SMOL_ERR_INVALID_ARG and "max_pos" in B.smol_last_error()
+    assert _backward(f32, w, pos0=-2) == B.SMOL_ERR_INVALID_ARG
+    assert _backward(f32, w, ws=None) == B.SMOL_ERR_INVALID_ARG
+    assert _backward(f32, w, ws=FAKE + 64) == B.SMOL_ERR_INVALID_ARG and "aligned" in B.smol_last_error()
+    need = ctypes.c_size_t(0)
+    B.lib().smol_block_backward_workspace_size(ctypes.byref(f32.c()), 1, 8, ctypes.byref(need))
+    assert _backward(f32, w, ws_bytes=need.value - 1) == B.SMOL_ERR_WORKSPACE
+    assert B.lib().smol_block_backward(None, ctypes.byref(w), 0, FAKE, FAKE, 1, 8, 0, None, FAKE, None, 0, FAKE,
+                                       need.value, None) == B.SMOL_ERR_INVALID_ARG
+
+
 def test_trim_at_eos():
     out = np.array([[1, 2], [0, 3], [0, 0], [5, 0]])
     assert B.trim_at_eos(out, 0).shape[0] == 3      # step 2: every sequence's new token is eos

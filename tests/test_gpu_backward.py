@@ -1,0 +1,124 @@
+"""GPU parity of smol_block_backward (float32) against the float64 CPU oracle
+(oracle/backward.py): the input gradient and all nine weight gradients, element by
+element, at rel <= 1e-4 (max |gpu - oracle| / max |oracle| per tensor).
+
+Shapes: the SmolLM2-135M block (9 query heads over 3 kv heads of 64) with a ragged
+sequence (not a multiple of the 64-row tiles) at a position offset, a padding mask
+with several key blocks, a SmolLM3-like NoPE block with a sliding window and head
+dim 128 (4 query heads over 1 kv head), and the full 4 x 512 shape the benchmark
+times; plus gradient accumulation and run-to-run determinism."""
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle.backward as BW  # noqa: E402
+from llama_decoder_only_amd import binding as B  # noqa: E402
+from llama_decoder_only_amd import synthetic as S  # noqa: E402
+from tests.gpu_helpers import TOL_F32, ocfg, olayer, rel, say, to_np  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+NAMES = ("x",) + S.Layer.NAMES
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(s, layer=0, pos0=0, mask=None, accumulate=False, grads=None, seed=0):
+    """(GPU gradients as float64 dict, inputs) for the block of shape s."""
+    lw = S.layer_weights(s, seed, layer)
+    x = S.hidden_states(s, seed)
+    dy = S.output_grad(s, seed)
+    w = B.upload_layer(lw)
+    xt, dyt = B.to_device(x), B.to_device(dy)
+    dx = torch.empty_like(xt)
+    g = grads if grads is not None else B.LayerGrads.zeros_like(w)
+    km = None if mask is None else torch.from_numpy(mask.astype(np.uint8)).to(DEV)
+    B.smol_block_backward(B.Config.from_shape(s), w, xt, dyt, dx, g, layer=layer, pos0=pos0, key_mask=km,
+                          accumulate=accumulate)
+    torch.cuda.synchronize()
+    got = {"x": to_np(dx), **{n: to_np(t) for n, t in g.as_dict().items()}}
+    return got, (lw, x, dy, w, xt, dyt, g)
+
+
+def _oracle(s, lw, x, dy, layer=0, pos0=0, mask=None):
+    full = None
+    if mask is not None:  # the oracle indexes the mask by absolute position
+        full = np.ones((s.batch, pos0 + s.seq), bool)
+        full[:, pos0:] = mask
+    return BW.block_backward(x.f64, olayer(lw), ocfg(s), dy.f64, pos0=pos0, layer=layer, key_mask=full)
+
+
+def _compare(got, want, tol=TOL_F32):
+    worst = 0.0
+    for n in NAMES:
+        assert got[n].shape == want[n].shape, n
+        assert np.isfinite(got[n]).all(), n
+        r = rel(got[n], want[n])
+        worst = max(worst, r)
+        assert r <= tol, (n, r)
+    say(f"worst rel over the ten gradients: {worst:.2e}")
+
+
+def test_backward_smollm2_block_ragged():
+    s = S.workload("block_backward_f32", batch=2, seq=100)
+    say("backward SmolLM2 block B=2 T=100 pos0=5")
+    got, (lw, x, dy, *_) = _run(s, pos0=5)
+    _compare(got, _oracle(s, lw, x, dy, pos0=5))
+
+
+def test_backward_key_mask_several_key_blocks():
+    s = S.Shape(hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=512, n_layers=1, vocab=64,
+                max_pos=2048, rms_eps=1e-5, rope_theta=1e5, dtype="f32", batch=3, seq=333, std=0.06,
+                workload_id=41, norm_jitter=0.2)
+    rng = np.random.default_rng(7)
+    mask = rng.random((3, 333)) < 0.7
+    mask[:, 0] = True
+    say("backward masked B=3 T=333 (6 key blocks)")
+    got, (lw, x, dy, *_) = _run(s, mask=mask)
+    _compare(got, _oracle(s, lw, x, dy, mask=mask))
+
+
+def test_backward_nope_window_head_dim_128():
+    s = S.Shape(hidden=512, n_heads=4, n_kv_heads=1, head_dim=128, intermediate=1024, n_layers=4, vocab=64,
+                max_pos=4096, rms_eps=1e-6, rope_theta=5e6, dtype="f32", batch=2, seq=300, std=0.04,
+                workload_id=42, norm_jitter=0.1, no_rope_interval=2, sliding_window=90)
+    for layer in (1, 2):  # block 1 is NoPE with the window, block 2 rotary with full attention
+        say(f"backward d=128 G=4 T=300 layer {layer}")
+        got, (lw, x, dy, *_) = _run(s, layer=layer, pos0=17)
+        _compare(got, _oracle(s, lw, x, dy, layer=layer, pos0=17))
+
+
+def test_backward_full_shape():
+    """The 4 x 512 SmolLM2-135M block the benchmark times, every gradient element."""
+    s = S.workload("block_backward_f32")
+    say("backward SmolLM2 block B=4 T=512")
+    got, (lw, x, dy, *_) = _run(s)
+    _compare(got, _oracle(s, lw, x, dy))
+
+
+def test_backward_accumulate_and_determinism():
+    s = S.workload("block_backward_f32", batch=2, seq=70)
+    say("backward accumulate + determinism")
+    got, (lw, x, dy, w, xt, dyt, g) = _run(s)
+    first = {n: t.clone() for n, t in g.as_dict().items()}
+    dx2 = torch.empty_like(xt)
+    B.smol_block_backward(B.Config.from_shape(s), w, xt, dyt, dx2, g, accumulate=True)
+    torch.cuda.synchronize()
+    for n, t in g.as_dict().items():
+        assert torch.equal(t, 2 * first[n]), n  # v + v is exact
+    assert np.array_equal(to_np(dx2), got["x"])
+    g2 = B.LayerGrads.zeros_like(w)
+    B.smol_block_backward(B.Config.from_shape(s), w, xt, dyt, dx2, g2)
+    torch.cuda.synchronize()
+    for n, t in g2.as_dict().items():
+        assert torch.equal(t, first[n]), n
