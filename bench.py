@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+F32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 
 
 def prefill_flops(s) -> dict:
@@ -60,6 +61,20 @@ def decode_bytes(s, P: int) -> dict:
         "decode_attention_per_launch": kv_read,
     }
     out["total"] = out["kv_read"] + out["weights"] + out["kv_append"] + out["logits"]
+    return out
+
+
+def backward_flops(s) -> dict:
+    """Algorithmic FLOPs of one block backward (forward recomputed): every linear layer
+    three times (the forward product, the data gradient, the weight gradient), and per
+    visible (query, key) pair of every head 12 d (S and P V forward; dV, dP, dQ, dK)."""
+    M, H, I, d = s.batch * s.seq, s.hidden, s.intermediate, s.head_dim
+    qkv = (s.n_heads + 2 * s.n_kv_heads) * d
+    lin = 2 * M * H * (qkv + s.n_heads * d + 2 * I + I)
+    pairs = s.batch * s.n_heads * s.seq * (s.seq + 1) // 2
+    out = {"gemm": 3 * lin, "attention": 12 * d * pairs,
+           "attention_forward": 4 * d * pairs, "attention_dq": 4 * d * pairs, "attention_dkdv": 8 * d * pairs}
+    out["total"] = out["gemm"] + out["attention"]
     return out
 
 
@@ -188,6 +203,69 @@ def cpu_baseline(s, model, ids_np, budget_s=12.0):
                       f"logits, numpy float64, {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
 
 
+def backward_section(B, S, torch, dev, stream, args):
+    """smol_block_backward on one SmolLM2-135M block, float32, batch 4 x seq 512: the
+    whole call (graph-replayed, median over reps) and each kernel class's summed
+    launch durations from the runtime's dispatch events."""
+    sb = S.workload("block_backward_f32")
+    cfg = B.Config.from_shape(sb)
+    w = B.upload_layer(S.layer_weights(sb, 0, 0), dev)
+    x, dy = B.to_device(S.hidden_states(sb, 0), dev), B.to_device(S.output_grad(sb, 0), dev)
+    dx = torch.empty_like(x)
+    g = B.LayerGrads.zeros_like(w)
+    ws = torch.empty(B.smol_block_backward_workspace_size(cfg, sb.batch, sb.seq), dtype=torch.uint8, device=dev)
+
+    def bstep():
+        B.smol_block_backward(cfg, w, x, dy, dx, g, ws=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            bstep()
+    torch.cuda.synchronize()
+    ref = dx.clone()
+    fn, mode = bstep, "eager"
+    if not args.no_graph:
+        bg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bg, stream=stream):
+            bstep()
+        dx.zero_()
+        bg.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(dx, ref):
+            raise RuntimeError("backward graph replay differs from the eager result")
+        fn, mode = bg.replay, "hip_graph"
+    reps = _rep_ms(fn, max(args.steps, 5), torch, stream)
+    t_s = float(np.median(reps)) * 1e-3
+    fl = backward_flops(sb)
+    kern = {}
+    for k in ("bw_gemm", "bw_attn_fwd", "bw_attn_dq", "bw_attn_dkdv", "bw_rows"):
+        with torch.cuda.stream(stream):
+            ms, n = _kernel_time(B, k, bstep, torch)
+        kern[k] = {"us": round(ms * 1e3, 2), "launches": n}
+    ach = {"bw_gemm": fl["gemm"], "bw_attn_fwd": fl["attention_forward"], "bw_attn_dq": fl["attention_dq"],
+           "bw_attn_dkdv": fl["attention_dkdv"]}
+    for k, f in ach.items():
+        kern[k]["tflops"] = round(f / (kern[k]["us"] * 1e-6) / 1e12, 2) if kern[k]["us"] > 0 else None
+    dom = max(ach, key=lambda k: kern[k]["us"])
+    dom_tf = kern[dom]["tflops"] or 0.0
+    del w, x, dy, dx, g, ws
+    return {
+        "workload": "backward of one SmolLM2-135M block (forward recomputed), float32, batch 4 x seq 512, "
+                    "input and all nine weight gradients",
+        "timing": mode + " (median of reps)",
+        "ms_per_call": round(t_s * 1e3, 4),
+        "rep_ms": _pct(reps),
+        "tokens_per_s": round(sb.batch * sb.seq / t_s, 1),
+        "algorithmic_gflop": round(fl["total"] / 1e9, 3),
+        "tflops": round(fl["total"] / t_s / 1e12, 2),
+        "mfma_f32_frac": round(fl["total"] / t_s / 1e12 / F32_PEAK_TFLOPS, 4),
+        "kernels": kern,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tf, "peak": F32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom_tf / F32_PEAK_TFLOPS, 4), "traffic": None,
+                     "note": "summed over the class's launches in one call"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +275,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (outside the timed region): "
                          "a known-size reference for hardware byte counters")
@@ -406,6 +485,9 @@ def main():
             "sample_us": samp,
         }
         del kc, vc
+
+    if not args.no_backward:
+        out["backward"] = backward_section(B, S, torch, dev, stream, args)
 
     if not args.no_decode:
         out["ceilings"] = ceilings(torch, dev)

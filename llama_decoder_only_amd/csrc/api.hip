@@ -450,8 +450,20 @@ smol_status check_model(const Dims &D, const smol_model_weights *w) {
 // smol_block_backward: the forward recomputed with its activations kept, then the
 // chain rule in reverse (backward.hip). M = B*T rows; C3 = (nq + 2 nkv) d.
 struct BwWs {
-  size_t u, r1, qkv, o, lse, h, wn, r2, gu, dgu, y, dwn, dh, dO, dsum, dqkv, part, du, npart, total;
+  size_t u, r1, qkv, o, lse, h, wn, r2, gu, dgu, y, dwn, dh, dO, dsum, dqkv, part, du, npart, gpart, total;
 };
+
+// The GEMMs of one block backward: (M, N, K, epilogue) of each launch, in order.
+struct BwShape {
+  int M, N, K, epi;
+};
+std::vector<BwShape> bw_shapes(const Dims &D, int M) {
+  const int H = D.H, I = D.I, QD = D.nq * D.d, C3 = QD + 2 * D.nkv * D.d;
+  using namespace smol;
+  return {{M, C3, H, BW_STORE},  {M, H, QD, BW_RESID},  {M, 2 * I, H, BW_STORE}, {M, I, H, BW_SWIGLU},
+          {H, I, M, BW_ACCUM},   {M, H, 2 * I, BW_STORE}, {2 * I, H, M, BW_ACCUM}, {H, QD, M, BW_ACCUM},
+          {M, QD, H, BW_STORE},  {C3, H, M, BW_ACCUM},  {M, H, C3, BW_STORE}};
+}
 
 BwWs bw_layout(const Dims &D, int B, int T) {
   BwWs w{};
@@ -477,6 +489,9 @@ BwWs bw_layout(const Dims &D, int B, int T) {
   w.part = take(2 * (size_t)D.nq * M * D.d);
   w.du = take(M * H);
   w.npart = take((size_t)smol::bw_rms_part_rows((int)M) * H);
+  size_t gp = 0;
+  for (const BwShape &g : bw_shapes(D, (int)M)) gp = std::max(gp, smol::bw_gemm_part_floats(g.M, g.N, g.K, g.epi));
+  w.gpart = take(std::max<size_t>(gp, 1));
   w.total = off;
   return w;
 }
@@ -494,7 +509,18 @@ smol::BwGemm gemm_args(const smol::BwOperand &a, const smol::BwOperand &b, int M
   g.N = N;
   g.K = K;
   g.C = C;
+  g.cseg0 = g.cseg1 = 1 << 30;
   g.ldc = ldc;
+  g.ksplit = 1;
+  return g;
+}
+
+// Output rows split over up to three matrices (fused weight gradients).
+smol::BwGemm with_c_segments(smol::BwGemm g, float *C1, int cseg0, float *C2 = nullptr, int cseg1 = 1 << 30) {
+  g.C1 = C1;
+  g.cseg0 = cseg0;
+  g.C2 = C2;
+  g.cseg1 = cseg1;
   return g;
 }
 
@@ -507,24 +533,30 @@ smol_status backward_impl(const Dims &D, const smol_layer_weights *w, int layer,
   auto F = [&](size_t off) { return (float *)(ws + off); };
   float *u = F(L.u), *r1 = F(L.r1), *qkv = F(L.qkv), *o = F(L.o), *h = F(L.h), *wn = F(L.wn), *r2 = F(L.r2);
   float *gu = F(L.gu), *dgu = F(L.dgu), *y = F(L.y), *dwn = F(L.dwn), *dh = F(L.dh), *dO = F(L.dO);
-  float *dqkv = F(L.dqkv), *du = F(L.du), *npart = F(L.npart);
+  float *dqkv = F(L.dqkv), *du = F(L.du), *npart = F(L.npart), *gpart = F(L.gpart);
   const float *Wq = (const float *)w->wq, *Wk = (const float *)w->wk, *Wv = (const float *)w->wv;
   const float *Wo = (const float *)w->wo, *Wg = (const float *)w->w_gate, *Wu = (const float *)w->w_up;
   const float *Wd = (const float *)w->w_down;
+  const float *an = (const float *)w->attn_norm, *mn = (const float *)w->mlp_norm;
   const int wgrad = accumulate ? smol::BW_ACCUM : smol::BW_STORE;
   using smol::BW_NN;
   using smol::BW_NT;
   using smol::BW_TN;
+  using smol::BW_STORE;
+  // every GEMM goes through here: the K split its shape calls for, over gpart
+  auto gemm = [&](int layout, int epi, smol::BwGemm g) -> hipError_t {
+    g.ksplit = smol::bw_gemm_ksplit(g.M, g.N, g.K, epi);
+    g.part = gpart;
+    return smol::bw_gemm(layout, epi, g, s);
+  };
 
   // ---- forward, keeping what the backward reads
-  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_fwd(x, (const float *)w->attn_norm, u, r1, M, H, D.eps, s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NT, smol::BW_STORE,
-                                            gemm_args(operand(u, H), operand(Wq, H, Wk, QD, Wv, QD + KD), M, C3, H,
-                                                      qkv, C3), s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_fwd(x, an, u, r1, M, H, D.eps, s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NT, BW_STORE, gemm_args(operand(u, H), operand(Wq, H, Wk, QD, Wv, QD + KD),
+                                                              M, C3, H, qkv, C3)));
   smol::InvFreq inv{};
   fill_inv_freq(D, inv.v);
-  if (rope_on)
-    SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rope(qkv, M, T, C3, D.nq + D.nkv, d, pos0, inv, s));
+  if (rope_on) SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rope(qkv, M, T, C3, D.nq + D.nkv, d, pos0, inv, s));
   smol::BwAttn at{};
   at.qkv = qkv;
   at.ld = C3;
@@ -552,12 +584,11 @@ smol_status backward_impl(const Dims &D, const smol_layer_weights *w, int layer,
     smol::BwGemm g = gemm_args(operand(o, QD), operand(Wo, QD), M, H, QD, h, H);
     g.R = x;
     g.ldr = H;
-    SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NT, smol::BW_RESID, g, s));
+    SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NT, smol::BW_RESID, g));
   }
-  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_fwd(h, (const float *)w->mlp_norm, wn, r2, M, H, D.eps, s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NT, smol::BW_STORE,
-                                            gemm_args(operand(wn, H), operand(Wg, H, Wu, I), M, 2 * I, H, gu, 2 * I),
-                                            s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_fwd(h, mn, wn, r2, M, H, D.eps, s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NT, BW_STORE, gemm_args(operand(wn, H), operand(Wg, H, Wu, I), M, 2 * I, H,
+                                                              gu, 2 * I)));
 
   // ---- MLP: dy_mlp = dy W_d, through SwiGLU into d(gate | up), and y = silu(g) u
   {
@@ -567,41 +598,34 @@ smol_status backward_impl(const Dims &D, const smol_layer_weights *w, int layer,
     g.half = I;
     g.Y = y;
     g.ldy = I;
-    SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_SWIGLU, g, s));
+    SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NN, smol::BW_SWIGLU, g));
   }
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dy, H), operand(y, I), H, I, M,
-                                                                    gr->w_down, I), s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_STORE,
-                                            gemm_args(operand(dgu, 2 * I), operand(Wg, H, Wu, I), M, H, 2 * I, dwn, H),
-                                            s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dgu, 2 * I), operand(wn, H), I, H, M,
-                                                                    gr->w_gate, H), s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dgu + I, 2 * I), operand(wn, H), I, H, M,
-                                                                    gr->w_up, H), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_TN, wgrad, gemm_args(operand(dy, H), operand(y, I), H, I, M, gr->w_down, I)));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NN, BW_STORE, gemm_args(operand(dgu, 2 * I), operand(Wg, H, Wu, I), M, H,
+                                                              2 * I, dwn, H)));
+  // dW_gate | dW_up in one launch: rows [0, I) of d(gate | up)^T w to W_gate's gradient
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_TN, wgrad, with_c_segments(gemm_args(operand(dgu, 2 * I), operand(wn, H), 2 * I,
+                                                                           H, M, gr->w_gate, H),
+                                                                 gr->w_up, I)));
   // dh = dy + RMSNorm_m backward
-  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_bwd(dwn, h, r2, (const float *)w->mlp_norm, dy, dh, npart, M, H, s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_bwd(dwn, h, r2, mn, dy, dh, npart, M, H, s));
   SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_colsum(npart, smol::bw_rms_part_rows(M), H, gr->mlp_norm, accumulate, s));
 
   // ---- attention
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dh, H), operand(o, QD), H, QD, M,
-                                                                    gr->wo, QD), s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_STORE, gemm_args(operand(dh, H), operand(Wo, QD), M, QD,
-                                                                             H, dO, QD), s));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_TN, wgrad, gemm_args(operand(dh, H), operand(o, QD), H, QD, M, gr->wo, QD)));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NN, BW_STORE, gemm_args(operand(dh, H), operand(Wo, QD), M, QD, H, dO, QD)));
   SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rowdot(dO, o, F(L.dsum), M, T, D.nq, d, s));
   SMOL_LAUNCH(SMOL_K_BW_ATTN_DQ, smol::bw_attention(1, at, s));
   SMOL_LAUNCH(SMOL_K_BW_ATTN_DKDV, smol::bw_attention(2, at, s));
   SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_kv_reduce(F(L.part), dqkv, M, D.nq, D.nkv, D.G, d, C3, s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dqkv, C3), operand(u, H), QD, H, M,
-                                                                    gr->wq, H), s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dqkv + QD, C3), operand(u, H), KD, H, M,
-                                                                    gr->wk, H), s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_TN, wgrad, gemm_args(operand(dqkv + QD + KD, C3), operand(u, H), KD,
-                                                                    H, M, gr->wv, H), s));
-  SMOL_LAUNCH(SMOL_K_BW_GEMM, smol::bw_gemm(BW_NN, smol::BW_STORE,
-                                            gemm_args(operand(dqkv, C3), operand(Wq, H, Wk, QD, Wv, QD + KD), M, H, C3,
-                                                      du, H), s));
+  // dW_q | dW_k | dW_v in one launch
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_TN, wgrad, with_c_segments(gemm_args(operand(dqkv, C3), operand(u, H), C3, H, M,
+                                                                           gr->wq, H),
+                                                                 gr->wk, QD, gr->wv, QD + KD)));
+  SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NN, BW_STORE, gemm_args(operand(dqkv, C3), operand(Wq, H, Wk, QD, Wv, QD + KD),
+                                                              M, H, C3, du, H)));
   // dx = dh + RMSNorm_a backward
-  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_bwd(du, x, r1, (const float *)w->attn_norm, dh, dx, npart, M, H, s));
+  SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_bwd(du, x, r1, an, dh, dx, npart, M, H, s));
   SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_colsum(npart, smol::bw_rms_part_rows(M), H, gr->attn_norm, accumulate, s));
   return SMOL_OK;
 }

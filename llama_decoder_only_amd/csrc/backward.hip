@@ -35,6 +35,8 @@
 // No atomics: every float sum has a fixed order, so a call is deterministic.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -108,10 +110,18 @@ __device__ __forceinline__ void stage_store(float (*X)[GLD], const f32x4 (&v)[2]
 
 __device__ __forceinline__ float sigmoid(float g) { return 1.0f / (1.0f + expf(-g)); }
 
+// Destination of C element (row, col): the row's segment picks the matrix.
+__device__ __forceinline__ float *c_at(const BwGemm &p, int row, int col) {
+  if (row < p.cseg0) return p.C + (size_t)row * p.ldc + col;
+  if (row < p.cseg1) return p.C1 + (size_t)(row - p.cseg0) * p.ldc + col;
+  return p.C2 + (size_t)(row - p.cseg1) * p.ldc + col;
+}
+
 // A 64 x 64 tile per workgroup of 4 waves, each wave one 32 x 32 quarter. K runs in
 // stages of 32 through two LDS buffers: the next stage's global loads are in flight
-// while the current one feeds the MFMAs; one barrier per stage.
-template <bool AK, bool BK, int EB>
+// while the current one feeds the MFMAs; one barrier per stage. With a K split,
+// workgroup i takes tile i % tiles and K range i / tiles, and writes its partial tile.
+template <bool AK, bool BK, int EB, bool SPLIT>
 __global__ __launch_bounds__(256) void bw_gemm_kernel(const BwGemm p) {
   __shared__ float As[2][GK][GLD];
   __shared__ float Bs[2][GK][GLD];
@@ -119,32 +129,41 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(const BwGemm p) {
   const int l32 = lane & 31, hl = lane >> 5;
   const int wm = wave & 1, wn = wave >> 1;
   const int ntn = (p.N + GT - 1) / GT;
-  const int m0 = (blockIdx.x / ntn) * GT, n0 = (blockIdx.x % ntn) * GT;
-  const int nk = (p.K + GK - 1) / GK;
-
-  f32x4 ra[2], rb[2];
-  stage_load<AK>(ra, p.a, m0, p.M, 0, p.K, tid);
-  stage_load<BK>(rb, p.b, n0, p.N, 0, p.K, tid);
-  stage_store<AK>(As[0], ra, tid);
-  stage_store<BK>(Bs[0], rb, tid);
-  __syncthreads();
+  const int tiles = ntn * ((p.M + GT - 1) / GT);
+  const int tile = SPLIT ? blockIdx.x % tiles : blockIdx.x;
+  const int m0 = (tile / ntn) * GT, n0 = (tile % ntn) * GT;
+  const int nk_all = (p.K + GK - 1) / GK;
+  int kt0 = 0, kt1 = nk_all;
+  if constexpr (SPLIT) {
+    const int per = (nk_all + p.ksplit - 1) / p.ksplit, split = blockIdx.x / tiles;
+    kt0 = min(split * per, nk_all);
+    kt1 = min(kt0 + per, nk_all);
+  }
 
   f32x16 acc = {};
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      stage_load<AK>(ra, p.a, m0, p.M, (kt + 1) * GK, p.K, tid);
-      stage_load<BK>(rb, p.b, n0, p.N, (kt + 1) * GK, p.K, tid);
-    }
-#pragma unroll
-    for (int kk = 0; kk < GK / 2; ++kk)
-      acc = mfma2(As[cur][2 * kk + hl][wm * 32 + l32], Bs[cur][2 * kk + hl][wn * 32 + l32], acc);
-    if (more) {
-      stage_store<AK>(As[cur ^ 1], ra, tid);
-      stage_store<BK>(Bs[cur ^ 1], rb, tid);
-    }
+  if (kt0 < kt1) {
+    f32x4 ra[2], rb[2];
+    stage_load<AK>(ra, p.a, m0, p.M, kt0 * GK, p.K, tid);
+    stage_load<BK>(rb, p.b, n0, p.N, kt0 * GK, p.K, tid);
+    stage_store<AK>(As[0], ra, tid);
+    stage_store<BK>(Bs[0], rb, tid);
     __syncthreads();
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      const bool more = kt + 1 < kt1;
+      if (more) {
+        stage_load<AK>(ra, p.a, m0, p.M, (kt + 1) * GK, p.K, tid);
+        stage_load<BK>(rb, p.b, n0, p.N, (kt + 1) * GK, p.K, tid);
+      }
+#pragma unroll
+      for (int kk = 0; kk < GK / 2; ++kk)
+        acc = mfma2(As[cur][2 * kk + hl][wm * 32 + l32], Bs[cur][2 * kk + hl][wn * 32 + l32], acc);
+      if (more) {
+        stage_store<AK>(As[cur ^ 1], ra, tid);
+        stage_store<BK>(Bs[cur ^ 1], rb, tid);
+      }
+      __syncthreads();
+    }
   }
 
   const int col = n0 + wn * 32 + l32;
@@ -154,14 +173,16 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(const BwGemm p) {
     const int row = m0 + wm * 32 + acc_row(r, lane);
     if (row >= p.M) continue;
     const float v = acc[r];
-    float *c = p.C + (size_t)row * p.ldc + col;
-    if constexpr (EB == BW_STORE) {
-      *c = v;
+    if constexpr (SPLIT) {
+      p.part[((size_t)(blockIdx.x / tiles) * p.M + row) * p.N + col] = v;
+    } else if constexpr (EB == BW_STORE) {
+      *c_at(p, row, col) = v;
     } else if constexpr (EB == BW_ACCUM) {
-      *c += v;
+      *c_at(p, row, col) += v;
     } else if constexpr (EB == BW_RESID) {
-      *c = p.R[(size_t)row * p.ldr + col] + v;
+      *c_at(p, row, col) = p.R[(size_t)row * p.ldr + col] + v;
     } else {  // BW_SWIGLU: v = dL/dy_mlp at (row, col); gate and up from the forward
+      float *c = c_at(p, row, col);
       const float g = p.G[(size_t)row * p.ldg + col], u = p.G[(size_t)row * p.ldg + p.half + col];
       const float sg = sigmoid(g), sl = g * sg;
       c[0] = v * u * (sg * (1.0f + g * (1.0f - sg)));  // d silu(g)/dg = s (1 + g (1 - s))
@@ -171,10 +192,36 @@ __global__ __launch_bounds__(256) void bw_gemm_kernel(const BwGemm p) {
   }
 }
 
+// The K split's partial tiles added in split order, then the epilogue. One thread
+// per 4 consecutive columns (N is a multiple of 4).
+template <int EB>
+__global__ __launch_bounds__(256) void bw_split_reduce_kernel(const BwGemm p) {
+  const int n4 = p.N / 4;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.M * n4) return;
+  const int row = i / n4, col = (i % n4) * 4;
+  const size_t mn = (size_t)p.M * p.N, at = (size_t)row * p.N + col;
+  f32x4 v = *reinterpret_cast<const f32x4 *>(p.part + at);
+  for (int k = 1; k < p.ksplit; ++k) v += *reinterpret_cast<const f32x4 *>(p.part + k * mn + at);
+  float *c = c_at(p, row, col);
+  if constexpr (EB == BW_ACCUM) v += *reinterpret_cast<const f32x4 *>(c);
+  if constexpr (EB == BW_RESID) v += *reinterpret_cast<const f32x4 *>(p.R + (size_t)row * p.ldr + col);
+  *reinterpret_cast<f32x4 *>(c) = v;
+}
+
 template <bool AK, bool BK, int EB>
 hipError_t bw_gemm_launch(const BwGemm &p, hipStream_t s) {
   const int tiles = ((p.M + GT - 1) / GT) * ((p.N + GT - 1) / GT);
-  return launch(bw_gemm_kernel<AK, BK, EB>, dim3(tiles), dim3(256), s, p);
+  if constexpr (EB != BW_SWIGLU) {
+    if (p.ksplit > 1) {  // timed as one operation: start at the first kernel, stop after the reduce
+      hipEvent_t e0 = nullptr, e1 = nullptr;
+      timing_take(&e0, &e1);
+      hipError_t e = launch_ev(bw_gemm_kernel<AK, BK, EB, true>, dim3(tiles * p.ksplit), dim3(256), s, e0, nullptr, p);
+      if (e != hipSuccess) return e;
+      return launch_ev(bw_split_reduce_kernel<EB>, dim3((p.M * (p.N / 4) + 255) / 256), dim3(256), s, nullptr, e1, p);
+    }
+  }
+  return launch(bw_gemm_kernel<AK, BK, EB, false>, dim3(tiles), dim3(256), s, p);
 }
 
 // ------------------------------------------------------------------ attention
@@ -184,13 +231,14 @@ __device__ __forceinline__ bool visible(const BwAttn &a, int b, int tq, int tk) 
          (a.key_mask == nullptr || a.key_mask[(size_t)b * a.T + tk] != 0);
 }
 
-// Rows key0 .. key0 + 63 of two column blocks of qkv (or of any [M, ld] matrices)
-// into LDS [64][D + 1] (the +1 spreads a column read over all banks); zeros past T.
+// Rows row0 .. row0 + 127 (two blocks of 64) of two column blocks of [B*T, ld]
+// matrices into LDS [128][D + 1] (the +1 spreads a column read over all banks);
+// zeros past T. All 256 threads of the workgroup take part.
 template <int D>
 __device__ __forceinline__ void stage_rows2(float *X, float *Y, const float *xs, const float *ys, int ldx, int ldy,
                                             int b, int T, int row0, int tid) {
   constexpr int LD = D + 1;
-  for (int f = tid; f < 64 * D / 4; f += 128) {
+  for (int f = tid; f < 128 * D / 4; f += 256) {
     const int r = f / (D / 4), c4 = f % (D / 4);
     const int t = row0 + r;
     f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
@@ -240,16 +288,23 @@ __device__ __forceinline__ void rotate_back(f32x16 (&g)[D / 32], int pos, const 
   }
 }
 
-// Forward attention of one (sequence, query head) and 64 queries, keeping the
-// log-sum-exp (base 2) of every query's scores for the backward. Two waves, 32
-// queries each; keys in blocks of 64 through LDS.
+// The three attention kernels share one work split: a workgroup of 4 waves owns 64
+// rows (queries, or keys for dK/dV) of one (sequence, query head), blockIdx.x the
+// (sequence, head) and blockIdx.y the row block (the heaviest first); wave w takes the
+// 32 rows of group w & 1 and the blocks of 64 columns (keys, or queries) of parity
+// w >> 1, two blocks staged in LDS per round. The two parities' partial results meet
+// in LDS at the end and are combined in a fixed order.
+
+// Forward attention, keeping the log-sum-exp (base 2) of every query's scores for
+// the backward.
 template <int D>
-__global__ __launch_bounds__(128) void bw_attn_fwd_kernel(const BwAttn a) {
-  constexpr int LD = D + 1, HD = D / 2, NT = D / 32;
-  __shared__ float Ks[64 * LD], Vs[64 * LD];
+__global__ __launch_bounds__(256) void bw_attn_fwd_kernel(const BwAttn a) {
+  constexpr int LD = D + 1, HD = D / 2, NT = D / 32, CS = NT * 16 + 2;
+  __shared__ float Ks[128 * LD], Vs[128 * LD];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
-  const int qb = blockIdx.x, b = blockIdx.y / a.nq, hd = blockIdx.y % a.nq, g = hd / a.G;
-  const int tq = qb * 64 + w * 32 + l32;
+  const int rg = w & 1, par = w >> 1;
+  const int qb = gridDim.y - 1 - blockIdx.y, b = blockIdx.x / a.nq, hd = blockIdx.x % a.nq, g = hd / a.G;
+  const int tq = qb * 64 + rg * 32 + l32;
   const bool qok = tq < a.T;
   const size_t rowq = (size_t)b * a.T + min(tq, a.T - 1);
   float qreg[HD];
@@ -262,14 +317,17 @@ __global__ __launch_bounds__(128) void bw_attn_fwd_kernel(const BwAttn a) {
   float m_run = NEG_INF, l_run = 0.f;
   const int kb_hi = min(qb * 64 + 63, a.T - 1) / 64;
   const int kb_lo = a.window > 0 ? max(0, qb * 64 - a.window + 1) / 64 : 0;
-  for (int kb = kb_lo; kb <= kb_hi; ++kb) {
+  for (int kb0 = kb_lo; kb0 <= kb_hi; kb0 += 2) {
     __syncthreads();
-    stage_rows2<D>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb * 64, tid);
+    stage_rows2<D>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb0 * 64, tid);
     __syncthreads();
+    const int kb = kb0 + par;
+    if (kb > kb_hi) continue;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      const int r0 = par * 64 + c * 32;  // LDS row of this 32-key sub-block
       f32x16 st = {};
-      const float *kr = Ks + (c * 32 + l32) * LD + hl * HD;
+      const float *kr = Ks + (r0 + l32) * LD + hl * HD;
 #pragma unroll
       for (int s = 0; s < HD; ++s) st = mfma2(kr[s], qreg[s], st);
       float p[16], mx = NEG_INF;
@@ -297,30 +355,47 @@ __global__ __launch_bounds__(128) void bw_attn_fwd_kernel(const BwAttn a) {
         oacc[t] *= f;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          oacc[t] = mfma2(Vs[(c * 32 + acc_row(j, lane)) * LD + t * 32 + l32], p[j], oacc[t]);
+          oacc[t] = mfma2(Vs[(r0 + acc_row(j, lane)) * LD + t * 32 + l32], p[j], oacc[t]);
       }
     }
   }
-  if (!qok) return;
-  const float inv = 1.0f / l_run;  // a query with no visible key: 0 / 0, NaN
+  // parity 1 hands (O, m, l) to parity 0 of the same row group
+  __syncthreads();
+  float *xch = Ks + (rg * 64 + lane) * CS;
+  if (par == 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[t * 16 + r] = oacc[t][r];
+    xch[NT * 16] = m_run;
+    xch[NT * 16 + 1] = l_run;
+  }
+  __syncthreads();
+  if (par == 1 || !qok) return;
+  const float m2 = xch[NT * 16], l2 = xch[NT * 16 + 1];
+  const float mm = fmaxf(m_run, m2), mu = mm == NEG_INF ? 0.f : mm;
+  const float f1 = exp2f(m_run - mu), f2 = exp2f(m2 - mu);
+  const float l = l_run * f1 + l2 * f2;
+  const float inv = 1.0f / l;  // a query with no visible key: 0 / 0, NaN
   float *orow = a.o + rowq * (size_t)(a.nq * D) + hd * D;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) orow[t * 32 + acc_row(r, lane)] = oacc[t][r] * inv;
-  if (hl == 0) a.lse[((size_t)b * a.nq + hd) * a.T + tq] = m_run + log2f(l_run);
+    for (int r = 0; r < 16; ++r) orow[t * 32 + acc_row(r, lane)] = (oacc[t][r] * f1 + xch[t * 16 + r] * f2) * inv;
+  if (hl == 0) a.lse[((size_t)b * a.nq + hd) * a.T + tq] = mm + log2f(l);
 }
 
-// dQ of one (sequence, query head) and 64 queries: for every visible key block,
-// P = exp2(S log2(e)/sqrt(d) - lse), dS = P (dO V^T - rowsum(dO O)), dQ += dS K.
-// Then dQ / sqrt(d) is rotated back (on a rotary block) into dqkv.
+// dQ: for every visible key block, P = exp2(S log2(e)/sqrt(d) - lse),
+// dS = P (dO V^T - rowsum(dO O)), dQ += dS K; then dQ / sqrt(d), rotated back on a
+// rotary block, into dqkv.
 template <int D>
-__global__ __launch_bounds__(128) void bw_attn_dq_kernel(const BwAttn a) {
-  constexpr int LD = D + 1, HD = D / 2, NT = D / 32;
-  __shared__ float Ks[64 * LD], Vs[64 * LD];
+__global__ __launch_bounds__(256) void bw_attn_dq_kernel(const BwAttn a) {
+  constexpr int LD = D + 1, HD = D / 2, NT = D / 32, CS = NT * 16;
+  __shared__ float Ks[128 * LD], Vs[128 * LD];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
-  const int qb = blockIdx.x, b = blockIdx.y / a.nq, hd = blockIdx.y % a.nq, g = hd / a.G;
-  const int tq = qb * 64 + w * 32 + l32;
+  const int rg = w & 1, par = w >> 1;
+  const int qb = gridDim.y - 1 - blockIdx.y, b = blockIdx.x / a.nq, hd = blockIdx.x % a.nq, g = hd / a.G;
+  const int tq = qb * 64 + rg * 32 + l32;
   const bool qok = tq < a.T;
   const size_t rowq = (size_t)b * a.T + min(tq, a.T - 1);
   float qreg[HD], doreg[HD];
@@ -335,15 +410,18 @@ __global__ __launch_bounds__(128) void bw_attn_dq_kernel(const BwAttn a) {
   for (int t = 0; t < NT; ++t) dq[t] = (f32x16){};
   const int kb_hi = min(qb * 64 + 63, a.T - 1) / 64;
   const int kb_lo = a.window > 0 ? max(0, qb * 64 - a.window + 1) / 64 : 0;
-  for (int kb = kb_lo; kb <= kb_hi; ++kb) {
+  for (int kb0 = kb_lo; kb0 <= kb_hi; kb0 += 2) {
     __syncthreads();
-    stage_rows2<D>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb * 64, tid);
+    stage_rows2<D>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb0 * 64, tid);
     __syncthreads();
+    const int kb = kb0 + par;
+    if (kb > kb_hi) continue;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      const int r0 = par * 64 + c * 32;
       f32x16 st = {}, dp = {};
-      const float *kr = Ks + (c * 32 + l32) * LD + hl * HD;
-      const float *vr = Vs + (c * 32 + l32) * LD + hl * HD;
+      const float *kr = Ks + (r0 + l32) * LD + hl * HD;
+      const float *vr = Vs + (r0 + l32) * LD + hl * HD;
 #pragma unroll
       for (int s = 0; s < HD; ++s) {
         st = mfma2(kr[s], qreg[s], st);
@@ -360,12 +438,23 @@ __global__ __launch_bounds__(128) void bw_attn_dq_kernel(const BwAttn a) {
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          dq[t] = mfma2(Ks[(c * 32 + acc_row(j, lane)) * LD + t * 32 + l32], ds[j], dq[t]);
+          dq[t] = mfma2(Ks[(r0 + acc_row(j, lane)) * LD + t * 32 + l32], ds[j], dq[t]);
     }
   }
-  if (!qok) return;
+  __syncthreads();
+  float *xch = Ks + (rg * 64 + lane) * CS;
+  if (par == 1) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) dq[t] *= a.scale;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[t * 16 + r] = dq[t][r];
+  }
+  __syncthreads();
+  if (par == 1 || !qok) return;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[t][r] = (dq[t][r] + xch[t * 16 + r]) * a.scale;
   if (a.rope_on) rotate_back<D>(dq, a.pos0 + tq, a.inv_freq, lane);
   float *out = a.dqkv + rowq * a.ld + hd * D;
 #pragma unroll
@@ -374,17 +463,18 @@ __global__ __launch_bounds__(128) void bw_attn_dq_kernel(const BwAttn a) {
     for (int r = 0; r < 16; ++r) out[t * 32 + acc_row(r, lane)] = dq[t][r];
 }
 
-// dK and dV of one (sequence, query head) and 64 keys, over every query block
-// that can see them: dV += P^T dO, dK += dS^T Q / sqrt(d). Written as this query
-// head's partial (rotated back on a rotary block); bw_kv_reduce_kernel sums the
-// partials of the query heads that share a kv head.
+// dK and dV of 64 keys over every query block that can see them: dV += P^T dO,
+// dK += dS^T Q / sqrt(d). Written as this query head's partial (rotated back on a
+// rotary block); bw_kv_reduce_kernel sums the partials of the query heads that
+// share a kv head.
 template <int D>
-__global__ __launch_bounds__(128) void bw_attn_dkdv_kernel(const BwAttn a) {
-  constexpr int LD = D + 1, HD = D / 2, NT = D / 32;
-  __shared__ float Qs[64 * LD], Os[64 * LD], Ls[64], Ds[64];
+__global__ __launch_bounds__(256) void bw_attn_dkdv_kernel(const BwAttn a) {
+  constexpr int LD = D + 1, HD = D / 2, NT = D / 32, CS = 2 * NT * 16, UC = D == 64 ? 2 : 1;
+  __shared__ float Qs[128 * LD], Os[128 * LD], Ls[128], Ds[128];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
-  const int kb = blockIdx.x, b = blockIdx.y / a.nq, hd = blockIdx.y % a.nq, g = hd / a.G;
-  const int tk = kb * 64 + w * 32 + l32;
+  const int kg = w & 1, par = w >> 1;
+  const int kb = blockIdx.y, b = blockIdx.x / a.nq, hd = blockIdx.x % a.nq, g = hd / a.G;
+  const int tk = kb * 64 + kg * 32 + l32;
   const bool kok = tk < a.T;
   const size_t rowk = (size_t)b * a.T + min(tk, a.T - 1);
   float kreg[HD], vreg[HD];
@@ -396,20 +486,24 @@ __global__ __launch_bounds__(128) void bw_attn_dkdv_kernel(const BwAttn a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) dk[t] = dv[t] = (f32x16){};
   const int q_last = a.window > 0 ? min(a.T - 1, kb * 64 + 63 + a.window - 1) : a.T - 1;
-  for (int qb = kb; qb <= q_last / 64; ++qb) {
+  const int qb_hi = q_last / 64;
+  for (int qb0 = kb; qb0 <= qb_hi; qb0 += 2) {
     __syncthreads();
-    stage_rows2<D>(Qs, Os, a.qkv + hd * D, a.dO + hd * D, a.ld, a.nq * D, b, a.T, qb * 64, tid);
-    if (tid < 64) {
-      const int t = qb * 64 + tid;
+    stage_rows2<D>(Qs, Os, a.qkv + hd * D, a.dO + hd * D, a.ld, a.nq * D, b, a.T, qb0 * 64, tid);
+    if (tid < 128) {
+      const int t = qb0 * 64 + tid;
       Ls[tid] = t < a.T ? a.lse[stat0 + t] : 0.f;
       Ds[tid] = t < a.T ? a.dsum[stat0 + t] : 0.f;
     }
     __syncthreads();
-#pragma unroll
+    const int qb = qb0 + par;
+    if (qb > qb_hi) continue;
+#pragma unroll UC  // (head dim 128: one sub-block at a time, or the registers spill)
     for (int c = 0; c < 2; ++c) {
+      const int r0 = par * 64 + c * 32;  // LDS row of this 32-query sub-block
       f32x16 st = {}, dp = {};
-      const float *qr = Qs + (c * 32 + l32) * LD + hl * HD;
-      const float *orow = Os + (c * 32 + l32) * LD + hl * HD;
+      const float *qr = Qs + (r0 + l32) * LD + hl * HD;
+      const float *orow = Os + (r0 + l32) * LD + hl * HD;
 #pragma unroll
       for (int s = 0; s < HD; ++s) {
         st = mfma2(qr[s], kreg[s], st);
@@ -418,8 +512,8 @@ __global__ __launch_bounds__(128) void bw_attn_dkdv_kernel(const BwAttn a) {
       float pr[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qi = c * 32 + acc_row(r, lane);
-        const int tq = qb * 64 + qi;
+        const int qi = r0 + acc_row(r, lane);
+        const int tq = qb0 * 64 + qi;
         pr[r] = (kok && visible(a, b, tq, tk)) ? exp2f(st[r] * a.scale2 - Ls[qi]) : 0.f;
         ds[r] = pr[r] * (dp[r] - Ds[qi]);
       }
@@ -427,15 +521,32 @@ __global__ __launch_bounds__(128) void bw_attn_dkdv_kernel(const BwAttn a) {
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int qi = c * 32 + acc_row(j, lane);
+          const int qi = r0 + acc_row(j, lane);
           dv[t] = mfma2(Os[qi * LD + t * 32 + l32], pr[j], dv[t]);
           dk[t] = mfma2(Qs[qi * LD + t * 32 + l32], ds[j], dk[t]);
         }
     }
   }
-  if (!kok) return;
+  __syncthreads();
+  float *xch = Qs + (kg * 64 + lane) * CS;
+  if (par == 1) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) dk[t] *= a.scale;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        xch[t * 16 + r] = dk[t][r];
+        xch[(NT + t) * 16 + r] = dv[t][r];
+      }
+  }
+  __syncthreads();
+  if (par == 1 || !kok) return;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[t][r] = (dk[t][r] + xch[t * 16 + r]) * a.scale;
+      dv[t][r] += xch[(NT + t) * 16 + r];
+    }
   if (a.rope_on) rotate_back<D>(dk, a.pos0 + tk, a.inv_freq, lane);
   const size_t M = (size_t)a.B * a.T;
   float *pk = a.part + ((size_t)hd * M + rowk) * D;
@@ -522,14 +633,17 @@ __global__ __launch_bounds__(256) void bw_rms_fwd_kernel(const float *x, const f
 
 // RMSNorm backward for u = w * n, n = x * r: with dn = du * w,
 //   dx = resid + r * (dn - n * mean(dn * n))
-// (resid: the gradient that reaches x around the sublayer), and each wave's column
-// partial sum of du * n over its rows (the weight gradient before the final sum).
-// 16 rows per workgroup, 4 per wave; NC = 16-byte columns per lane (H <= 256 NC).
+// (resid: the gradient that reaches x around the sublayer), and the workgroup's
+// column sums of du * n over its rows (the weight gradient before the final sum):
+// each wave sums its rows, waves 1-3 hand theirs to wave 0 through LDS, which adds
+// them in wave order. 16 rows per workgroup, 4 per wave; NC = 16-byte columns per
+// lane (H <= 256 NC).
 constexpr int RMS_ROWS = 16;
 template <int NC>
 __global__ __launch_bounds__(256) void bw_rms_bwd_kernel(const float *du, const float *x, const float *r,
                                                          const float *w, const float *resid, float *dx, float *part,
                                                          int M, int H) {
+  __shared__ f32x4 red[3][NC * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   f32x4 colacc[NC];
 #pragma unroll
@@ -564,27 +678,38 @@ __global__ __launch_bounds__(256) void bw_rms_bwd_kernel(const float *du, const 
       }
     }
   }
-  float *pr = part + ((size_t)blockIdx.x * 4 + wave) * H;
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) red[wave - 1][lane + 64 * j] = colacc[j];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  float *pr = part + (size_t)blockIdx.x * H;
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const int c = (lane + 64 * j) * 4;
-    if (c < H) *reinterpret_cast<f32x4 *>(pr + c) = colacc[j];
+    if (c < H)
+      *reinterpret_cast<f32x4 *>(pr + c) =
+          ((colacc[j] + red[0][lane + 64 * j]) + red[1][lane + 64 * j]) + red[2][lane + 64 * j];
   }
 }
 
-// dw[c] (+)= sum over the partial rows, in row order. 64 columns per workgroup; the
-// 4 waves take every 4th partial row and their sums are added in wave order.
-__global__ __launch_bounds__(256) void bw_colsum_kernel(const float *part, int nrows, int H, float *dw, int accumulate) {
-  __shared__ float red[4][64];
+// dw[c] (+)= sum over the partial rows. 64 columns per workgroup of 16 waves; wave
+// v sums rows v, v + 16, ... and the 16 wave sums are added in wave order.
+__global__ __launch_bounds__(1024) void bw_colsum_kernel(const float *part, int nrows, int H, float *dw,
+                                                         int accumulate) {
+  __shared__ float red[16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lane;
   float s = 0.f;
   if (c < H)
-    for (int i = wave; i < nrows; i += 4) s += part[(size_t)i * H + c];
+    for (int i = wave; i < nrows; i += 16) s += part[(size_t)i * H + c];
   red[wave][lane] = s;
   __syncthreads();
   if (wave == 0 && c < H) {
-    const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    float t = red[0][lane];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) t += red[v][lane];
     dw[c] = accumulate ? dw[c] + t : t;
   }
 }
@@ -593,8 +718,27 @@ __global__ __launch_bounds__(256) void bw_colsum_kernel(const float *part, int n
 
 // ------------------------------------------------------------------ launchers
 
+// Few tiles and a long K (weight gradients contract over all B*T tokens): split K
+// until about 1024 workgroups run, at most 8 ways and at least 4 stages (128 of K)
+// per split. Not for the SwiGLU epilogue, which needs the whole sum at once.
+int bw_gemm_ksplit(int M, int N, int K, int epi) {
+  if (epi == BW_SWIGLU) return 1;
+  const int tiles = ((M + GT - 1) / GT) * ((N + GT - 1) / GT);
+  const int stages = (K + GK - 1) / GK;
+  int ks = std::min(8, 1024 / std::max(tiles, 1));
+  ks = std::min(ks, stages / 4);
+  return std::max(ks, 1);
+}
+
+size_t bw_gemm_part_floats(int M, int N, int K, int epi) {
+  const int ks = bw_gemm_ksplit(M, N, K, epi);
+  return ks > 1 ? (size_t)ks * M * N : 0;
+}
+
 hipError_t bw_gemm(int layout, int epi, const BwGemm &p, hipStream_t s) {
   if (p.M < 1 || p.N < 1 || p.K < 1) return hipErrorInvalidValue;
+  if (p.ksplit > 1 && (p.part == nullptr || p.N % 4 || epi == BW_SWIGLU || p.ldc % 4 || (epi == BW_RESID && p.ldr % 4)))
+    return hipErrorInvalidValue;
   const bool ak = layout == BW_NT || layout == BW_NN, bk = layout == BW_NT;
   // 16-byte loads: the contiguous extent of each operand and its row length must be
   // multiples of 4 floats
@@ -616,16 +760,18 @@ hipError_t bw_gemm(int layout, int epi, const BwGemm &p, hipStream_t s) {
 }
 
 hipError_t bw_attention(int which, const BwAttn &a, hipStream_t s) {
-  const dim3 grid((a.T + 63) / 64, a.B * a.nq);
+  // blocks of 64 rows along y, dispatched after x: the causally heaviest blocks (last
+  // queries; first keys) first, so a second round of workgroups holds the lightest
+  const dim3 grid(a.B * a.nq, (a.T + 63) / 64);
   if (a.D == 64) {
-    if (which == 0) return launch(bw_attn_fwd_kernel<64>, grid, dim3(128), s, a);
-    if (which == 1) return launch(bw_attn_dq_kernel<64>, grid, dim3(128), s, a);
-    return launch(bw_attn_dkdv_kernel<64>, grid, dim3(128), s, a);
+    if (which == 0) return launch(bw_attn_fwd_kernel<64>, grid, dim3(256), s, a);
+    if (which == 1) return launch(bw_attn_dq_kernel<64>, grid, dim3(256), s, a);
+    return launch(bw_attn_dkdv_kernel<64>, grid, dim3(256), s, a);
   }
   if (a.D == 128) {
-    if (which == 0) return launch(bw_attn_fwd_kernel<128>, grid, dim3(128), s, a);
-    if (which == 1) return launch(bw_attn_dq_kernel<128>, grid, dim3(128), s, a);
-    return launch(bw_attn_dkdv_kernel<128>, grid, dim3(128), s, a);
+    if (which == 0) return launch(bw_attn_fwd_kernel<128>, grid, dim3(256), s, a);
+    if (which == 1) return launch(bw_attn_dq_kernel<128>, grid, dim3(256), s, a);
+    return launch(bw_attn_dkdv_kernel<128>, grid, dim3(256), s, a);
   }
   return hipErrorInvalidValue;
 }
@@ -649,7 +795,7 @@ hipError_t bw_rms_fwd(const float *x, const float *w, float *u, float *r, int M,
   return launch(bw_rms_fwd_kernel, dim3((M + 3) / 4), dim3(256), s, x, w, u, r, M, H, eps);
 }
 
-int bw_rms_part_rows(int M) { return (M + RMS_ROWS - 1) / RMS_ROWS * 4; }
+int bw_rms_part_rows(int M) { return (M + RMS_ROWS - 1) / RMS_ROWS; }
 
 hipError_t bw_rms_bwd(const float *du, const float *x, const float *r, const float *w, const float *resid, float *dx,
                       float *part, int M, int H, hipStream_t s) {
@@ -665,7 +811,7 @@ hipError_t bw_rms_bwd(const float *du, const float *x, const float *r, const flo
 }
 
 hipError_t bw_colsum(const float *part, int nrows, int H, float *dw, int accumulate, hipStream_t s) {
-  return launch(bw_colsum_kernel, dim3((H + 63) / 64), dim3(256), s, part, nrows, H, dw, accumulate);
+  return launch(bw_colsum_kernel, dim3((H + 63) / 64), dim3(1024), s, part, nrows, H, dw, accumulate);
 }
 
 }  // namespace smol

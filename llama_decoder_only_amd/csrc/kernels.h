@@ -142,19 +142,30 @@ struct BwOperand {
 // Y[m, n] = silu(g) u.
 enum { BW_NT = 0, BW_NN = 1, BW_TN = 2 };
 enum { BW_STORE = 0, BW_ACCUM = 1, BW_RESID = 2, BW_SWIGLU = 3 };
+// C rows [0, cseg0) go to C, [cseg0, cseg1) to C1, the rest to C2 (e.g. the three
+// gradients dW_q | dW_k | dW_v of one fused launch); all with row length ldc.
+// ksplit > 1: K is cut into ksplit ranges whose workgroups write unscaled partial
+// tiles to part ([ksplit, M, N] floats); a second kernel adds them in split order
+// and applies the epilogue (store, add or residual only).
 struct BwGemm {
   BwOperand a, b;
   int M, N, K;
-  float *C;
-  int ldc;
+  float *C, *C1, *C2;
+  int cseg0, cseg1, ldc;
   const float *R;
   int ldr;
   const float *G;
   int ldg, half;
   float *Y;
   int ldy;
+  int ksplit;
+  float *part;
 };
 hipError_t bw_gemm(int layout, int epi, const BwGemm &p, hipStream_t s);
+// The K split bw_gemm would take for this shape and epilogue (1: none), and the
+// partial-sum floats it then needs.
+int bw_gemm_ksplit(int M, int N, int K, int epi);
+size_t bw_gemm_part_floats(int M, int N, int K, int epi);
 
 struct InvFreq {
   float v[64];

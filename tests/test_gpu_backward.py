@@ -107,7 +107,7 @@ def test_backward_full_shape():
 
 
 def test_backward_accumulate_and_determinism():
-    s = S.workload("block_backward_f32", batch=2, seq=70)
+    s = S.workload("block_backward_f32", batch=2, seq=300)  # 600 tokens: the weight gradients split K
     say("backward accumulate + determinism")
     got, (lw, x, dy, w, xt, dyt, g) = _run(s)
     first = {n: t.clone() for n, t in g.as_dict().items()}
