@@ -253,6 +253,58 @@ def test_long_block_bf16_sampled_rows():
     assert r <= TOL_BF16
 
 
+def test_smollm3_block_full_size_sampled_rows():
+    """One block of the SmolLM3-3B-shaped prefill at its full size (bf16, batch 2 x seq 4096, H
+    2048, 16/4 heads x 128, I 11008): 24 sampled rows of each sequence (first and last key tiles
+    among them) against the oracle's own steps."""
+    s = S.workload("smollm3_prefill_bf16", n_layers=1, norm_jitter=0.1)
+    say("SmolLM3-shaped block bf16 B=2 T=4096 sampled rows")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.f64))
+    rows = np.unique(np.concatenate([[0, 127, 128, 2047, 4094, 4095], np.random.default_rng(5).integers(0, 4096, 18)]))
+    for b in range(2):
+        want = block_rows_oracle(x.f64[b], olayer(layer), ocfg(s), rows)
+        r = rel(got[b, rows], want)
+        say(f"sequence {b}: rel = {r:.3e}")
+        assert r <= TOL_BF16
+
+
+def test_smollm3_prefill_full_size_properties():
+    """The whole SmolLM3-3B-shaped prefill (36 layers, batch 2 x seq 4096, vocab 128256) with
+    weights drawn on the GPU from a seeded generator (N(0, 0.02^2), unit norms): finite logits;
+    two runs bit-identical; changing tokens after position 3000 of sequence 0 leaves its rows
+    <= 3000 and all of sequence 1 bit-identical (causality, batch independence)."""
+    s = S.workload("smollm3_prefill_bf16")
+    say("SmolLM3-shaped prefill bf16 36 layers B=2 T=4096")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+
+    def normal(*shape):
+        return (torch.randn(*shape, generator=gen, device=DEV, dtype=torch.float32) * s.std).to(torch.bfloat16)
+
+    H, I, d = s.hidden, s.intermediate, s.head_dim
+    ones = torch.ones(H, dtype=torch.bfloat16, device=DEV)
+    layers = [B.LayerWeights([ones, normal(s.n_heads * d, H), normal(s.n_kv_heads * d, H), normal(s.n_kv_heads * d, H),
+                              normal(H, s.n_heads * d), ones, normal(I, H), normal(I, H), normal(H, I)])
+              for _ in range(s.n_layers)]
+    md = B.ModelWeights(normal(s.vocab, H), layers, ones)
+    ids_np = S.token_ids(s, 0)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    a = _prefill(s, md, ids)
+    assert torch.isfinite(a.float()).all()
+    b = _prefill(s, md, ids)
+    assert torch.equal(a, b), "prefill is not deterministic"
+    del b
+    ids2 = ids.clone()
+    ids2[0, 3001:] = (ids2[0, 3001:] + 11) % s.vocab
+    c = _prefill(s, md, ids2)
+    assert torch.equal(a[0, :3001], c[0, :3001]), "rows before the perturbation changed"
+    assert torch.equal(a[1], c[1]), "the other sequence changed"
+    assert not torch.equal(a[0, 3001:], c[0, 3001:])
+    del a, c
+
+
 # ------------------------------------------------------------------ decode
 
 
