@@ -190,7 +190,7 @@ struct LayerCtx {
   const int *cache_len;  // decode only
   const uint8_t *key_mask;  // [B, mask_ld] over key indices, or nullptr
   int mask_ld;
-  float inv_freq[64];
+  double inv_freq[64];
   hipStream_t s;
 };
 
@@ -242,9 +242,9 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, 
   return SMOL_OK;
 }
 
-void fill_inv_freq(const Dims &D, float *f) {
-  // omega_i = theta^(-2i/d) (abi96062 components.py, RotaryEmbedding), in double, rounded once
-  for (int i = 0; i < D.d / 2; ++i) f[i] = (float)std::pow((double)D.theta, -2.0 * i / D.d);
+void fill_inv_freq(const Dims &D, double *f) {
+  // omega_i = theta^(-2i/d) (abi96062 components.py, RotaryEmbedding), in double
+  for (int i = 0; i < D.d / 2; ++i) f[i] = std::pow((double)D.theta, -2.0 * i / D.d);
 }
 
 smol_status check_ws(const Dims &D, int op, int B, int T, void *ws, size_t ws_bytes, Ws *lay) {
@@ -450,7 +450,7 @@ smol_status check_model(const Dims &D, const smol_model_weights *w) {
 // smol_block_backward: the forward recomputed with its activations kept, then the
 // chain rule in reverse (backward.hip). M = B*T rows; C3 = (nq + 2 nkv) d.
 struct BwWs {
-  size_t u, r1, qkv, o, lse, h, wn, r2, gu, dgu, y, dwn, dh, dO, dsum, dqkv, part, du, npart, gpart, total;
+  size_t u, r1, qkv, o, lse, h, wn, r2, gu, dgu, y, dwn, dh, dO, dsum, dqkv, part, du, npart, gpart, rope, total;
 };
 
 // The GEMMs of one block backward: (M, N, K, epilogue) of each launch, in order.
@@ -492,6 +492,7 @@ BwWs bw_layout(const Dims &D, int B, int T) {
   size_t gp = 0;
   for (const BwShape &g : bw_shapes(D, (int)M)) gp = std::max(gp, smol::bw_gemm_part_floats(g.M, g.N, g.K, g.epi));
   w.gpart = take(std::max<size_t>(gp, 1));
+  w.rope = take(M * (D.d / 2) * 2);  // (cos, sin) per row and frequency
   w.total = off;
   return w;
 }
@@ -554,9 +555,13 @@ smol_status backward_impl(const Dims &D, const smol_layer_weights *w, int layer,
   SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rms_fwd(x, an, u, r1, M, H, D.eps, s));
   SMOL_LAUNCH(SMOL_K_BW_GEMM, gemm(BW_NT, BW_STORE, gemm_args(operand(u, H), operand(Wq, H, Wk, QD, Wv, QD + KD),
                                                               M, C3, H, qkv, C3)));
-  smol::InvFreq inv{};
-  fill_inv_freq(D, inv.v);
-  if (rope_on) SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rope(qkv, M, T, C3, D.nq + D.nkv, d, pos0, inv, s));
+  float2 *rope_cs = (float2 *)F(L.rope);
+  if (rope_on) {
+    smol::InvFreq inv{};
+    fill_inv_freq(D, inv.v);
+    SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rope_table(rope_cs, M, T, d, pos0, inv, s));
+    SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_rope(qkv, M, C3, D.nq + D.nkv, d, rope_cs, s));
+  }
   smol::BwAttn at{};
   at.qkv = qkv;
   at.ld = C3;
@@ -577,8 +582,7 @@ smol_status backward_impl(const Dims &D, const smol_layer_weights *w, int layer,
   at.dqkv = dqkv;
   at.part = F(L.part);
   at.rope_on = rope_on ? 1 : 0;
-  at.pos0 = pos0;
-  for (int i = 0; i < 64; ++i) at.inv_freq[i] = inv.v[i];
+  at.rope_cs = rope_cs;
   SMOL_LAUNCH(SMOL_K_BW_ATTN_FWD, smol::bw_attention(0, at, s));
   {  // h = x + o W_o^T
     smol::BwGemm g = gemm_args(operand(o, QD), operand(Wo, QD), M, H, QD, h, H);

@@ -269,21 +269,20 @@ __device__ __forceinline__ void load_half_row(float (&v)[D / 2], const float *ro
 }
 
 // Inverse RoPE of a gradient held as 32 x 32 accumulator tiles over d (tile t holds
-// d = 32 t + acc_row(r, lane)): the rotation at `pos` is orthogonal, so its
-// transpose (the rotation by -angle) carries the gradient back to the projection.
+// d = 32 t + acc_row(r, lane)): the rotation at the row's position is orthogonal, so
+// its transpose (the rotation by -angle) carries the gradient back to the
+// projection. cs: the row's (cos, sin) per frequency.
 template <int D>
-__device__ __forceinline__ void rotate_back(f32x16 (&g)[D / 32], int pos, const float *inv_freq, int lane) {
+__device__ __forceinline__ void rotate_back(f32x16 (&g)[D / 32], const float2 *cs, int lane) {
   constexpr int TH = D / 64;  // tiles per half: pair (i, i + D/2) sits in tiles t, t + TH
 #pragma unroll
   for (int t = 0; t < TH; ++t) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int i = t * 32 + acc_row(r, lane);
-      float sn, cs;
-      sincosf((float)pos * inv_freq[i], &sn, &cs);
+      const float2 c = cs[t * 32 + acc_row(r, lane)];
       const float x = g[t][r], y = g[t + TH][r];
-      g[t][r] = x * cs + y * sn;
-      g[t + TH][r] = y * cs - x * sn;
+      g[t][r] = x * c.x + y * c.y;
+      g[t + TH][r] = y * c.x - x * c.y;
     }
   }
 }
@@ -455,7 +454,7 @@ __global__ __launch_bounds__(256) void bw_attn_dq_kernel(const BwAttn a) {
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[t][r] = (dq[t][r] + xch[t * 16 + r]) * a.scale;
-  if (a.rope_on) rotate_back<D>(dq, a.pos0 + tq, a.inv_freq, lane);
+  if (a.rope_on) rotate_back<D>(dq, a.rope_cs + rowq * (D / 2), lane);
   float *out = a.dqkv + rowq * a.ld + hd * D;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -547,7 +546,7 @@ __global__ __launch_bounds__(256) void bw_attn_dkdv_kernel(const BwAttn a) {
       dk[t][r] = (dk[t][r] + xch[t * 16 + r]) * a.scale;
       dv[t][r] += xch[(NT + t) * 16 + r];
     }
-  if (a.rope_on) rotate_back<D>(dk, a.pos0 + tk, a.inv_freq, lane);
+  if (a.rope_on) rotate_back<D>(dk, a.rope_cs + rowk * (D / 2), lane);
   const size_t M = (size_t)a.B * a.T;
   float *pk = a.part + ((size_t)hd * M + rowk) * D;
   float *pv = a.part + ((size_t)(a.nq + hd) * M + rowk) * D;
@@ -592,21 +591,32 @@ __global__ __launch_bounds__(256) void bw_kv_reduce_kernel(const float *part, fl
   *reinterpret_cast<f32x4 *>(dqkv + (size_t)m * ld + (nq + which * nkv + g) * D + e) = s;
 }
 
-// RoPE on the q and k columns of qkv, in place: pair (i, i + D/2) of every head
-// rotated by (pos0 + t) * inv_freq[i] (Sualeh77 model.py, "3. RoPE").
-__global__ __launch_bounds__(256) void bw_rope_kernel(float *qkv, int M, int T, int ld, int heads, int D, int pos0,
-                                                      const InvFreq f) {
+// The RoPE table of the call: cs[m * D/2 + i] = (cos, sin) of (pos0 + m % T) * omega_i,
+// the angle formed and evaluated in double (a float32 product is off by up to
+// 1.4e-4 rad at position 8191) and rounded once to float.
+__global__ __launch_bounds__(256) void bw_rope_table_kernel(float2 *cs, int M, int T, int half, int pos0,
+                                                            const InvFreq f) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * half) return;
+  const int m = i / half, j = i % half;
+  double sn, c;
+  sincos((double)(pos0 + m % T) * f.v[j], &sn, &c);
+  cs[i] = make_float2((float)c, (float)sn);
+}
+
+// RoPE on the q and k columns of qkv, in place: pair (j, j + D/2) of every head
+// rotated by the row's angle j (Sualeh77 model.py, "3. RoPE").
+__global__ __launch_bounds__(256) void bw_rope_kernel(float *qkv, int M, int ld, int heads, int D, const float2 *cs) {
   const int half = D / 2;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= M * heads * half) return;
   const int m = i / (heads * half), rest = i % (heads * half);
   const int h = rest / half, j = rest % half;
-  float sn, cs;
-  sincosf((float)(pos0 + m % T) * f.v[j], &sn, &cs);
+  const float2 c = cs[(size_t)m * half + j];
   float *z = qkv + (size_t)m * ld + h * D;
   const float x = z[j], y = z[j + half];
-  z[j] = x * cs - y * sn;
-  z[j + half] = y * cs + x * sn;
+  z[j] = x * c.x - y * c.y;
+  z[j + half] = y * c.x + x * c.y;
 }
 
 // u = w * x * r, r = 1 / sqrt(mean(x^2) + eps) per row (abi96062 components.py,
@@ -785,9 +795,15 @@ hipError_t bw_kv_reduce(const float *part, float *dqkv, int M, int nq, int nkv, 
   return launch(bw_kv_reduce_kernel, dim3((n + 255) / 256), dim3(256), s, part, dqkv, M, nq, nkv, G, D, ld);
 }
 
-hipError_t bw_rope(float *qkv, int M, int T, int ld, int heads, int D, int pos0, const InvFreq &f, hipStream_t s) {
+hipError_t bw_rope_table(float2 *cs, int M, int T, int D, int pos0, const InvFreq &f, hipStream_t s) {
+  if (D / 2 > 64) return hipErrorInvalidValue;
+  const int n = M * (D / 2);
+  return launch(bw_rope_table_kernel, dim3((n + 255) / 256), dim3(256), s, cs, M, T, D / 2, pos0, f);
+}
+
+hipError_t bw_rope(float *qkv, int M, int ld, int heads, int D, const float2 *cs, hipStream_t s) {
   const int n = M * heads * (D / 2);
-  return launch(bw_rope_kernel, dim3((n + 255) / 256), dim3(256), s, qkv, M, T, ld, heads, D, pos0, f);
+  return launch(bw_rope_kernel, dim3((n + 255) / 256), dim3(256), s, qkv, M, ld, heads, D, cs);
 }
 
 hipError_t bw_rms_fwd(const float *x, const float *w, float *u, float *r, int M, int H, float eps, hipStream_t s) {

@@ -71,7 +71,7 @@ struct RopeIn {
   float2 *cs;  // nullptr: none
   int half, pos0, seq;
   const int *cache_len;
-  float inv_freq[64];
+  double inv_freq[64];  // omega_i in double: the angle is formed and reduced in double
 };
 template <typename T>
 hipError_t rows_ss(const int32_t *ids, const T *E, const float *src, float *x, float *ss_new, float *ss_old,
@@ -168,7 +168,7 @@ int bw_gemm_ksplit(int M, int N, int K, int epi);
 size_t bw_gemm_part_floats(int M, int N, int K, int epi);
 
 struct InvFreq {
-  float v[64];
+  double v[64];
 };
 // Attention of the block being differentiated: qkv [B*T, ld] holds q | k | v (q and
 // k rotated), query head h reads kv head h / G; key_mask [B, T] (token index) or
@@ -186,13 +186,16 @@ struct BwAttn {
   const float *dsum;    // [B, nq, T]
   float *dqkv;          // [B*T, ld]: dq written by dq; dk, dv by bw_kv_reduce
   float *part;          // [2, nq, B*T, D]: per-query-head dk, dv partials (dkdv)
-  int rope_on, pos0;
-  float inv_freq[64];
+  int rope_on;
+  const float2 *rope_cs;  // [B*T, D/2] (cos, sin) of each row's angles (bw_rope_table)
 };
 hipError_t bw_attention(int which, const BwAttn &a, hipStream_t s);  // 0 forward, 1 dq, 2 dk/dv
 hipError_t bw_rowdot(const float *dO, const float *O, float *dsum, int M, int T, int nq, int D, hipStream_t s);
 hipError_t bw_kv_reduce(const float *part, float *dqkv, int M, int nq, int nkv, int G, int D, int ld, hipStream_t s);
-hipError_t bw_rope(float *qkv, int M, int T, int ld, int heads, int D, int pos0, const InvFreq &f, hipStream_t s);
+// The RoPE (cos, sin) of every row of the call: cs[m * D/2 + i] at angle
+// (pos0 + m % T) * omega_i, formed and evaluated in double, rounded once to float.
+hipError_t bw_rope_table(float2 *cs, int M, int T, int D, int pos0, const InvFreq &f, hipStream_t s);
+hipError_t bw_rope(float *qkv, int M, int ld, int heads, int D, const float2 *cs, hipStream_t s);
 hipError_t bw_rms_fwd(const float *x, const float *w, float *u, float *r, int M, int H, float eps, hipStream_t s);
 int bw_rms_part_rows(int M);  // rows of the column partials bw_rms_bwd writes
 hipError_t bw_rms_bwd(const float *du, const float *x, const float *r, const float *w, const float *resid, float *dx,

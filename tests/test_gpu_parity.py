@@ -136,6 +136,32 @@ def test_block_f32_with_cache_and_offset():
     assert torch.all(kc[:, :, pos0 + s.seq:] == 0)
 
 
+def test_block_f32_at_the_last_positions():
+    """Positions 8092 .. 8191 (the end of max_pos) over a cache of 8092 random keys: the
+    RoPE angles there are large (p * omega_0 ~ 8e3 rad), which float32 angle arithmetic
+    gets wrong by ~1e-4 rad; the keys written to the cache and the block output must still
+    match the oracle at 1e-4."""
+    s = S.workload("block_f32", batch=2, seq=100, norm_jitter=0.1)
+    pos0, cap = 8092, 8192
+    say("block f32 with cache, pos0=8092")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    past_k = np.random.default_rng(7).standard_normal((2, s.n_kv_heads, pos0, s.head_dim)).astype(np.float32)
+    past_v = np.random.default_rng(8).standard_normal((2, s.n_kv_heads, pos0, s.head_dim)).astype(np.float32)
+    kc = torch.zeros(2, s.n_kv_heads, cap, s.head_dim, device=DEV)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :pos0] = torch.from_numpy(past_k).to(DEV)
+    vc[:, :, :pos0] = torch.from_numpy(past_v).to(DEV)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.data, pos0=pos0, kc=kc, vc=vc))
+    cfg, lw = ocfg(s), olayer(layer)
+    attn, k, v = O.attention_sublayer(x.f64, lw, cfg, np.arange(pos0, cap), past_k, past_v, np.arange(pos0))
+    h = x.f64 + attn
+    want = h + O.mlp_sublayer(h, lw, cfg)
+    rk, r = rel(to_np(kc[:, :, pos0:]), k), rel(got, want)
+    say(f"cache k rel = {rk:.2e}, output rel = {r:.2e}")
+    assert rk <= TOL_F32 and r <= TOL_F32
+
+
 def test_gqa_equals_mha_with_repeated_kv():
     """9/3 heads equals 9/9 heads whose k/v projections repeat each kv head 3 times."""
     s = S.workload("block_f32", batch=2, seq=96)
