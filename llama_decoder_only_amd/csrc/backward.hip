@@ -237,14 +237,14 @@ __device__ __forceinline__ bool visible(const BwAttn &a, int b, int tq, int tk) 
          (a.key_mask == nullptr || a.key_mask[(size_t)b * a.T + tk] != 0);
 }
 
-// Rows row0 .. row0 + 127 (two blocks of 64) of two column blocks of [B*T, ld]
-// matrices into LDS [128][D + 1] (the +1 spreads a column read over all banks);
-// zeros past T. All 256 threads of the workgroup take part.
-template <int D>
+// Rows row0 .. row0 + 64 NP - 1 (NP blocks of 64) of two column blocks of [B*T, ld]
+// matrices into LDS [64 NP][D + 1] (the +1 spreads a column read over all banks);
+// zeros past T. All 128 NP threads of the workgroup take part.
+template <int D, int NP>
 __device__ __forceinline__ void stage_rows2(float *X, float *Y, const float *xs, const float *ys, int ldx, int ldy,
                                             int b, int T, int row0, int tid) {
   constexpr int LD = D + 1;
-  for (int f = tid; f < 128 * D / 4; f += 256) {
+  for (int f = tid; f < 64 * NP * D / 4; f += 128 * NP) {
     const int r = f / (D / 4), c4 = f % (D / 4);
     const int t = row0 + r;
     f32x4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
@@ -293,19 +293,21 @@ __device__ __forceinline__ void rotate_back(f32x16 (&g)[D / 32], const float2 *c
   }
 }
 
-// The three attention kernels share one work split: a workgroup of 4 waves owns 64
-// rows (queries, or keys for dK/dV) of one (sequence, query head), blockIdx.x the
+// The three attention kernels share one work split: a workgroup of 2 NP waves owns
+// 64 rows (queries, or keys for dK/dV) of one (sequence, query head), blockIdx.x the
 // (sequence, head) and blockIdx.y the row block (the heaviest first); wave w takes the
-// 32 rows of group w & 1 and the blocks of 64 columns (keys, or queries) of parity
-// w >> 1, two blocks staged in LDS per round. The two parities' partial results meet
-// in LDS at the end and are combined in a fixed order.
+// 32 rows of group w & 1 and the blocks of 64 columns (keys, or queries) whose index
+// is w >> 1 modulo NP, NP blocks staged in LDS per round. The parities' partial
+// results meet in LDS at the end and are combined in parity order. NP is 4 where
+// the registers and LDS allow two such workgroups' worth of waves per CU (forward
+// and dQ at head dim 64), else 2.
 
 // Forward attention, keeping the log-sum-exp (base 2) of every query's scores for
 // the backward.
-template <int D>
-__global__ __launch_bounds__(256) void bw_attn_fwd_kernel(const BwAttn a) {
+template <int D, int NP>
+__global__ __launch_bounds__(128 * NP) void bw_attn_fwd_kernel(const BwAttn a) {
   constexpr int LD = D + 1, HD = D / 2, NT = D / 32, CS = NT * 16 + 2;
-  __shared__ float Ks[128 * LD], Vs[128 * LD];
+  __shared__ float Ks[64 * NP * LD], Vs[64 * NP * LD];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
   const int rg = w & 1, par = w >> 1;
   const int qb = gridDim.y - 1 - blockIdx.y, b = blockIdx.x / a.nq, hd = blockIdx.x % a.nq, g = hd / a.G;
@@ -322,9 +324,9 @@ __global__ __launch_bounds__(256) void bw_attn_fwd_kernel(const BwAttn a) {
   float m_run = NEG_INF, l_run = 0.f;
   const int kb_hi = min(qb * 64 + 63, a.T - 1) / 64;
   const int kb_lo = a.window > 0 ? max(0, qb * 64 - a.window + 1) / 64 : 0;
-  for (int kb0 = kb_lo; kb0 <= kb_hi; kb0 += 2) {
+  for (int kb0 = kb_lo; kb0 <= kb_hi; kb0 += NP) {
     __syncthreads();
-    stage_rows2<D>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb0 * 64, tid);
+    stage_rows2<D, NP>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb0 * 64, tid);
     __syncthreads();
     const int kb = kb0 + par;
     if (kb > kb_hi) continue;
@@ -364,10 +366,11 @@ __global__ __launch_bounds__(256) void bw_attn_fwd_kernel(const BwAttn a) {
       }
     }
   }
-  // parity 1 hands (O, m, l) to parity 0 of the same row group
+  // parities 1 .. NP-1 hand (O, m, l) to parity 0 of the same row group, which merges
+  // them in parity order
   __syncthreads();
-  float *xch = Ks + (rg * 64 + lane) * CS;
-  if (par == 1) {
+  if (par > 0) {
+    float *xch = Ks + (((par - 1) * 2 + rg) * 64 + lane) * CS;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -376,27 +379,36 @@ __global__ __launch_bounds__(256) void bw_attn_fwd_kernel(const BwAttn a) {
     xch[NT * 16 + 1] = l_run;
   }
   __syncthreads();
-  if (par == 1 || !qok) return;
-  const float m2 = xch[NT * 16], l2 = xch[NT * 16 + 1];
-  const float mm = fmaxf(m_run, m2), mu = mm == NEG_INF ? 0.f : mm;
-  const float f1 = exp2f(m_run - mu), f2 = exp2f(m2 - mu);
-  const float l = l_run * f1 + l2 * f2;
-  const float inv = 1.0f / l;  // a query with no visible key: 0 / 0, NaN
+  if (par > 0 || !qok) return;
+#pragma unroll
+  for (int q = 1; q < NP; ++q) {
+    const float *xch = Ks + (((q - 1) * 2 + rg) * 64 + lane) * CS;
+    const float m2 = xch[NT * 16], l2 = xch[NT * 16 + 1];
+    const float mm = fmaxf(m_run, m2), mu = mm == NEG_INF ? 0.f : mm;
+    const float f1 = exp2f(m_run - mu), f2 = exp2f(m2 - mu);
+    l_run = l_run * f1 + l2 * f2;
+    m_run = mm;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[t][r] = oacc[t][r] * f1 + xch[t * 16 + r] * f2;
+  }
+  const float inv = 1.0f / l_run;  // a query with no visible key: 0 / 0, NaN
   float *orow = a.o + rowq * (size_t)(a.nq * D) + hd * D;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) orow[t * 32 + acc_row(r, lane)] = (oacc[t][r] * f1 + xch[t * 16 + r] * f2) * inv;
-  if (hl == 0) a.lse[((size_t)b * a.nq + hd) * a.T + tq] = mm + log2f(l);
+    for (int r = 0; r < 16; ++r) orow[t * 32 + acc_row(r, lane)] = oacc[t][r] * inv;
+  if (hl == 0) a.lse[((size_t)b * a.nq + hd) * a.T + tq] = m_run + log2f(l_run);
 }
 
 // dQ: for every visible key block, P = exp2(S log2(e)/sqrt(d) - lse),
 // dS = P (dO V^T - rowsum(dO O)), dQ += dS K; then dQ / sqrt(d), rotated back on a
 // rotary block, into dqkv.
-template <int D>
-__global__ __launch_bounds__(256) void bw_attn_dq_kernel(const BwAttn a) {
+template <int D, int NP>
+__global__ __launch_bounds__(128 * NP) void bw_attn_dq_kernel(const BwAttn a) {
   constexpr int LD = D + 1, HD = D / 2, NT = D / 32, CS = NT * 16;
-  __shared__ float Ks[128 * LD], Vs[128 * LD];
+  __shared__ float Ks[64 * NP * LD], Vs[64 * NP * LD];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hl = lane >> 5;
   const int rg = w & 1, par = w >> 1;
   const int qb = gridDim.y - 1 - blockIdx.y, b = blockIdx.x / a.nq, hd = blockIdx.x % a.nq, g = hd / a.G;
@@ -415,9 +427,9 @@ __global__ __launch_bounds__(256) void bw_attn_dq_kernel(const BwAttn a) {
   for (int t = 0; t < NT; ++t) dq[t] = (f32x16){};
   const int kb_hi = min(qb * 64 + 63, a.T - 1) / 64;
   const int kb_lo = a.window > 0 ? max(0, qb * 64 - a.window + 1) / 64 : 0;
-  for (int kb0 = kb_lo; kb0 <= kb_hi; kb0 += 2) {
+  for (int kb0 = kb_lo; kb0 <= kb_hi; kb0 += NP) {
     __syncthreads();
-    stage_rows2<D>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb0 * 64, tid);
+    stage_rows2<D, NP>(Ks, Vs, kbase, vbase, a.ld, a.ld, b, a.T, kb0 * 64, tid);
     __syncthreads();
     const int kb = kb0 + par;
     if (kb > kb_hi) continue;
@@ -447,19 +459,25 @@ __global__ __launch_bounds__(256) void bw_attn_dq_kernel(const BwAttn a) {
     }
   }
   __syncthreads();
-  float *xch = Ks + (rg * 64 + lane) * CS;
-  if (par == 1) {
+  if (par > 0) {
+    float *xch = Ks + (((par - 1) * 2 + rg) * 64 + lane) * CS;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) xch[t * 16 + r] = dq[t][r];
   }
   __syncthreads();
-  if (par == 1 || !qok) return;
+  if (par > 0 || !qok) return;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int q = 1; q < NP; ++q) {  // the parities' partial sums, added in parity order
+    const float *xch = Ks + (((q - 1) * 2 + rg) * 64 + lane) * CS;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dq[t][r] = (dq[t][r] + xch[t * 16 + r]) * a.scale;
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[t][r] += xch[t * 16 + r];
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) dq[t] *= a.scale;
   if (a.rope_on) rotate_back<D>(dq, a.rope_cs + rowq * (D / 2), lane);
   float *out = a.dqkv + rowq * a.ld + hd * D;
 #pragma unroll
@@ -494,7 +512,7 @@ __global__ __launch_bounds__(256) void bw_attn_dkdv_kernel(const BwAttn a) {
   const int qb_hi = q_last / 64;
   for (int qb0 = kb; qb0 <= qb_hi; qb0 += 2) {
     __syncthreads();
-    stage_rows2<D>(Qs, Os, a.qkv + hd * D, a.dO + hd * D, a.ld, a.nq * D, b, a.T, qb0 * 64, tid);
+    stage_rows2<D, 2>(Qs, Os, a.qkv + hd * D, a.dO + hd * D, a.ld, a.nq * D, b, a.T, qb0 * 64, tid);
     if (tid < 128) {
       const int t = qb0 * 64 + tid;
       Ls[tid] = t < a.T ? a.lse[stat0 + t] : 0.f;
@@ -780,13 +798,13 @@ hipError_t bw_attention(int which, const BwAttn &a, hipStream_t s) {
   // queries; first keys) first, so a second round of workgroups holds the lightest
   const dim3 grid(a.B * a.nq, (a.T + 63) / 64);
   if (a.D == 64) {
-    if (which == 0) return launch(bw_attn_fwd_kernel<64>, grid, dim3(256), s, a);
-    if (which == 1) return launch(bw_attn_dq_kernel<64>, grid, dim3(256), s, a);
+    if (which == 0) return launch(bw_attn_fwd_kernel<64, 4>, grid, dim3(512), s, a);
+    if (which == 1) return launch(bw_attn_dq_kernel<64, 4>, grid, dim3(512), s, a);
     return launch(bw_attn_dkdv_kernel<64>, grid, dim3(256), s, a);
   }
   if (a.D == 128) {
-    if (which == 0) return launch(bw_attn_fwd_kernel<128>, grid, dim3(256), s, a);
-    if (which == 1) return launch(bw_attn_dq_kernel<128>, grid, dim3(256), s, a);
+    if (which == 0) return launch(bw_attn_fwd_kernel<128, 2>, grid, dim3(256), s, a);
+    if (which == 1) return launch(bw_attn_dq_kernel<128, 2>, grid, dim3(256), s, a);
     return launch(bw_attn_dkdv_kernel<128>, grid, dim3(256), s, a);
   }
   return hipErrorInvalidValue;
