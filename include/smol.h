@@ -235,10 +235,12 @@ typedef struct {
  *   grads: the nine weight gradients, written (accumulate == 0) or added to what the
  *     buffers hold (accumulate == 1: gradient accumulation over micro-batches).
  * The forward is recomputed inside (activations are not taken from a forward call).
- * Supports config.dtype SMOL_F32 only (float32 weights; every contraction is a
- * float32 MFMA); SMOL_BF16 returns SMOL_ERR_UNSUPPORTED. Requires pos0 >= 0, pos0 +
- * seq <= max_pos, 0 <= layer < n_layers. ws: smol_block_backward_workspace_size()
- * bytes, 256-byte aligned. Deterministic: no atomics, every sum in a fixed order. */
+ * Every contraction is a float32 MFMA: with config.dtype SMOL_BF16 the bfloat16
+ * weights (16-byte aligned) are first widened to float32 in the workspace (exact),
+ * so a bf16 model gets the float32 gradients of its own weights. Requires pos0 >= 0,
+ * pos0 + seq <= max_pos, 0 <= layer < n_layers. ws:
+ * smol_block_backward_workspace_size() bytes, 256-byte aligned. Deterministic: no
+ * atomics, every sum in a fixed order. */
 smol_status smol_block_backward_workspace_size(const smol_config *cfg, int batch, int seq, size_t *bytes);
 smol_status smol_block_backward(const smol_config *cfg, const smol_layer_weights *w, int layer,
                                 const float *x, const float *dy, int batch, int seq, int pos0,

@@ -450,7 +450,9 @@ smol_status check_model(const Dims &D, const smol_model_weights *w) {
 // smol_block_backward: the forward recomputed with its activations kept, then the
 // chain rule in reverse (backward.hip). M = B*T rows; C3 = (nq + 2 nkv) d.
 struct BwWs {
-  size_t u, r1, qkv, o, lse, h, wn, r2, gu, dgu, y, dwn, dh, dO, dsum, dqkv, part, du, npart, gpart, rope, total;
+  size_t u, r1, qkv, o, lse, h, wn, r2, gu, dgu, y, dwn, dh, dO, dsum, dqkv, part, du, npart, gpart, rope;
+  size_t wf32[9];  // a bf16 model's weights widened to float32 (unused for float32 models)
+  size_t total;
 };
 
 // The GEMMs of one block backward: (M, N, K, epilogue) of each launch, in order.
@@ -493,6 +495,9 @@ BwWs bw_layout(const Dims &D, int B, int T) {
   for (const BwShape &g : bw_shapes(D, (int)M)) gp = std::max(gp, smol::bw_gemm_part_floats(g.M, g.N, g.K, g.epi));
   w.gpart = take(std::max<size_t>(gp, 1));
   w.rope = take(M * (D.d / 2) * 2);  // (cos, sin) per row and frequency
+  const size_t KD = (size_t)D.nkv * D.d;
+  const size_t wsz[9] = {H, QD * H, KD * H, KD * H, H * QD, H, (size_t)D.I * H, (size_t)D.I * H, H * D.I};
+  for (int i = 0; i < 9; ++i) w.wf32[i] = D.bf16 ? take(wsz[i]) : 0;
   w.total = off;
   return w;
 }
@@ -822,7 +827,6 @@ smol_status smol_block_backward(const smol_config *cfg, const smol_layer_weights
   Dims D;
   smol_status st = check_config(cfg, &D);
   if (st != SMOL_OK) return st;
-  if (D.bf16) return fail(SMOL_ERR_UNSUPPORTED, "smol_block_backward supports dtype SMOL_F32 only");
   if ((st = check_layer(w, layer)) != SMOL_OK) return st;
   if (layer < 0 || layer >= D.L) return fail(SMOL_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, D.L);
   if (!x || !dy || !dx) return fail(SMOL_ERR_INVALID_ARG, "x / dy / dx is NULL");
@@ -848,8 +852,25 @@ smol_status smol_block_backward(const smol_config *cfg, const smol_layer_weights
   if (!ws) return fail(SMOL_ERR_INVALID_ARG, "ws is NULL");
   if (ws_bytes < lay.total) return fail(SMOL_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, lay.total);
   if ((uintptr_t)ws % ALIGN) return fail(SMOL_ERR_INVALID_ARG, "ws must be 256-byte aligned");
-  return backward_impl(D, w, layer, x, dy, batch, seq, pos0, key_mask, dx, grads, accumulate, (char *)ws, lay,
-                       (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  smol_layer_weights wf = *w;
+  if (D.bf16) {
+    const void *pw[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
+    for (const void *p : pw)
+      if ((uintptr_t)p % 16) return fail(SMOL_ERR_INVALID_ARG, "bf16 weights must be 16-byte aligned");
+  }
+  if (D.bf16) {  // widen the weights to float32 once (exact) and differentiate in float32
+    const void *src[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
+    const void **dst[9] = {&wf.attn_norm, &wf.wq, &wf.wk, &wf.wv, &wf.wo, &wf.mlp_norm, &wf.w_gate, &wf.w_up, &wf.w_down};
+    const size_t QD = (size_t)D.nq * D.d, KD = (size_t)D.nkv * D.d, H = D.H;
+    const size_t n[9] = {H, QD * H, KD * H, KD * H, H * QD, H, (size_t)D.I * H, (size_t)D.I * H, H * D.I};
+    for (int i = 0; i < 9; ++i) {
+      float *to = (float *)((char *)ws + lay.wf32[i]);
+      SMOL_LAUNCH(SMOL_K_BW_ROWS, smol::bw_widen((const bf16 *)src[i], to, n[i], s));
+      *dst[i] = to;
+    }
+  }
+  return backward_impl(D, &wf, layer, x, dy, batch, seq, pos0, key_mask, dx, grads, accumulate, (char *)ws, lay, s);
 }
 
 const char *smol_status_string(smol_status s) {

@@ -748,6 +748,25 @@ __global__ __launch_bounds__(1024) void bw_colsum_kernel(const float *part, int 
   }
 }
 
+// bfloat16 -> float32 (exact: the bits move to the top half), 8 elements per thread.
+__global__ __launch_bounds__(256) void bw_widen_kernel(const bf16 *src, float *dst, size_t n) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  if (i + 8 <= n) {
+    const Chunk16 c = ld16(src + i);
+    f32x4 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = __uint_as_float(c[j >> 1] << ((j & 1) ? 0 : 16) & 0xffff0000u);
+      hi[j] = __uint_as_float(c[2 + (j >> 1)] << ((j & 1) ? 0 : 16) & 0xffff0000u);
+    }
+    *reinterpret_cast<f32x4 *>(dst + i) = lo;
+    *reinterpret_cast<f32x4 *>(dst + i + 4) = hi;
+  } else {
+    for (size_t j = i; j < n; ++j) dst[j] = (float)src[j];
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -848,6 +867,11 @@ hipError_t bw_rms_bwd(const float *du, const float *x, const float *r, const flo
   if (nc <= 4) return launch(bw_rms_bwd_kernel<4>, grid, block, s, du, x, r, w, resid, dx, part, M, H);
   if (nc <= 8) return launch(bw_rms_bwd_kernel<8>, grid, block, s, du, x, r, w, resid, dx, part, M, H);
   return launch(bw_rms_bwd_kernel<16>, grid, block, s, du, x, r, w, resid, dx, part, M, H);
+}
+
+hipError_t bw_widen(const bf16 *src, float *dst, size_t n, hipStream_t s) {
+  if ((uintptr_t)src % 16 || (uintptr_t)dst % 16) return hipErrorInvalidValue;
+  return launch(bw_widen_kernel, dim3((unsigned)((n + 2047) / 2048)), dim3(256), s, src, dst, n);
 }
 
 hipError_t bw_colsum(const float *part, int nrows, int H, float *dw, int accumulate, hipStream_t s) {

@@ -201,6 +201,7 @@ int bw_rms_part_rows(int M);  // rows of the column partials bw_rms_bwd writes
 hipError_t bw_rms_bwd(const float *du, const float *x, const float *r, const float *w, const float *resid, float *dx,
                       float *part, int M, int H, hipStream_t s);
 hipError_t bw_colsum(const float *part, int nrows, int H, float *dw, int accumulate, hipStream_t s);
+hipError_t bw_widen(const bf16 *src, float *dst, size_t n, hipStream_t s);  // dst = (float)src, exact
 
 // Kernel-class timing (see smol_timing_begin). timing_before arms the next launch()
 // of that class with a start/stop event pair, which hipExtLaunchKernelGGL records at

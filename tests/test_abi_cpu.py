@@ -237,7 +237,13 @@ def test_block_backward_rejects():
     n = ctypes.c_size_t(0)
     assert B.lib().smol_block_backward_workspace_size(ctypes.byref(f32.c()), 4, 512, ctypes.byref(n)) == 0
     assert n.value > 4 * 512 * (576 * 8 + 1536 * 5) * 4
-    assert _backward(_cfg(), w) == B.SMOL_ERR_UNSUPPORTED and "F32" in B.smol_last_error()  # bf16 config
+    bf = _cfg()  # a bf16 config: accepted, its weights must be 16-byte aligned
+    nb, nf = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    B.lib().smol_block_backward_workspace_size(ctypes.byref(bf.c()), 1, 8, ctypes.byref(nb))
+    B.lib().smol_block_backward_workspace_size(ctypes.byref(f32.c()), 1, 8, ctypes.byref(nf))
+    assert nb.value > nf.value  # room for the widened weights
+    odd = B.smol_layer_weights(*[FAKE + 8 if n == "wq" else FAKE for n in B.LAYER_FIELDS])
+    assert _backward(bf, odd) == B.SMOL_ERR_INVALID_ARG and "aligned" in B.smol_last_error()
     assert _backward(f32, _layer_struct(null="wo")) == B.SMOL_ERR_INVALID_ARG and "wo" in B.smol_last_error()
     assert _backward(f32, w, g=_grads_struct(null="w_up")) == B.SMOL_ERR_INVALID_ARG
     assert _backward(f32, w, layer=30) == B.SMOL_ERR_INVALID_ARG and "layer" in B.smol_last_error()

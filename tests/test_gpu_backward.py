@@ -39,7 +39,9 @@ def _run(s, layer=0, pos0=0, mask=None, accumulate=False, grads=None, seed=0):
     x = S.hidden_states(s, seed)
     dy = S.output_grad(s, seed)
     w = B.upload_layer(lw)
-    xt, dyt = B.to_device(x), B.to_device(dy)
+    # the block interface is float32 for both model dtypes
+    xt = torch.from_numpy(x.f64.astype(np.float32)).to(DEV)
+    dyt = torch.from_numpy(dy.f64.astype(np.float32)).to(DEV)
     dx = torch.empty_like(xt)
     g = grads if grads is not None else B.LayerGrads.zeros_like(w)
     km = None if mask is None else torch.from_numpy(mask.astype(np.uint8)).to(DEV)
@@ -114,6 +116,15 @@ def test_backward_edge_sizes(batch, seq, pos0):
     say(f"backward edge B={batch} T={seq} pos0={pos0}")
     got, (lw, x, dy, *_) = _run(s, pos0=pos0)
     _compare(got, _oracle(s, lw, x, dy, pos0=pos0))
+
+
+def test_backward_bf16_model():
+    """A bf16 model: its weights are widened to float32 exactly, so the gradients match
+    the oracle on the bf16-rounded weights at the float32 bar."""
+    s = S.workload("block_backward_f32", dtype="bf16", batch=2, seq=130)
+    say("backward bf16 model B=2 T=130 pos0=9")
+    got, (lw, x, dy, *_) = _run(s, pos0=9)
+    _compare(got, _oracle(s, lw, x, dy, pos0=9))
 
 
 def test_backward_full_shape():
