@@ -129,10 +129,12 @@ def test_prefill_key_mask_with_cache_and_fully_masked_query():
     assert rel(got[ok], want[ok]) <= TOL_F32
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_decode_key_mask(dtype):
+@pytest.mark.parametrize("dtype,batch", [("f32", 3), ("bf16", 3), ("f32", 48), ("bf16", 48)])
+def test_decode_key_mask(dtype, batch):
+    """At batch 3 and at batch 48 (144 sequence / kv-head pairs, near the benchmarked
+    decode's 192)."""
     name = "model_f32" if dtype == "f32" else "prefill_bf16"
-    s = S.workload(name, n_layers=2, batch=3, seq=271, norm_jitter=0.1)
+    s = S.workload(name, n_layers=2, batch=batch, seq=271, norm_jitter=0.1)
     say(f"masked decode {dtype}")
     model = S.model_weights(s, 0)
     md = B.upload_model(model)
@@ -143,9 +145,9 @@ def test_decode_key_mask(dtype):
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     kc, vc = _caches(s, cap, tdt)
     B.smol_model_prefill_ex(cfg, md, ids[:, :P].contiguous(), _logits(s, P), 0, None, kc, vc)
-    mask = _mask(np.random.default_rng(8), 3, cap, 0.6)
-    out = torch.empty(3, s.vocab, dtype=tdt, device=DEV)
-    cl = torch.full((3,), P, dtype=torch.int32, device=DEV)
+    mask = _mask(np.random.default_rng(8), batch, cap, 0.6)
+    out = torch.empty(batch, s.vocab, dtype=tdt, device=DEV)
+    cl = torch.full((batch,), P, dtype=torch.int32, device=DEV)
     B.smol_decode_step_ex(cfg, md, ids[:, P].contiguous(), cl, kc, vc, out,
                           torch.from_numpy(mask.astype(np.uint8)).to(DEV))
     torch.cuda.synchronize()
@@ -160,7 +162,7 @@ def test_decode_key_mask(dtype):
     # no mask at all equals the all-ones mask
     out2 = torch.empty_like(out)
     B.smol_decode_step_ex(cfg, md, ids[:, P].contiguous(), cl, kc, vc, out2,
-                          torch.ones(3, cap, dtype=torch.uint8, device=DEV))
+                          torch.ones(batch, cap, dtype=torch.uint8, device=DEV))
     out3 = torch.empty_like(out)
     B.smol_decode_step(cfg, md, ids[:, P].contiguous(), cl, kc, vc, out3)
     torch.cuda.synchronize()

@@ -434,19 +434,21 @@ def test_decode_bf16_ragged_lengths():
     assert torch.equal(kc[:, -1], torch.stack([B.to_device(k)[-1] for k in ks]))
 
 
-def test_decode_invalid_cache_len_gives_nan_and_no_write():
-    s = S.workload("model_f32", n_layers=2, batch=3, seq=1)
-    say("decode invalid cache_len")
+@pytest.mark.parametrize("batch", [3, 48])
+def test_decode_invalid_cache_len_gives_nan_and_no_write(batch):
+    s = S.workload("model_f32", n_layers=2, batch=batch, seq=1)
+    say(f"decode invalid cache_len, batch {batch}")
     md = B.upload_model(S.model_weights(s, 0))
     cap = 16
-    kc = torch.zeros(2, 3, s.n_kv_heads, cap, s.head_dim, device=DEV)
+    kc = torch.zeros(2, batch, s.n_kv_heads, cap, s.head_dim, device=DEV)
     vc = torch.zeros_like(kc)
-    cl = torch.tensor([4, cap, -1], dtype=torch.int32, device=DEV)
-    ids = torch.tensor([1, 2, 3], dtype=torch.int32, device=DEV)
+    cl = torch.full((batch,), 4, dtype=torch.int32, device=DEV)
+    cl[1], cl[2] = cap, -1
+    ids = torch.arange(1, batch + 1, dtype=torch.int32, device=DEV)
     out = _decode(s, md, ids, cl, kc, vc)
-    assert torch.isfinite(out[0]).all()
+    assert torch.isfinite(out[0]).all() and torch.isfinite(out[3:]).all()
     assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
-    assert torch.all(kc[:, 1:] == 0) and torch.all(vc[:, 1:] == 0)
+    assert torch.all(kc[:, 1:3] == 0) and torch.all(vc[:, 1:3] == 0)
     assert torch.any(kc[:, 0, :, 4] != 0)
 
 

@@ -63,11 +63,12 @@ def test_variants_prefill(dtype, seq, window):
     assert rel(to_np(logits)[:, rows], want) > 10 * (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_variants_decode(dtype):
+@pytest.mark.parametrize("dtype,batch", [("f32", 2), ("bf16", 2), ("bf16", 128)])
+def test_variants_decode(dtype, batch):
     """Decode at P = 300 over a prefilled cache: the NoPE blocks see keys 201 .. 300
-    only (window 100), in a cache of two 256-key chunks whose first is partly outside."""
-    s = _shape(dtype, 301, 100)
+    only (window 100), in a cache of two 256-key chunks whose first is partly outside
+    (batch 2, and batch 128 with its 128 sequence / kv-head pairs)."""
+    s = _shape(dtype, 301, 100, batch=batch)
     model = S.model_weights(s, 0)
     md = B.upload_model(model)
     cfg = B.Config.from_shape(s)
@@ -75,11 +76,12 @@ def test_variants_decode(dtype):
     ids = torch.from_numpy(ids_np).to(DEV)
     P, cap = 300, 512
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
-    kc = torch.zeros(s.n_layers, 2, s.n_kv_heads, cap, s.head_dim, dtype=tdt, device=DEV)
+    kc = torch.zeros(s.n_layers, batch, s.n_kv_heads, cap, s.head_dim, dtype=tdt, device=DEV)
     vc = torch.zeros_like(kc)
-    B.smol_model_prefill(cfg, md, ids[:, :P].contiguous(), torch.empty(2, P, s.vocab, dtype=tdt, device=DEV), kc, vc)
-    out = torch.empty(2, s.vocab, dtype=tdt, device=DEV)
-    cl = torch.full((2,), P, dtype=torch.int32, device=DEV)
+    B.smol_model_prefill(cfg, md, ids[:, :P].contiguous(), torch.empty(batch, P, s.vocab, dtype=tdt, device=DEV), kc,
+                         vc)
+    out = torch.empty(batch, s.vocab, dtype=tdt, device=DEV)
+    cl = torch.full((batch,), P, dtype=torch.int32, device=DEV)
     B.smol_decode_step(cfg, md, ids[:, P].contiguous(), cl, kc, vc, out)
     torch.cuda.synchronize()
     om = omodel(model)
