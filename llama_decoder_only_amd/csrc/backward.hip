@@ -615,17 +615,14 @@ __global__ __launch_bounds__(256) void bw_kv_reduce_kernel(const float *part, fl
   *reinterpret_cast<f32x4 *>(dqkv + (size_t)m * ld + (nq + which * nkv + g) * D + e) = s;
 }
 
-// The RoPE table of the call: cs[m * D/2 + i] = (cos, sin) of (pos0 + m % T) * omega_i,
-// the angle formed and evaluated in double (a float32 product is off by up to
-// 1.4e-4 rad at position 8191) and rounded once to float.
+// The RoPE table of the call: cs[m * D/2 + i] = (cos, sin) of (pos0 + m % T) * omega_i
+// (rope_cos_sin: the angle formed and reduced in double).
 __global__ __launch_bounds__(256) void bw_rope_table_kernel(float2 *cs, int M, int T, int half, int pos0,
                                                             const InvFreq f) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= M * half) return;
   const int m = i / half, j = i % half;
-  double sn, c;
-  sincos((double)(pos0 + m % T) * f.v[j], &sn, &c);
-  cs[i] = make_float2((float)c, (float)sn);
+  cs[i] = rope_cos_sin(pos0 + m % T, f.v[j]);
 }
 
 // RoPE on the q and k columns of qkv, in place: pair (j, j + D/2) of every head

@@ -87,6 +87,22 @@ constexpr int SMOL_XCDS = 8;
 __host__ __device__ inline bool xcd_rows(int M) { return M >= 1024; }
 __host__ __device__ inline int rows_per_xcd(int M) { return ((M + SMOL_XCDS - 1) / SMOL_XCDS + 127) / 128 * 128; }
 
+// ---------------------------------------------------------------- RoPE angles
+// (cos, sin) of p * omega, accurate at any position up to float rounding of the
+// result: the angle is formed and reduced modulo 2 pi in double (Cody-Waite, with
+// 2 pi split into the double nearest to it plus the remainder), and only the reduced
+// angle, |r| <= pi, goes to float sincosf. A float product p * omega alone is off by
+// up to 1.4e-4 rad at p = 8191; this is within ~2e-7 everywhere (and much cheaper
+// than a double sincos).
+__device__ __forceinline__ float2 rope_cos_sin(int pos, double omega) {
+  const double x = (double)pos * omega;
+  const double k = rint(x * 0.15915494309189535);  // round(x / (2 pi))
+  const double r = fma(-k, 6.283185307179586, x) - k * 2.4492935982947064e-16;
+  float s, c;
+  sincosf((float)r, &s, &c);
+  return make_float2(c, s);
+}
+
 // ---------------------------------------------------------------- reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

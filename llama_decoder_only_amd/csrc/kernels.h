@@ -193,7 +193,7 @@ hipError_t bw_attention(int which, const BwAttn &a, hipStream_t s);  // 0 forwar
 hipError_t bw_rowdot(const float *dO, const float *O, float *dsum, int M, int T, int nq, int D, hipStream_t s);
 hipError_t bw_kv_reduce(const float *part, float *dqkv, int M, int nq, int nkv, int G, int D, int ld, hipStream_t s);
 // The RoPE (cos, sin) of every row of the call: cs[m * D/2 + i] at angle
-// (pos0 + m % T) * omega_i, formed and evaluated in double, rounded once to float.
+// (pos0 + m % T) * omega_i (rope_cos_sin in common.h).
 hipError_t bw_rope_table(float2 *cs, int M, int T, int D, int pos0, const InvFreq &f, hipStream_t s);
 hipError_t bw_rope(float *qkv, int M, int ld, int heads, int D, const float2 *cs, hipStream_t s);
 hipError_t bw_rms_fwd(const float *x, const float *w, float *u, float *r, int M, int H, float eps, hipStream_t s);

@@ -24,11 +24,7 @@ rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const f
   if (rope.cs && lane < rope.half) {
     // RoPE angle i of this row (abi96062 components.py, RotaryEmbedding: pos * omega_i)
     const int pos = rope.cache_len ? rope.cache_len[row] : rope.pos0 + row % rope.seq;
-    // formed and reduced in double: a float32 product p * omega_i is off by up to
-    // 1.4e-4 rad at p = 8191, where a double one is exact to ~1e-12
-    double sn, cs;
-    sincos((double)pos * rope.inv_freq[lane], &sn, &cs);
-    rope.cs[(size_t)row * rope.half + lane] = make_float2((float)cs, (float)sn);
+    rope.cs[(size_t)row * rope.half + lane] = rope_cos_sin(pos, rope.inv_freq[lane]);
   }
   float *xr = x + (size_t)row * H;
   const int id = ids ? ids[row] : 0;
