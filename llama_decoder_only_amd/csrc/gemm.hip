@@ -769,8 +769,8 @@ static hipError_t launch_split(GemmParams p, int ks, hipStream_t s) {
                    nullptr, e1, p);
 }
 
-// Tile choice, from sweeps on MI355X over the model's shapes (2-stage rings were
-// never slower than deeper ones; 256-byte stages did not pay):
+// Tile choice, from sweeps on MI355X over the model's shapes (256-byte stages did
+// not pay):
 //   * a plain store with >= 512 tiles of 256 x 256 (lm_head): 256 x 256 in 4 x 4 waves,
 //     which halves the L2 -> LDS bytes per FLOP of 128 x 128 (lm_head at batch 4 x seq
 //     512: 160 us against 200);
@@ -784,8 +784,13 @@ static hipError_t launch_split(GemmParams p, int ks, hipStream_t s) {
 // chain then runs exposed: those split each stage's K steps over two wave groups.
 // Grids under 128 tiles (a decode step: M = batch) stream weights that are cold in
 // L2 and MALL through few workgroups; there a 4-deep ring keeps three stages of HBM
-// reads in flight (measured 25-30% faster than 2 stages with cold weights, while
-// warm prefill GEMMs gain nothing from depth).
+// reads in flight (measured 25-30% faster than 2 stages with cold weights). In the
+// prefill each layer's weights are also cold in L2 (they come from MALL or HBM): the
+// residual GEMMs (o_proj, and down with its 24 stages) run a 3-deep ring (down
+// 22.2 -> 18.8 us at batch 4 x seq 512; 4 stages or 4 wave groups gain nothing
+// more). QKV and gate/up stay at 2: QKV gains nothing, and a third stage of the
+// 64 x 128 gate/up tiles leaves room for two workgroups per CU instead of three, so
+// its 768 workgroups no longer run in one round (18.7 -> 20.8 us).
 template <typename T, int EPI>
 static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (p.part && (EPI != EPI_QKV_ROPE || p.head_dim == 64)) {
@@ -801,6 +806,7 @@ static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (EPI == EPI_QKV_ROPE && p.head_dim == 128) return launch_cfg<T, 64, 128, 2, 2, 128, EPI, 2, 2>(p, s);
   if (EPI != EPI_QKV_ROPE && p.N % 128 == 0 && tm64 * (p.N / 128) >= 512)
     return launch_cfg<T, 64, 128, 1, 4, 128, EPI, 2, 2>(p, s);
+  if (EPI == EPI_RESIDUAL) return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 3, 2>(p, s);
   return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 2, 2>(p, s);
 }
 
