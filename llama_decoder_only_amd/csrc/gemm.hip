@@ -127,13 +127,19 @@ __host__ __device__ inline int xcd_mode(int M, int N, int BN) {
 // A store to global memory through a global-address-space pointer: the compiler
 // then emits global_store, never a flat store (the pointers here are loaded from the
 // kernel's parameter struct, where it cannot infer the address space itself).
-template <typename V>
+// NTS: a non-temporal store (global_store ... nt), for output that streams out and
+// is not read again by the next kernels.
+template <bool NTS = false, typename V>
 __device__ __forceinline__ void gstore(void *dst, const V &v) {
-  *reinterpret_cast<__attribute__((address_space(1))) V *>(reinterpret_cast<uintptr_t>(dst)) = v;
+  auto *g = reinterpret_cast<__attribute__((address_space(1))) V *>(reinterpret_cast<uintptr_t>(dst));
+  if constexpr (NTS)
+    __builtin_nontemporal_store(v, g);
+  else
+    *g = v;
 }
 
-// Store N (4 or 8) consecutive floats as type O.
-template <typename O, int N>
+// Store N (4 or 8) consecutive floats as type O (non-temporal with NTS).
+template <typename O, int N, bool NTS = false>
 __device__ __forceinline__ void store_vec(O *dst, const float *v) {
   if constexpr (sizeof(O) == 2 && N == 8) {
     Chunk16 c;
@@ -141,7 +147,7 @@ __device__ __forceinline__ void store_vec(O *dst, const float *v) {
     for (int i = 0; i < 4; ++i)
       c[i] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i])) |
              ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i + 1])) << 16);
-    gstore(dst, c);
+    gstore<NTS>(dst, c);
   } else if constexpr (sizeof(O) == 2 && N == 4) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     u32x2 c;
@@ -149,11 +155,11 @@ __device__ __forceinline__ void store_vec(O *dst, const float *v) {
     for (int i = 0; i < 2; ++i)
       c[i] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i])) |
              ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<O>(v[2 * i + 1])) << 16);
-    gstore(dst, c);
+    gstore<NTS>(dst, c);
   } else {
     static_assert(sizeof(O) == 4, "float output");
 #pragma unroll
-    for (int i = 0; i < N; i += 4) gstore((float *)dst + i, (f32x4){v[i], v[i + 1], v[i + 2], v[i + 3]});
+    for (int i = 0; i < N; i += 4) gstore<NTS>((float *)dst + i, (f32x4){v[i], v[i + 1], v[i + 2], v[i + 3]});
   }
 }
 
@@ -232,6 +238,9 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams &p, const float *
 
   // ------------------------------------------------------------ epilogue (row-major walk)
   if constexpr (EPI == EPI_STORE) {
+    // Logits stream out (201 MB at batch 4 x seq 512) and nothing here reads them
+    // again: non-temporal stores keep them from displacing the weights in MALL, which
+    // the next prefill reads again (measured: prefill step 2.33 -> 2.20 ms).
     if (p.c_f32 || sizeof(W) == 4) {
       constexpr int V = 4;
       for (int it = tid; it < ER * BN / V; it += NT) {
@@ -241,7 +250,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams &p, const float *
         float v[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
-        store_vec<float, V>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
+        store_vec<float, V, true>((float *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
       }
     } else {
       constexpr int V = 8;
@@ -252,7 +261,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams &p, const float *
         float v[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) v[e] = tile[r * OP + c + e] * f;
-        if constexpr (sizeof(W) == 2) store_vec<W, V>((W *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
+        if constexpr (sizeof(W) == 2) store_vec<W, V, true>((W *)p.C + (size_t)(em0 + r) * p.ldc + n0 + c, v);
       }
     }
   } else if constexpr (EPI == EPI_RESIDUAL) {
