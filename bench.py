@@ -178,6 +178,65 @@ def measured_traffic(key: str):
     return int(fields[key]) if h.hexdigest() == fields["source-sha256"].strip() else None
 
 
+def other_prefill(B, torch, dev, name, md, reps, warmup):
+    """One of the other prefill shapes (context, not the headline): graph replays of a
+    whole prefill, median and p10/p90, MFMA fraction and per-class kernel durations.
+    md: device weights of that shape's model."""
+    from llama_decoder_only_amd import synthetic as S
+
+    s = S.workload(name)
+    cfg = B.Config.from_shape(s)
+    ids = torch.from_numpy(S.token_ids(s, 0)).to(dev)
+    logits = torch.empty(s.batch, s.seq, s.vocab, dtype=torch.bfloat16, device=dev)
+    ws = B.workspace(cfg, B.SMOL_OP_PREFILL, s.batch, s.seq, dev)
+    stream = torch.cuda.Stream()
+
+    def step():
+        B.smol_model_prefill(cfg, md, ids, logits, ws=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = _rep_ms(lambda: g.replay(), reps, torch, stream)
+    t = float(np.median(ms)) * 1e-3
+    flops = prefill_flops(s)
+    kern = {}
+    with torch.cuda.stream(stream):
+        for k in ("qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head"):
+            kms, n = _kernel_time(B, k, step, torch)
+            kern[k] = round(1e3 * kms / max(n, 1), 2)
+    del ws, logits
+    return {"workload": f"{name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_heads}/{s.n_kv_heads} heads x "
+                        f"{s.head_dim}, intermediate {s.intermediate}, vocab {s.vocab}; batch {s.batch} x seq {s.seq}",
+            "timing": "hip_graph (median of reps)", "ms_per_step": round(t * 1e3, 3),
+            "tokens_per_s": round(s.batch * s.seq / t, 1), "rep_ms": _pct(ms),
+            "algorithmic_gflop_per_step": round(flops["total"] / 1e9, 1),
+            "mfma_frac": round(flops["total"] / t / 1e12 / BF16_PEAK_TFLOPS, 4), "kernels_us": kern}
+
+
+def random_model(B, torch, dev, s, seed=1):
+    """Device weights of shape s drawn on the GPU (torch's generator, N(0, std^2), norm
+    weights 1): for timing only, where the values do not matter and drawing billions
+    of them on the host would take minutes."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    H, I, d = s.hidden, s.intermediate, s.head_dim
+
+    def w(*shape):
+        return (torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32) * s.std).to(torch.bfloat16)
+
+    ones = lambda: torch.ones(H, device=dev, dtype=torch.bfloat16)  # noqa: E731
+    layers = [B.LayerWeights([ones(), w(s.n_heads * d, H), w(s.n_kv_heads * d, H), w(s.n_kv_heads * d, H),
+                              w(H, s.n_heads * d), ones(), w(I, H), w(I, H), w(H, I)]) for _ in range(s.n_layers)]
+    return B.ModelWeights(w(s.vocab, H), layers, ones())
+
+
 def cpu_baseline(s, model, ids_np, budget_s=12.0):
     """The CPU oracle (numpy float64, as it stands) on whole sequences of the same prefill,
     one after another until about budget_s seconds have passed."""
@@ -276,13 +335,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the long-context and SmolLM3-shaped prefills")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (outside the timed region): "
                          "a known-size reference for hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the whole forward on a single MI355X "
+        print("bench.py measures one GPU only: the library runs the whole forward on a single MI355X "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
@@ -397,6 +457,17 @@ def main():
         "roofline": roofline,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
     }
+
+    if not args.no_other:
+        # the long-context prefill runs the same model; the SmolLM3-3B shape gets weights
+        # drawn on the GPU
+        out["long_prefill"] = other_prefill(B, torch, dev, "long_prefill_bf16", md, reps=10, warmup=2)
+        s5 = S.workload("smollm3_prefill_bf16")
+        m5 = random_model(B, torch, dev, s5)
+        out["smollm3_prefill"] = other_prefill(B, torch, dev, "smollm3_prefill_bf16", m5, reps=5, warmup=1)
+        out["smollm3_prefill"]["data"] = "weights N(0, 0.02^2) drawn on the GPU (torch generator), norm weights 1"
+        del m5
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         sd = S.workload("decode_bf16")
