@@ -372,7 +372,10 @@ static hipError_t launch_attn_g(const AttnArgs &a, hipStream_t s) {  // T: stora
   // Short sequences have few key tiles per query block and too few workgroups to
   // fill the chip: split each block's keys over 4 wave groups (one workgroup per
   // 32 queries). Long ones have work enough; 64 queries per workgroup halve the
-  // K/V traffic per query.
+  // K/V traffic per query, and at head_dim 64 two key groups still pay: the longest
+  // query blocks, which bound the kernel, walk half their keys each (1 x 8192:
+  // 260 -> 162 us; four groups of 32 queries 199, two of 32 257, one of 64 260;
+  // float caches keep one group, whose registers would spill).
   // The split count is capped so that a 2-round ring of KS K+V tile pairs fits LDS.
   constexpr int PAIR = 2 * 64 * D * (int)sizeof(T);
   constexpr bool can4 = 2 * 4 * PAIR <= 160 * 1024 && G * 4 <= 16;
@@ -380,7 +383,9 @@ static hipError_t launch_attn_g(const AttnArgs &a, hipStream_t s) {  // T: stora
   const int keys = a.T + a.q_key_off;
   if (can4 && keys <= 1024) return launch_attn_cfg<T, D, G, 1, can4 ? 4 : 1>(a, s);
   if (can2 && keys <= 4096) return launch_attn_cfg<T, D, G, 1, can2 ? 2 : 1>(a, s);
-  if (G == 1 || (long)a.B * a.n_kv * ((a.T + 63) / 64) >= 256) return launch_attn_cfg<T, D, G, 2, 1>(a, s);
+  const bool big = G == 1 || (long)a.B * a.n_kv * ((a.T + 63) / 64) >= 256;
+  if constexpr (D == 64 && can2 && G <= 3 && sizeof(T) == 2) return big ? launch_attn_cfg<T, D, G, 2, 2>(a, s) : launch_attn_cfg<T, D, G, 1, 2>(a, s);
+  if (big) return launch_attn_cfg<T, D, G, 2, 1>(a, s);
   return launch_attn_cfg<T, D, G, 1, 1>(a, s);
 }
 

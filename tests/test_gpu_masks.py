@@ -196,3 +196,28 @@ def test_generate_ragged_prompts():
             compared += 1
     say(f"tokens compared: {compared} of {3 * n_new}")
     assert compared >= 15
+
+
+def test_long_prefill_key_mask_and_window():
+    """Keys past 4096 (the long-sequence attention configuration: 64-query blocks, two key
+    groups) under a key mask and, on the second block, NoPE with a sliding window: bf16, 2
+    layers, batch 1 x seq 4200 (a ragged last key tile), 192 logit rows against the oracle."""
+    T = 4200
+    s = S.workload("prefill_bf16", n_layers=2, batch=1, seq=T, norm_jitter=0.1, no_rope_interval=2,
+                   sliding_window=1000)
+    say(f"masked + windowed prefill bf16 T={T}")
+    model = S.model_weights(s, 0)
+    md = B.upload_model(model)
+    cfg = B.Config.from_shape(s)
+    ids_np = S.token_ids(s, 0)
+    mask = _mask(np.random.default_rng([T, 7]), 1, T)
+    out = _logits(s, T)
+    B.smol_model_prefill_ex(cfg, md, torch.from_numpy(ids_np).to(DEV), out, 0,
+                            torch.from_numpy(mask.astype(np.uint8)).to(DEV))
+    torch.cuda.synchronize()
+    rows = np.r_[0:64, T // 2:T // 2 + 64, T - 64:T]
+    got = to_np(out)[0, rows]
+    want = O.model_prefill(ids_np, omodel(model), ocfg(s), logit_rows=list(rows), key_mask=mask)
+    r = rel(got, want)
+    say(f"rel = {r:.3e}")
+    assert np.isfinite(got).all() and r <= TOL_BF16
