@@ -220,6 +220,20 @@ def other_prefill(B, torch, dev, name, md, reps, warmup):
             "mfma_frac": round(flops["total"] / t / 1e12 / BF16_PEAK_TFLOPS, 4), "kernels_us": kern}
 
 
+def other_prefills(B, torch, dev, md):
+    """The long-context prefill (the same model as the headline, md) and the SmolLM3-3B
+    shape (weights drawn on the GPU)."""
+    from llama_decoder_only_amd import synthetic as S
+
+    out = {"long_prefill": other_prefill(B, torch, dev, "long_prefill_bf16", md, reps=10, warmup=2)}
+    m5 = random_model(B, torch, dev, S.workload("smollm3_prefill_bf16"))
+    out["smollm3_prefill"] = other_prefill(B, torch, dev, "smollm3_prefill_bf16", m5, reps=5, warmup=1)
+    out["smollm3_prefill"]["data"] = "weights N(0, 0.02^2) drawn on the GPU (torch generator), norm weights 1"
+    del m5
+    torch.cuda.empty_cache()
+    return out
+
+
 def random_model(B, torch, dev, s, seed=1):
     """Device weights of shape s drawn on the GPU (torch's generator, N(0, std^2), norm
     weights 1): for timing only, where the values do not matter and drawing billions
@@ -336,6 +350,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the long-context and SmolLM3-shaped prefills")
+    ap.add_argument("--other-only", action="store_true",
+                    help="time only the long-context and SmolLM3-shaped prefills (a profiling aid; no headline)")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (outside the timed region): "
                          "a known-size reference for hardware byte counters")
@@ -361,6 +377,9 @@ def main():
     cfg = B.Config.from_shape(s)
     model = S.model_weights(s, 0)
     md = B.upload_model(model, dev)
+    if args.other_only:
+        print(json.dumps(other_prefills(B, torch, dev, md)), flush=True)
+        return
     ids_np = S.token_ids(s, 0)
     ids = torch.from_numpy(ids_np).to(dev)
     logits = torch.empty(s.batch, s.seq, s.vocab, dtype=torch.bfloat16, device=dev)
@@ -459,15 +478,7 @@ def main():
     }
 
     if not args.no_other:
-        # the long-context prefill runs the same model; the SmolLM3-3B shape gets weights
-        # drawn on the GPU
-        out["long_prefill"] = other_prefill(B, torch, dev, "long_prefill_bf16", md, reps=10, warmup=2)
-        s5 = S.workload("smollm3_prefill_bf16")
-        m5 = random_model(B, torch, dev, s5)
-        out["smollm3_prefill"] = other_prefill(B, torch, dev, "smollm3_prefill_bf16", m5, reps=5, warmup=1)
-        out["smollm3_prefill"]["data"] = "weights N(0, 0.02^2) drawn on the GPU (torch generator), norm weights 1"
-        del m5
-        torch.cuda.empty_cache()
+        out.update(other_prefills(B, torch, dev, md))
 
     if not args.no_decode:
         sd = S.workload("decode_bf16")

@@ -85,7 +85,12 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return ((r >> 2) << 3)
 // that, every XCD must get work.
 constexpr int SMOL_XCDS = 8;
 __host__ __device__ inline bool xcd_rows(int M) { return M >= 1024; }
-__host__ __device__ inline int rows_per_xcd(int M) { return ((M + SMOL_XCDS - 1) / SMOL_XCDS + 127) / 128 * 128; }
+// An eighth of M rounded up to whole tiles of max(128, BM) rows, so that every XCD's
+// range is made of whole BM-row tiles.
+__host__ __device__ inline int rows_per_xcd(int M, int BM) {
+  const int g = BM > 128 ? BM : 128;
+  return ((M + SMOL_XCDS - 1) / SMOL_XCDS + g - 1) / g * g;
+}
 
 // ---------------------------------------------------------------- RoPE angles
 // (cos, sin) of p * omega, accurate at any position up to float rounding of the

@@ -452,7 +452,7 @@ gemm_kernel(const GemmParams p) {
       break;
     }
     case 2: {  // rows
-      const int mtx = rows_per_xcd(p.M) / BM;
+      const int mtx = rows_per_xcd(p.M, BM) / BM;
       tm = xcd * mtx + local % mtx;
       tn = local / mtx;
       if (tm >= tiles_m) return;  // whole workgroup
@@ -721,7 +721,7 @@ static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
     int tiles;
     switch (xcd_mode(p.M, p.N, BN)) {
       case 1: tiles = SMOL_XCDS * ((tiles_n + SMOL_XCDS - 1) / SMOL_XCDS) * tiles_m; break;
-      case 2: tiles = SMOL_XCDS * (rows_per_xcd(p.M) / BM) * tiles_n; break;
+      case 2: tiles = SMOL_XCDS * (rows_per_xcd(p.M, BM) / BM) * tiles_n; break;
       default: tiles = tiles_m * tiles_n;
     }
     return launch(gemm_kernel<W, BM, BN, WM, WN, RB, EPI, S, KW>, dim3(tiles), dim3(64 * WM * WN * KW), s, p);
@@ -780,9 +780,11 @@ static hipError_t launch_split(GemmParams p, int ks, hipStream_t s) {
 
 // Tile choice, from sweeps on MI355X over the model's shapes (256-byte stages did
 // not pay):
-//   * a plain store with >= 512 tiles of 256 x 256 (lm_head): 256 x 256 in 4 x 4 waves,
-//     which halves the L2 -> LDS bytes per FLOP of 128 x 128 (lm_head at batch 4 x seq
-//     512: 160 us against 200);
+//   * a plain store or SwiGLU with >= 512 tiles of 256 x 256, a residual with >= 256
+//     (one per CU): 256 x 256 in 4 x 4 waves, which halves the L2 -> LDS bytes per
+//     FLOP of 128 x 128 (lm_head at batch 4 x seq 512: 160 us against 200; the
+//     SmolLM3-3B shape at batch 2 x seq 4096: gate/up 1003 -> 870 us, down 451 -> 396,
+//     o_proj 119 -> 105);
 //   * >= 512 tiles of 128 x 128: 128 x 128 with the four waves side by side along N,
 //     so each converted weight fragment feeds four MFMAs;
 //   * >= 512 tiles of 64 x 128: the same 1 x 4 wave layout (gate/up);
@@ -807,7 +809,8 @@ static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
     if (ks > 1) return launch_split<T, EPI>(p, ks, s);
   }
   const long tm128 = (p.M + 127) / 128, tm64 = (p.M + 63) / 64;
-  if (EPI == EPI_STORE && p.N % 256 == 0 && ((p.M + 255) / 256) * (long)(p.N / 256) >= 512)
+  const long t256 = p.N % 256 == 0 ? ((p.M + 255) / 256) * (long)(p.N / 256) : 0;
+  if (((EPI == EPI_STORE || EPI == EPI_SWIGLU) && t256 >= 512) || (EPI == EPI_RESIDUAL && t256 >= 256))
     return launch_cfg<T, 256, 256, 4, 4, 128, EPI, 2, 1>(p, s);
   if (EPI != EPI_QKV_ROPE || p.head_dim == 64)
     if (tm64 * (p.N / 64) < 128 && p.N % 64 == 0) return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 4, 2>(p, s);

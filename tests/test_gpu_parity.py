@@ -279,6 +279,23 @@ def test_long_block_bf16_sampled_rows():
     assert r <= TOL_BF16
 
 
+def test_block_bf16_many_rows_last_tiles():
+    """A bf16 block over M = 26 x 500 = 13000 rows: gate/up runs 256 x 256 tiles with each XCD
+    owning a range of whole tiles, the last one ragged (13000 = 50 x 256 + 200). The last rows of
+    the last sequence, and rows of a middle one, against the oracle."""
+    s = S.workload("prefill_bf16", n_layers=1, batch=26, seq=500, norm_jitter=0.1)
+    say("block bf16 B=26 T=500 (M = 13000)")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.f64))
+    rows = np.r_[0:8, 240:260, 436:500]
+    for b in (12, 25):
+        want = block_rows_oracle(x.f64[b], olayer(layer), ocfg(s), rows)
+        r = rel(got[b, rows], want)
+        say(f"sequence {b}: rel = {r:.3e}")
+        assert r <= TOL_BF16
+
+
 def test_smollm3_block_full_size_sampled_rows():
     """One block of the SmolLM3-3B-shaped prefill at its full size (bf16, batch 2 x seq 4096, H
     2048, 16/4 heads x 128, I 11008): 24 sampled rows of each sequence (first and last key tiles
