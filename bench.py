@@ -67,13 +67,15 @@ def decode_bytes(s, P: int) -> dict:
 def backward_flops(s) -> dict:
     """Algorithmic FLOPs of one block backward (forward recomputed): every linear layer
     three times (the forward product, the data gradient, the weight gradient), and per
-    visible (query, key) pair of every head 12 d (S and P V forward; dV, dP, dQ, dK)."""
+    visible (query, key) pair of every head 12 d (S and P V forward; dV, dP, dQ, dK). By
+    kernel: the forward S and P V; the dQ kernel dP and dQ (S recomputed); the dK/dV
+    kernel dV and dK (S and dP recomputed), so the three add up to the 12 d."""
     M, H, I, d = s.batch * s.seq, s.hidden, s.intermediate, s.head_dim
     qkv = (s.n_heads + 2 * s.n_kv_heads) * d
     lin = 2 * M * H * (qkv + s.n_heads * d + 2 * I + I)
     pairs = s.batch * s.n_heads * s.seq * (s.seq + 1) // 2
     out = {"gemm": 3 * lin, "attention": 12 * d * pairs,
-           "attention_forward": 4 * d * pairs, "attention_dq": 4 * d * pairs, "attention_dkdv": 8 * d * pairs}
+           "attention_forward": 4 * d * pairs, "attention_dq": 4 * d * pairs, "attention_dkdv": 4 * d * pairs}
     out["total"] = out["gemm"] + out["attention"]
     return out
 
