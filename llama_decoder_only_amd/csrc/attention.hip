@@ -387,7 +387,8 @@ static hipError_t launch_attn_g(const AttnArgs &a, hipStream_t s) {  // T: stora
   // (SmolLM3-3B shape at batch 2 x seq 4096: 283 -> 230 us; one group of 32 queries 432)
   const bool d128_long = D == 128 && sizeof(T) == 2 && keys > 2048 && big;
   if (can2 && keys <= 4096 && !d128_long) return launch_attn_cfg<T, D, G, 1, can2 ? 2 : 1>(a, s);
-  if constexpr (D == 64 && can2 && G <= 3 && sizeof(T) == 2) return big ? launch_attn_cfg<T, D, G, 2, 2>(a, s) : launch_attn_cfg<T, D, G, 1, 2>(a, s);
+  if constexpr (D == 64 && can2 && G <= 3 && sizeof(T) == 2)
+    return big ? launch_attn_cfg<T, D, G, 2, 2>(a, s) : launch_attn_cfg<T, D, G, 1, 2>(a, s);
   if (big) return launch_attn_cfg<T, D, G, 2, 1>(a, s);
   return launch_attn_cfg<T, D, G, 1, 1>(a, s);
 }
