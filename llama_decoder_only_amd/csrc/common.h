@@ -78,11 +78,13 @@ __device__ __forceinline__ void load_frag(Frag<float> &f, const float *p) {
 __device__ __forceinline__ int acc_row(int r, int lane) { return ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3); }
 
 // ---------------------------------------------------------------- XCD row ownership
-// Workgroup i of a launch runs on XCD i % 8, and each XCD has its own L2. Row-wise
-// kernels of the prefill (GEMMs, RMSNorm) give XCD x the same row range
-// [x * rows_per_xcd, (x + 1) * rows_per_xcd) of the activations, so the rows one
-// kernel writes are read from the same L2 by the next. Only for M >= 1024: below
-// that, every XCD must get work.
+// Workgroup i of a launch runs on XCD i % 8, and each XCD has its own L2. The
+// prefill's GEMMs give XCD x the row range [x * rows_per_xcd, (x + 1) * rows_per_xcd)
+// of the activations, so each row of A is fetched into one L2 only and shared there
+// by the workgroups of that row (the weights are read once per XCD). Keeping the
+// same ranges from one kernel to the next was measured to buy nothing more: across
+// a kernel boundary the rows come back from MALL either way. Only for M >= 1024:
+// below that, every XCD must get work.
 constexpr int SMOL_XCDS = 8;
 __host__ __device__ inline bool xcd_rows(int M) { return M >= 1024; }
 // An eighth of M rounded up to whole tiles of max(128, BM) rows, so that every XCD's
