@@ -125,7 +125,7 @@ Ws layout(const Dims &D, int op, int B, int T) {
   if (op == SMOL_OP_DECODE) {
     int chunk;
     const int cap = std::min(T, D.max_pos);
-    const int splits = smol::decode_splits(cap, &chunk);
+    const int splits = smol::decode_splits(cap, D.d, D.esz, &chunk);
     w.part = take((size_t)B * D.nq * splits * (D.d + 2) * 4);
   } else {
     w.k = take((size_t)B * D.nkv * T * D.d * D.esz);
@@ -221,7 +221,7 @@ smol_status run_layer(const LayerCtx &c, const smol_layer_weights *w, float *x, 
                                                       (const T *)w->wk, (const T *)w->wv, qo, gpart, s));
   if (decode) {
     int chunk;
-    const int splits = smol::decode_splits(std::min(c.cap, D.max_pos), &chunk);
+    const int splits = smol::decode_splits(std::min(c.cap, D.max_pos), D.d, D.esz, &chunk);
     smol::DecodeAttnArgs da{q, c.kc, c.vc, o, c.cache_len, c.B, D.nq, D.nkv, D.d, c.cap, D.max_pos, splits, chunk,
                             (float *)(c.ws + c.lay.part), c.key_mask, c.mask_ld, window};
     hipError_t e = smol::attention_decode<T>(da, s);

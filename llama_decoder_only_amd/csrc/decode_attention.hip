@@ -20,11 +20,17 @@
 namespace smol {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_CHUNK = 256;
 
-int decode_splits(int cap, int *chunk) {
-  *chunk = DEC_CHUNK;
-  return (cap + DEC_CHUNK - 1) / DEC_CHUNK;
+// Keys per workgroup: 512 for a 2-byte cache at head_dim 64, else 256. At the batch-64
+// step over 2048 keys, 512-key chunks (4 splits, 150 registers, 3 waves per SIMD)
+// leave half the partials to merge: the step went from 1.853 to 1.791 ms although the
+// kernel itself went from 22.5 to 23.2 us (384 keys: 1.917 ms, 1024: 2.456 ms at one
+// wave per SIMD). Other instances would need about 250 registers at 512.
+__host__ __device__ constexpr int dec_chunk(int head_dim, int esz) { return head_dim == 64 && esz == 2 ? 512 : 256; }
+
+int decode_splits(int cap, int head_dim, int esz, int *chunk) {
+  *chunk = dec_chunk(head_dim, esz);
+  return (cap + *chunk - 1) / *chunk;
 }
 
 __device__ __forceinline__ bool decode_pos_ok(int P, int cap, int max_pos) { return P >= 0 && P < cap && P < max_pos; }
@@ -36,7 +42,7 @@ decode_attn_kernel(const DecodeAttnArgs a) {
   constexpr int EPC = 16 / sizeof(T);
   constexpr int LPK = D / EPC;             // lanes per key row
   constexpr int KPP = DEC_THREADS / LPK;   // keys per pass
-  constexpr int CHUNK = DEC_CHUNK;
+  constexpr int CHUNK = dec_chunk(D, sizeof(T));
   static_assert(64 % LPK == 0, "a key row must stay inside one wavefront");
 
   __shared__ float S[G][CHUNK];

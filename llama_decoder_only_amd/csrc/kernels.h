@@ -116,7 +116,7 @@ struct DecodeAttnArgs {
 };
 template <typename T>
 hipError_t attention_decode(const DecodeAttnArgs &a, hipStream_t s);
-int decode_splits(int cap, int *chunk);
+int decode_splits(int cap, int head_dim, int esz, int *chunk);
 
 // Next-token choice per row of logits (smol_sample in smol.h).
 template <typename T>

@@ -132,16 +132,17 @@ def test_prefill_key_mask_with_cache_and_fully_masked_query():
 @pytest.mark.parametrize("dtype,batch", [("f32", 3), ("bf16", 3), ("f32", 48), ("bf16", 48)])
 def test_decode_key_mask(dtype, batch):
     """At batch 3 and at batch 48 (144 sequence / kv-head pairs, near the benchmarked
-    decode's 192)."""
+    decode's 192), over 531 keys: two key chunks of the bf16 kernel (512 + 19), three of
+    the float one (256 + 256 + 19)."""
     name = "model_f32" if dtype == "f32" else "prefill_bf16"
-    s = S.workload(name, n_layers=2, batch=batch, seq=271, norm_jitter=0.1)
+    s = S.workload(name, n_layers=2, batch=batch, seq=531, norm_jitter=0.1)
     say(f"masked decode {dtype}")
     model = S.model_weights(s, 0)
     md = B.upload_model(model)
     cfg = B.Config.from_shape(s)
     ids_np = S.token_ids(s, 0)
     ids = torch.from_numpy(ids_np).to(DEV)
-    P, cap = 270, 300  # keys 0 .. 270: two key chunks of the decode kernel (256 + 15)
+    P, cap = 530, 560  # keys 0 .. 530
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     kc, vc = _caches(s, cap, tdt)
     B.smol_model_prefill_ex(cfg, md, ids[:, :P].contiguous(), _logits(s, P), 0, None, kc, vc)
@@ -167,6 +168,33 @@ def test_decode_key_mask(dtype, batch):
     B.smol_decode_step(cfg, md, ids[:, P].contiguous(), cl, kc, vc, out3)
     torch.cuda.synchronize()
     assert torch.equal(out2, out3)
+
+
+def test_decode_window_skips_whole_chunk():
+    """bf16 at head_dim 64 (512-key chunks), NoPE with a 100-key window on the second block,
+    decode at P = 700: that block's first chunk (keys 0 .. 511) lies wholly before the window
+    and contributes an empty partial, the second holds keys 512 .. 700. Against the oracle."""
+    s = S.workload("prefill_bf16", n_layers=2, batch=3, seq=701, norm_jitter=0.1, no_rope_interval=2,
+                   sliding_window=100)
+    say("windowed decode bf16 P=700")
+    model = S.model_weights(s, 0)
+    md = B.upload_model(model)
+    cfg = B.Config.from_shape(s)
+    ids_np = S.token_ids(s, 0)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    P, cap = 700, 1024
+    kc, vc = _caches(s, cap, torch.bfloat16)
+    B.smol_model_prefill_ex(cfg, md, ids[:, :P].contiguous(), _logits(s, P), 0, None, kc, vc)
+    out = torch.empty(3, s.vocab, dtype=torch.bfloat16, device=DEV)
+    cl = torch.full((3,), P, dtype=torch.int32, device=DEV)
+    B.smol_decode_step(cfg, md, ids[:, P].contiguous(), cl, kc, vc, out)
+    torch.cuda.synchronize()
+    om = omodel(model)
+    _, cache = O.model_prefill(ids_np[:, :P], om, ocfg(s), keep_cache=True)
+    want, _, _ = O.decode_step(ids_np[:, P], P, om, ocfg(s), [c[0] for c in cache], [c[1] for c in cache])
+    r = rel(to_np(out), want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_BF16
 
 
 def test_generate_ragged_prompts():
