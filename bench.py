@@ -158,15 +158,16 @@ def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_prefill_b4s512_gemms.md")
+TRAFFIC_DECODE_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b64.md")
 
 
-def measured_traffic(key: str):
+def measured_traffic(key: str, path: str = TRAFFIC_PROFILE):
     """HBM bytes per launch of a kernel from the committed counter summary (FETCH_SIZE +
     WRITE_SIZE passes scaled by a plain copy of known size), or None when the kernel
     sources have changed since the counters were taken."""
     import hashlib
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(path).read()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines()
@@ -529,6 +530,7 @@ def main():
             ms, n = _kernel_time(B, "decode_attention", dstep, torch)
         att_s = ms / max(n, 1) * 1e-3
         att_gbps = db["decode_attention_per_launch"] / att_s / 1e9
+        dtraffic = measured_traffic("decode_attention-traffic-bytes-per-launch", TRAFFIC_DECODE_PROFILE)
         out["decode"] = {
             "workload": "decode step: batch 64, 2047 cached positions (+1 new), 30 layers, bf16",
             "timing": dmode + ", cold: MALL/L2 flushed by a 512 MiB write before each step (median)",
@@ -542,7 +544,9 @@ def main():
             "hbm_frac": round(db["total"] / d_s / 1e9 / HBM_PEAK_GBPS, 4),
             "roofline": {"bound": "hbm", "kernel": "decode_attention", "achieved": round(att_gbps, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(att_gbps / HBM_PEAK_GBPS, 4),
-                         "traffic": None, "algorithmic_bytes_per_launch": db["decode_attention_per_launch"],
+                         "traffic": dtraffic,
+                         "traffic_source": os.path.relpath(TRAFFIC_DECODE_PROFILE, ROOT) if dtraffic is not None else None,
+                         "algorithmic_bytes_per_launch": db["decode_attention_per_launch"],
                          "avg_launch_us": round(att_s * 1e6, 2)},
         }
         # next-token choice on the decode step's logits [64, 49152] (smol_sample), and the
