@@ -159,6 +159,7 @@ def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_prefill_b4s512_gemms.md")
 TRAFFIC_DECODE_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b64.md")
+TRAFFIC_BACKWARD_PROFILE = os.path.join(ROOT, "profiles", "traffic_block_backward_b4s512.md")
 
 
 def measured_traffic(key: str, path: str = TRAFFIC_PROFILE):
@@ -323,6 +324,7 @@ def backward_section(B, S, torch, dev, stream, args):
     for k, f in ach.items():
         kern[k]["tflops"] = round(f / (kern[k]["us"] * 1e-6) / 1e12, 2) if kern[k]["us"] > 0 else None
     dom = max(ach, key=lambda k: kern[k]["us"])
+    btraffic = measured_traffic("bw_gemm-traffic-bytes-per-call", TRAFFIC_BACKWARD_PROFILE)
     dom_tf = kern[dom]["tflops"] or 0.0
     del w, x, dy, dx, g, ws
     return {
@@ -337,8 +339,11 @@ def backward_section(B, S, torch, dev, stream, args):
         "mfma_f32_frac": round(fl["total"] / t_s / 1e12 / F32_PEAK_TFLOPS, 4),
         "kernels": kern,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": dom_tf, "peak": F32_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(dom_tf / F32_PEAK_TFLOPS, 4), "traffic": None,
-                     "note": "summed over the class's launches in one call"},
+                     "unit": "TFLOP/s", "frac": round(dom_tf / F32_PEAK_TFLOPS, 4),
+                     "traffic": btraffic if dom == "bw_gemm" else None,
+                     "traffic_source": (os.path.relpath(TRAFFIC_BACKWARD_PROFILE, ROOT)
+                                        if dom == "bw_gemm" and btraffic is not None else None),
+                     "note": "summed over the class's launches in one call (traffic: with its K-split reductions)"},
     }
 
 
