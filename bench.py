@@ -162,11 +162,14 @@ TRAFFIC_DECODE_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b64.md")
 TRAFFIC_BACKWARD_PROFILE = os.path.join(ROOT, "profiles", "traffic_block_backward_b4s512.md")
 
 
-def measured_traffic(key: str, path: str = TRAFFIC_PROFILE):
+def measured_traffic(key: str, path=None):
     """HBM bytes per launch of a kernel from the committed counter summary (FETCH_SIZE +
     WRITE_SIZE passes scaled by a plain copy of known size), or None when the kernel
-    sources have changed since the counters were taken."""
+    sources have changed since the counters were taken. path None: the prefill GEMM
+    summary, looked up when called (not when this module is imported)."""
     import hashlib
+    if path is None:
+        path = TRAFFIC_PROFILE
     try:
         text = open(path).read()
     except OSError:

@@ -640,6 +640,61 @@ def pin_choice_brute_force():
         assert c.token == _brute_choice(l.tolist(), t, k, p, u), (trial, l, t, k, p, u)
 
 
+def pin_greedy_generate_brute_force():
+    """The greedy loop by full recompute (abi96062 model.py, SmolLM2Model.generate at
+    temperature 0: the whole sequence again each step, the last position's argmax
+    appended) against the scalar brute-force forward with an argmax written out by
+    comparisons (lowest index among equal maxima): two prompt lengths, three steps,
+    every sequence's token at every step, and the top-2 gaps the loop reports."""
+    cfg = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=2, vocab=16, max_pos=32,
+                   rms_eps=1e-5, rope_theta=1e5)
+    rng = _rng(57)
+    mw = _rand_model(cfg, rng, std=0.6, norm_jitter=0.3)
+    for T in (2, 5):
+        prompt = rng.integers(0, cfg.vocab, size=(2, T))
+        out, gaps = G.greedy_generate(prompt, 3, mw, cfg)
+        seqs = [list(map(int, row)) for row in prompt]
+        for j in range(3):
+            logits = _brute_force_logits(cfg, mw, seqs)  # [B, len, V]
+            for b in range(2):
+                last = logits[b, len(seqs[b]) - 1]
+                best = 0
+                for v in range(1, cfg.vocab):
+                    if last[v] > last[best]:
+                        best = v
+                srt = sorted(last)
+                assert out[j, b] == best, (T, j, b)
+                assert abs(gaps[j, b] - (srt[-1] - srt[-2])) < 1e-9
+            for b in range(2):
+                seqs[b].append(int(out[j, b]))
+
+
+def pin_masked_decode_equals_masked_prefill():
+    """A decode step under a padding mask (Sualeh77 model.py, "4. Attention": the
+    attention_mask also applies on the cache branch) equals the masked prefill of one
+    more token at that position and the scalar brute force; the cache it starts from
+    is the masked prefill's, and the appended k', v equal the masked prefill's."""
+    cfg = O.Config(hidden=12, n_heads=3, n_kv_heads=1, intermediate=8, n_layers=2, vocab=16, max_pos=32,
+                   rms_eps=1e-5, rope_theta=1e5)
+    rng = _rng(59)
+    mw = _rand_model(cfg, rng, std=0.6, norm_jitter=0.3)
+    B, P = 2, 6
+    ids = rng.integers(0, cfg.vocab, size=(B, P + 1))
+    mask = np.array([[True, False, True, True, False, True, True], [True, True, False, False, True, False, True]])
+    _, cache = O.model_prefill(ids[:, :P], mw, cfg, keep_cache=True, key_mask=mask[:, :P])
+    logits, nk, nv = O.decode_step(ids[:, P], P, mw, cfg, [c[0] for c in cache], [c[1] for c in cache],
+                                   key_mask=mask)
+    full, cache_full = O.model_prefill(ids, mw, cfg, keep_cache=True, key_mask=mask)
+    brute = _brute_force_logits(cfg, mw, ids.tolist(), mask.tolist())
+    assert np.isfinite(logits).all()
+    assert _rel(logits, full[:, P]) < 1e-12 and _rel(logits, brute[:, P]) < 1e-12
+    for li in range(cfg.n_layers):
+        assert np.allclose(nk[li], cache_full[li][0][:, :, P], rtol=1e-12)
+        assert np.allclose(nv[li], cache_full[li][1][:, :, P], rtol=1e-12)
+    unmasked, _, _ = O.decode_step(ids[:, P], P, mw, cfg, [c[0] for c in cache], [c[1] for c in cache])
+    assert _rel(unmasked, logits) > 1e-3  # the mask matters on the cache branch
+
+
 # ---------------------------------------------------------------- block backward
 # (oracle/backward.py: the chain rule through the block of oracle/smol.py)
 
@@ -797,6 +852,8 @@ ALL_PINS = [
     pin_inverse_cdf_stratified,
     pin_inverse_cdf_steps,
     pin_choice_brute_force,
+    pin_greedy_generate_brute_force,
+    pin_masked_decode_equals_masked_prefill,
     pin_backward_finite_differences,
     pin_backward_variants_finite_differences,
     pin_backward_vs_transformers_autograd,
@@ -805,6 +862,7 @@ ALL_PINS = [
 
 SAMPLER_PINS = [p for p in ALL_PINS if p.__name__ in (
     "pin_greedy_ties_and_nan", "pin_top_k_keeps_ties", "pin_top_p_hand_values", "pin_top_p_after_top_k",
-    "pin_inverse_cdf_stratified", "pin_inverse_cdf_steps", "pin_choice_brute_force")]
+    "pin_inverse_cdf_stratified", "pin_inverse_cdf_steps", "pin_choice_brute_force",
+    "pin_greedy_generate_brute_force")]
 
 BACKWARD_PINS = [p for p in ALL_PINS if p.__name__.startswith("pin_backward")]

@@ -46,10 +46,3 @@ def test_committed_traffic_profile_is_well_formed():
     assert "down-traffic-bytes-per-launch: " in text and "source-sha256: " in text
     for f in text.split("source-files: ", 1)[1].split("\n", 1)[0].split():
         assert os.path.exists(os.path.join(ROOT, f)), f
-
-
-def test_more_than_one_gpu_is_refused():
-    import subprocess
-    import sys
-    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
-    assert r.returncode == 2 and "one GPU" in r.stderr

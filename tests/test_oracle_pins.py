@@ -147,6 +147,13 @@ def _lm_head_no_final_norm(x, final_norm, E, cfg):
     return np.asarray(x, F64) @ np.asarray(E, F64).T
 
 
+_orig_decode_step = O.decode_step
+
+
+def _decode_step_ignores_mask(ids, cache_len, mw, cfg, k_cache, v_cache, key_mask=None):
+    return _orig_decode_step(ids, cache_len, mw, cfg, k_cache, v_cache)
+
+
 MISTAKES = {
     "rmsnorm eps outside the root": ("rms_norm", _rms_eps_outside),
     "rmsnorm sum instead of mean": ("rms_norm", _rms_sum_not_mean),
@@ -168,6 +175,7 @@ MISTAKES = {
     "rope applied to v": ("attention_sublayer", _attention_rotates_v),
     "o_proj transposed": ("attention_sublayer", _attention_wo_transposed),
     "final norm dropped": ("lm_head", _lm_head_no_final_norm),
+    "decode step ignores the padding mask": ("decode_step", _decode_step_ignores_mask),
 }
 
 
@@ -265,6 +273,31 @@ def _make_next_token(side="right", temp_mul=False, greedy_last=False):
     return next_token
 
 
+def _make_greedy_generate(row_off=1, append_first=False):
+    """The recompute loop with a slip: logits read from position T - row_off, or the
+    previous token appended before the step's forward instead of after it."""
+    def greedy_generate(prompt, max_new, mw, cfg):
+        ids = np.asarray(prompt, dtype=np.int64)
+        B = ids.shape[0]
+        out = np.zeros((max_new, B), dtype=np.int64)
+        gaps = np.zeros((max_new, B))
+        prev = ids[:, -1].copy()
+        for j in range(max_new):
+            if append_first:
+                ids = np.concatenate([ids, prev[:, None]], axis=1)
+            T = ids.shape[1]
+            row = O.model_prefill(ids, mw, cfg, logit_rows=[b * T + T - row_off for b in range(B)])
+            for b in range(B):
+                out[j, b] = G.next_token(row[b], 0.0).token
+                top2 = np.sort(row[b])[-2:]
+                gaps[j, b] = top2[1] - top2[0]
+            prev = out[j].copy()
+            if not append_first:
+                ids = np.concatenate([ids, out[j][:, None]], axis=1)
+        return out, gaps
+    return greedy_generate
+
+
 GEN_MISTAKES = {
     "top-k keeps exactly k tokens (drops ties)": ("top_k_keep", _top_k_exactly_k),
     "top-p drops the token that crosses p": ("top_p_keep", _top_p_without_crossing_token),
@@ -273,6 +306,8 @@ GEN_MISTAKES = {
     "draw takes the first cdf >= u": ("next_token", _make_next_token(side="left")),
     "temperature multiplies the logits": ("next_token", _make_next_token(temp_mul=True)),
     "greedy takes the last maximum": ("next_token", _make_next_token(greedy_last=True)),
+    "greedy loop reads the second-to-last position": ("greedy_generate", _make_greedy_generate(row_off=2)),
+    "greedy loop appends the token before the step": ("greedy_generate", _make_greedy_generate(append_first=True)),
 }
 
 
