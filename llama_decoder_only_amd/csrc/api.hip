@@ -11,12 +11,13 @@
 // The model gathers the embedding before the blocks and applies the final RMSNorm
 // and the tied head after them (abi96062 model.py, SmolLM2Model.forward). Every
 // RMSNorm is deferred (kernels.h, NormIn / NormOut): the kernel that last wrote x
-// leaves xs = w * x * r_old and the new row sums of squares, and the GEMM that reads
+// leaves xs = w * x * r_old * 2^-8 and the new row sums of squares, and the GEMM that reads
 // xs rescales its output rows. Five launches per block, no separate norm kernels.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -874,7 +875,11 @@ smol_status smol_block_backward(const smol_config *cfg, const smol_layer_weights
 }
 
 const char *smol_status_string(smol_status s) {
-  switch (s) {
+  // A C caller may pass any int; in C++ an enum object outside the enumerators' range
+  // is undefined, so the value is read as the int it is.
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case SMOL_OK: return "ok";
     case SMOL_ERR_INVALID_ARG: return "invalid argument";
     case SMOL_ERR_UNSUPPORTED: return "unsupported shape";

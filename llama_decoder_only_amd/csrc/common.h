@@ -36,6 +36,22 @@ template <typename W> struct OperandOf { using type = W; };
 template <> struct OperandOf<bf16> { using type = f16; };
 template <typename W> using Act = typename OperandOf<W>::type;
 
+// ---------------------------------------------------------------- deferred-norm operand scale
+// The deferred RMSNorm operand xs (kernels.h, NormIn / NormOut) is stored times
+// SMOL_XS_SCALE = 2^-8, and the GEMM that reads it multiplies its output rows by
+// 2^8 (exact power-of-two scalings). A normalised row has |value| <= sqrt(H) * max|w|
+// (<= 45 |w| at H = 2048); a residual epilogue stores w * x_new * r_old, which grows
+// with the row's rms growth g over one update, so an unscaled float16 xs overflows
+// (65504) once g passes about 1500 / max|w|. At 2^-8 the limit is 256 times higher
+// (g up to ~4e5 / max|w| at H = 2048), while typical values (~2^-8) stay normal in
+// float16 (down to 2^-14) and the elements that become subnormal keep the absolute
+// spacing (2^-24) of the bottom of the normal range, far below the rounding error of
+// the row's typical elements: the products do not lose accuracy. A row whose rms
+// shrinks by more than ~2^-6 in one update starts to lose float16 precision
+// gradually (no overflow, no NaN).
+constexpr float SMOL_XS_SCALE = 0.00390625f;  // 2^-8
+constexpr float SMOL_XS_UNSCALE = 256.0f;     // 2^8
+
 // ---------------------------------------------------------------- fragments
 // A 32x32x16 MFMA step takes, per lane, 8 consecutive K values of one row of A
 // (row = lane % 32, K chunk = lane / 32) and likewise of one column of B. Frag<T>

@@ -16,11 +16,12 @@
 // RMSNorm, deferred (u = w * x * r with r = 1 / sqrt(mean(x^2) + eps) per row,
 // abi96062 components.py, RMSNorm). A residual epilogue, which holds the updated
 // rows x only one BN-column slice at a time, cannot know r yet; it stores
-// xs = w_next * x * r_old, with r_old the row's r before this update (close to r,
-// so xs stays in the operand type's range at any scale of x), plus the row's sums
-// of squares per 64 columns. The GEMM that reads xs as A then scales each output
-// row by r / r_old, both taken from those partial sums, which makes its result
-// u B^T up to the one rounding of xs.
+// xs = w_next * x * r_old * 2^-8, with r_old the row's r before this update (the
+// fixed 2^-8 leaves float16 room for a row whose rms grows several thousand times in
+// one update; common.h, SMOL_XS_SCALE), plus the row's sums of squares per 64
+// columns. The GEMM that reads xs as A then scales each output row by r / r_old * 2^8,
+// both taken from those partial sums, which makes its result u B^T up to the one
+// rounding of xs.
 //
 // When the K loop ends, the float accumulators go to LDS (reusing the staging
 // buffers) and the epilogue walks the tile row-major, so every global write is a
@@ -215,12 +216,14 @@ __device__ __forceinline__ void prefetch_qkv(const GemmParams &p, int m0, int ti
   }
 }
 
-// Deferred-RMSNorm factor of one row: r_old for a residual epilogue (it scales xs),
-// r(ss_new) / r(ss_old) for a GEMM that reads xs.
+// Deferred-RMSNorm factor of one row: r_old * 2^-8 for a residual epilogue (it
+// scales xs, stored at SMOL_XS_SCALE), r(ss_new) / r(ss_old) * 2^8 for a GEMM that
+// reads xs.
 template <int EPI>
 __device__ __forceinline__ float row_factor(const GemmParams &p, int row) {
   const float r_old = row_r(p.ss_old, p.M, row, p.ss_cols, p.eps);
-  return EPI == EPI_RESIDUAL ? r_old : row_r(p.ss_new, p.M, row, p.ss_cols, p.eps) / r_old;
+  return EPI == EPI_RESIDUAL ? r_old * SMOL_XS_SCALE
+                             : row_r(p.ss_new, p.M, row, p.ss_cols, p.eps) / r_old * SMOL_XS_UNSCALE;
 }
 
 // The epilogue of ER rows of a tile, from the float accumulator sums in LDS (tile,

@@ -26,10 +26,11 @@ struct QkvOut {
 
 // The deferred RMSNorm u = w * x * r, r = 1 / sqrt(mean(x^2) + eps) per row of the
 // float residual stream x [M, H]. Whoever updates x also leaves, for the next norm,
-//   xs [M, H] (operand type) = w * x * r_old, r_old: the row's r before the update;
+//   xs [M, H] (operand type) = w * x * r_old * 2^-8, r_old: the row's r before the
+//   update (2^-8 = SMOL_XS_SCALE, common.h: float16 headroom for large growth);
 //   the row sums of squares of the new x as H/64 partials, ss[j * M + row] over
 //   columns [64 j, 64 j + 64) (ss_new; ss_old keeps those from before the update).
-// A GEMM with xs as its A operand scales output row m by r(ss_new) / r(ss_old).
+// A GEMM with xs as its A operand scales output row m by r(ss_new) / r(ss_old) * 2^8.
 struct NormIn {
   const float *ss_new, *ss_old;  // ss_new == nullptr: A is used as it is
   float eps;
@@ -63,7 +64,7 @@ size_t gemm_part_floats(int M, int N, int K, int esz);  // 0: that GEMM does not
 
 // x[m] = E[ids[m]] (ids != nullptr: the embedding gather) or x[m] = src[m], and what
 // the first deferred RMSNorm reads: the row sums of squares into both ss_new and
-// ss_old, and xs = w * x * r with the row's own r (w == nullptr: no xs).
+// ss_old, and xs = w * x * r * 2^-8 with the row's own r (w == nullptr: no xs).
 // The RoPE angles of every row, computed once per forward: cs[row * half + i] =
 // (cos, sin)(pos(row) * inv_freq[i]), pos(row) = cache_len[row] when cache_len != nullptr
 // (a decode step) else pos0 + row % seq.

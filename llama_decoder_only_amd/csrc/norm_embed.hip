@@ -10,8 +10,8 @@ namespace smol {
 
 // One wavefront per row: x[row] = E[ids[row]] (ids != nullptr) or x[row] = src[row];
 // the row's sums of squares per 64 columns into ss_new and ss_old ([H/64, M]); and,
-// when w != nullptr, xs[row] = w * x * r with the row's r -- the input of the first
-// deferred RMSNorm; and the row's RoPE (cos, sin) table (RopeIn). An id outside
+// when w != nullptr, xs[row] = w * x * r * 2^-8 with the row's r -- the input of the
+// first deferred RMSNorm (stored at SMOL_XS_SCALE, as every xs); and the row's RoPE (cos, sin) table (RopeIn). An id outside
 // [0, V) makes the row (and its sums) NaN.
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -44,7 +44,7 @@ rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const f
     }
   }
   if (!w) return;
-  const float r = 1.0f / sqrtf(tot / (float)H + eps);
+  const float r = 1.0f / sqrtf(tot / (float)H + eps) * SMOL_XS_SCALE;  // xs is stored times 2^-8
   Act<T> *ur = xs + (size_t)row * H;
   for (int i = lane; i < H; i += 64) ur[i] = from_f32<Act<T>>(to_f32(w[i]) * (xr[i] * r));
 }

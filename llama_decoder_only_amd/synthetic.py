@@ -122,6 +122,12 @@ def _store(x64: np.ndarray, dtype: str) -> Tensor:
     return Tensor(x32, "f32")
 
 
+def stored(x64: np.ndarray, dtype: str) -> Tensor:
+    """Values rounded to a storage format ("f32" or "bf16"), e.g. a test's edited copy
+    of a drawn tensor."""
+    return _store(np.asarray(x64, np.float64), dtype)
+
+
 def normal(s: Shape, seed: int, layer: int, tensor_id: int, shape, std: float) -> Tensor:
     x = _rng(s, seed, layer, tensor_id).standard_normal(size=shape) * std
     return _store(x, s.dtype)
