@@ -17,7 +17,9 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsmol.so")
+# The in-tree library; SMOL_LIB_PATH names another build of the same sources (the
+# host-sanitizer copy that build.py --sanitize-host writes, for the CPU ABI tests).
+LIB_PATH = os.environ.get("SMOL_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsmol.so")
 
 SMOL_OK, SMOL_ERR_INVALID_ARG, SMOL_ERR_UNSUPPORTED, SMOL_ERR_WORKSPACE, SMOL_ERR_HIP = range(5)
 SMOL_F32, SMOL_BF16 = 0, 1
