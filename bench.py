@@ -160,6 +160,7 @@ def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_prefill_b4s512_gemms.md")
 TRAFFIC_DECODE_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b64.md")
 TRAFFIC_BACKWARD_PROFILE = os.path.join(ROOT, "profiles", "traffic_block_backward_b4s512.md")
+TRAFFIC_OTHER_PROFILE = os.path.join(ROOT, "profiles", "traffic_prefill_smollm3_b2s4096.md")
 
 
 def measured_traffic(key: str, path=None):
@@ -217,14 +218,35 @@ def other_prefill(B, torch, dev, name, md, reps, warmup):
     with torch.cuda.stream(stream):
         for k in ("qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head"):
             kms, n = _kernel_time(B, k, step, torch)
-            kern[k] = round(1e3 * kms / max(n, 1), 2)
+            kern[k] = {"total_ms": kms, "launches": n, "avg_us": 1e3 * kms / max(n, 1)}
     del ws, logits
+    rl = prefill_rooflines(kern, flops)
+    dom = max(rl, key=lambda k: kern[k]["total_ms"])
     return {"workload": f"{name}: {s.n_layers} layers, hidden {s.hidden}, {s.n_heads}/{s.n_kv_heads} heads x "
                         f"{s.head_dim}, intermediate {s.intermediate}, vocab {s.vocab}; batch {s.batch} x seq {s.seq}",
             "timing": "hip_graph (median of reps)", "ms_per_step": round(t * 1e3, 3),
             "tokens_per_s": round(s.batch * s.seq / t, 1), "rep_ms": _pct(ms),
             "algorithmic_gflop_per_step": round(flops["total"] / 1e9, 1),
-            "mfma_frac": round(flops["total"] / t / 1e12 / BF16_PEAK_TFLOPS, 4), "kernels_us": kern}
+            "mfma_frac": round(flops["total"] / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
+            "roofline": dict(rl[dom], kernel=dom,
+                             traffic=measured_traffic(f"{name}:{dom}-traffic-bytes-per-launch", TRAFFIC_OTHER_PROFILE)),
+            "rooflines": rl}
+
+
+def prefill_rooflines(kern, flops):
+    """Per kernel class of a prefill: algorithmic FLOPs per launch over the class's average
+    launch duration, against the bf16 MFMA peak."""
+    out = {}
+    for k, v in kern.items():
+        if k not in flops["per_launch"] or v["launches"] == 0:
+            continue
+        ach = flops["per_launch"][k] / (v["avg_us"] * 1e-6) / 1e12
+        out[k] = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(ach / BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(v["avg_us"], 2),
+                  "launches": v["launches"], "total_ms": round(v["total_ms"], 4),
+                  "algorithmic_flop_per_launch": flops["per_launch"][k]}
+    return out
 
 
 def other_prefills(B, torch, dev, md):
@@ -258,16 +280,52 @@ def random_model(B, torch, dev, s, seed=1):
     return B.ModelWeights(w(s.vocab, H), layers, ones())
 
 
-def cpu_baseline(s, model, ids_np, budget_s=12.0):
-    """The CPU oracle (numpy float64, as it stands) on whole sequences of the same prefill,
-    one after another until about budget_s seconds have passed."""
-    import oracle.smol as O
+def _oracle_cfg(O, s):
+    return O.Config(hidden=s.hidden, n_heads=s.n_heads, n_kv_heads=s.n_kv_heads, intermediate=s.intermediate,
+                    n_layers=s.n_layers, vocab=s.vocab, max_pos=s.max_pos, rms_eps=s.rms_eps, rope_theta=s.rope_theta)
+
+
+def _oracle_layer(O, layer):
+    return O.LayerWeights(**{n: getattr(layer, n).f64 for n in layer.NAMES})
+
+
+def _host_info():
+    """CPU model, BLAS library and its thread count, as the oracle's numpy sees them."""
     from threadpoolctl import threadpool_info
 
-    cfg = O.Config(hidden=s.hidden, n_heads=s.n_heads, n_kv_heads=s.n_kv_heads, intermediate=s.intermediate,
-                   n_layers=s.n_layers, vocab=s.vocab, max_pos=s.max_pos, rms_eps=s.rms_eps, rope_theta=s.rope_theta)
-    om = O.ModelWeights(embed=model.embed.f64,
-                        layers=[O.LayerWeights(**{n: getattr(l, n).f64 for n in l.NAMES}) for l in model.layers],
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    vendor = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in blas})) or "unknown"
+    return model, vendor, int(threads)
+
+
+def cpu_baseline(s, model, ids_np, budget_s=8.0):
+    """The CPU oracle (numpy float64, as it stands) timed on the host, on bounded samples.
+
+    Headline (the prefill workload of the metric): whole sequences of the batch 4 x seq
+    512 prefill, one after another until about budget_s seconds have passed. `configs`
+    gives the other workloads, each a stated sample: the float32 block and the 30-layer
+    float32 model at batch 1 x seq 128 (whole); the seq-8192 prefill as one block over
+    the whole sequence plus the head on 256 rows, scaled to 30 blocks and 8192 rows
+    (extrapolated: the blocks cost the same); the decode step for 8 of its 64 sequences
+    (2047 cached positions, scaled to 64; the cache values of one layer serve all 30);
+    the SmolLM3-3B shape as one block over one sequence of 4096 plus the head on 128 rows,
+    scaled to 36 blocks, 2 sequences and 8192 rows (extrapolated)."""
+    import oracle.smol as O
+    from llama_decoder_only_amd import synthetic as S
+
+    cpu, blas, threads = _host_info()
+    cfg = _oracle_cfg(O, s)
+    om = O.ModelWeights(embed=model.embed.f64, layers=[_oracle_layer(O, l) for l in model.layers],
                         final_norm=model.final_norm.f64)
     t0 = time.perf_counter()
     done = 0
@@ -277,10 +335,77 @@ def cpu_baseline(s, model, ids_np, budget_s=12.0):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": done * s.seq / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {ids_np.shape[0]} sequences x {s.seq} tokens, full 30-layer forward and all "
-                      f"logits, numpy float64, {dt:.1f} s; host has {os.cpu_count()} logical CPUs"}
+    out = {"value": done * s.seq / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} of {ids_np.shape[0]} sequences x {s.seq} tokens, full 30-layer forward and all "
+                     f"logits, numpy float64, {dt:.1f} s; host has {os.cpu_count()} logical CPUs",
+           "cpu_model": cpu, "blas": blas, "configs": {}}
+    cf = out["configs"]
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    # float32 block and 30-layer model, batch 1 x seq 128: whole
+    s1 = S.workload("block_f32")
+    l1 = _oracle_layer(O, S.layer_weights(s1, 0, 0))
+    x1 = S.hidden_states(s1, 0).f64
+    t = timed(lambda: O.block_forward(x1, l1, _oracle_cfg(O, s1)))
+    cf["block_f32"] = {"tokens_per_s": round(s1.seq / t, 1), "seconds": round(t, 3), "sample": "whole (1 x 128)"}
+    s1b = S.workload("model_f32")
+    m1b = S.model_weights(s1b, 0)
+    om1b = O.ModelWeights(embed=m1b.embed.f64, layers=[_oracle_layer(O, l) for l in m1b.layers],
+                          final_norm=m1b.final_norm.f64)
+    ids1b = S.token_ids(s1b, 0)
+    t = timed(lambda: O.model_prefill(ids1b, om1b, _oracle_cfg(O, s1b)))
+    cf["model_f32"] = {"tokens_per_s": round(s1b.seq / t, 1), "seconds": round(t, 3), "sample": "whole (1 x 128)"}
+    del m1b, om1b
+    # seq-8192 prefill: one block over the whole sequence, the head on 256 rows
+    s3 = S.workload("long_prefill_bf16")
+    ids3 = S.token_ids(s3, 0)
+    x3 = O.embed(ids3, om.embed)
+    tb = timed(lambda: O.block_forward(x3, om.layers[0], cfg, layer=0))
+    th = timed(lambda: O.lm_head(x3[0, :256], om.final_norm, om.embed, cfg))
+    t = tb * s3.n_layers + th * s3.seq / 256
+    cf["long_prefill_bf16"] = {"tokens_per_s": round(s3.seq / t, 1), "seconds": round(t, 2), "extrapolated": True,
+                               "sample": f"one block at 1 x 8192 ({tb:.1f} s) x 30 + the head on 256 rows "
+                                         f"({th:.2f} s) x 32"}
+    del x3
+    # decode step: 8 of 64 sequences over 2047 cached positions
+    s4 = S.workload("decode_bf16")
+    nb = 8
+    kc, vc = S.kv_cache_values(S.workload("decode_bf16", batch=nb), 0, 0, s4.cache_len)
+    kc64, vc64 = kc.f64, vc.f64
+    dids = S.token_ids(s4, 0, S.T_DECODE_IDS)[:nb, 0]
+    t = timed(lambda: O.decode_step(dids, s4.cache_len, om, cfg, [kc64] * s4.n_layers, [vc64] * s4.n_layers))
+    t *= s4.batch / nb
+    cf["decode_bf16"] = {"tokens_per_s": round(s4.batch / t, 1), "ms_per_step": round(t * 1e3, 1),
+                         "extrapolated": True,
+                         "sample": f"{nb} of {s4.batch} sequences (2047 cached), scaled x {s4.batch // nb}; "
+                                   "one layer's cache values serve all 30 layers"}
+    del kc, vc, kc64, vc64
+    # SmolLM3-3B shape: one block over one sequence of 4096, the head on 128 rows
+    # (constant weights: drawing 3 G normals would take minutes, and the oracle's time
+    # does not depend on the values)
+    s5 = S.workload("smollm3_prefill_bf16")
+    c5 = _oracle_cfg(O, s5)
+    H5, I5, q5, k5 = s5.hidden, s5.intermediate, s5.n_heads * s5.head_dim, s5.n_kv_heads * s5.head_dim
+    l5 = O.LayerWeights(attn_norm=np.ones(H5), wq=np.full((q5, H5), 0.02), wk=np.full((k5, H5), 0.02),
+                        wv=np.full((k5, H5), -0.02), wo=np.full((H5, q5), 0.02), mlp_norm=np.ones(H5),
+                        w_gate=np.full((I5, H5), 0.02), w_up=np.full((I5, H5), -0.02), w_down=np.full((H5, I5), 0.02))
+    x5 = S.hidden_states(S.workload("smollm3_prefill_bf16", batch=1), 0).f64 * 0.02
+    tb = timed(lambda: O.block_forward(x5, l5, c5, layer=0))
+    del l5
+    e5 = np.full((s5.vocab, s5.hidden), 0.02)
+    th = timed(lambda: O.lm_head(x5[0, :128], np.ones(s5.hidden), e5, c5))
+    del e5, x5
+    t = tb * s5.n_layers * s5.batch + th * s5.batch * s5.seq / 128
+    cf["smollm3_prefill_bf16"] = {"tokens_per_s": round(s5.batch * s5.seq / t, 2), "seconds": round(t, 1),
+                                  "extrapolated": True,
+                                  "sample": f"one block at 1 x 4096 ({tb:.1f} s) x 36 blocks x 2 sequences + the "
+                                            f"head on 128 rows ({th:.2f} s) x 64; constant weights (the time "
+                                            "does not depend on the values)"}
+    return out
 
 
 def backward_section(B, S, torch, dev, stream, args):
@@ -454,6 +579,7 @@ def main():
     avg_s = kern[dominant]["avg_us"] * 1e-6
     ach = flops["per_launch"][dominant] / avg_s / 1e12
     traffic = measured_traffic(dominant + "-traffic-bytes-per-launch")
+    rooflines = prefill_rooflines(kern, flops)
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
@@ -472,7 +598,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",
+        "dtype_note": "the arithmetic: float16 MFMA operands (activations rounded to float16; bf16 weights and "
+                      "cache values converted to float16 exactly) with float32 accumulation, float32 residual "
+                      "stream and statistics; weights, embedding, KV cache and logits stored as bf16",
         "data": "synthetic: seeded N(0, (1/24)^2) weights, unit RMSNorm weights, uniform token ids",
         "config": {"workload": "SmolLM2-135M-shaped prefill: 30 layers, hidden 576, 9/3 heads x 64, "
                                "intermediate 1536, vocab 49152 tied head; batch 4 x seq 512, bf16 logits",
@@ -485,6 +614,7 @@ def main():
                  "tokens_per_s": round(tokens / (float(np.median(cold_ms)) * 1e-3), 1),
                  "rep_ms": _pct(cold_ms), "how": "MALL/L2 flushed by a 512 MiB write before each step"},
         "roofline": roofline,
+        "rooflines": rooflines,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
     }
 
@@ -539,6 +669,12 @@ def main():
         att_s = ms / max(n, 1) * 1e-3
         att_gbps = db["decode_attention_per_launch"] / att_s / 1e9
         dtraffic = measured_traffic("decode_attention-traffic-bytes-per-launch", TRAFFIC_DECODE_PROFILE)
+        dkern = {}
+        with torch.cuda.stream(stream):
+            for k in ("embed", "qkv_rope", "decode_attention", "decode_combine", "o_proj", "gate_up", "down",
+                      "lm_head"):
+                kms, kn = _kernel_time(B, k, dstep, torch)
+                dkern[k] = round(1e3 * kms / max(kn, 1), 2)
         out["decode"] = {
             "workload": "decode step: batch 64, 2047 cached positions (+1 new), 30 layers, bf16",
             "timing": dmode + ", cold: MALL/L2 flushed by a 512 MiB write before each step (median)",
@@ -556,6 +692,7 @@ def main():
                          "traffic_source": os.path.relpath(TRAFFIC_DECODE_PROFILE, ROOT) if dtraffic is not None else None,
                          "algorithmic_bytes_per_launch": db["decode_attention_per_launch"],
                          "avg_launch_us": round(att_s * 1e6, 2)},
+            "kernels_us": dkern,
         }
         # next-token choice on the decode step's logits [64, 49152] (smol_sample), and the
         # decode step + greedy choice captured together, timed cold like the step
