@@ -132,6 +132,24 @@ smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w
                              void *k_cache, void *v_cache, int cache_cap, void *logits,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* smol_decode_step without a workspace and without any allocation, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Arguments, results and errors as smol_decode_step
+ * (no key mask). The scratch is a fixed device array of SMOL_STATIC_SCRATCH_MIB MiB
+ * inside the library: each GPU the library runs on holds its own copy from the first
+ * call on it until the process ends. A call whose decode workspace
+ * (smol_workspace_size with SMOL_OP_DECODE and cache_cap) would exceed it returns
+ * SMOL_ERR_WORKSPACE (batch 64 over a 2048-key cache of the SmolLM2-135M shape needs
+ * about 2.4 MiB). Every call on a GPU shares that GPU's array and leaves its contents
+ * behind; nothing in it needs to start at zero (each call writes every value it reads
+ * before reading it), but calls that overlap on one GPU (different streams or host
+ * threads without ordering) race on it: the caller must serialise them. */
+#define SMOL_STATIC_SCRATCH_MIB 32
+smol_status smol_decode_step_static(const smol_config *cfg, const smol_model_weights *w,
+                                    const int32_t *ids, const int32_t *cache_len, int batch,
+                                    void *k_cache, void *v_cache, int cache_cap, void *logits,
+                                    void *stream);
+
 /* Next token of each sequence from one row of logits per sequence (the generation
  * loop of Sualeh77 model.py, "7. Top-level SmolLM2-135M Model Architecture",
  * generate, and abi96062 model.py, SmolLM2Model.generate).

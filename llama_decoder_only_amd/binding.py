@@ -28,7 +28,7 @@ KERNELS = ["embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "do
            "decode_attention", "decode_combine", "sample",
            "bw_gemm", "bw_attn_fwd", "bw_attn_dq", "bw_attn_dkdv", "bw_rows"]
 EXPORTED = ["smol_workspace_size", "smol_block_forward", "smol_model_prefill", "smol_decode_step",
-            "smol_model_prefill_ex", "smol_decode_step_ex",
+            "smol_model_prefill_ex", "smol_decode_step_ex", "smol_decode_step_static",
             "smol_sample", "smol_generate_workspace_size", "smol_generate",
             "smol_block_backward_workspace_size", "smol_block_backward",
             "smol_status_string", "smol_last_error", "smol_timing_begin", "smol_timing_end"]
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
                                             vp, i32, vp, sz, vp]
         L.smol_decode_step_ex.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, vp, i32, vp, vp, vp, i32,
                                           vp, vp, sz, vp]
+        L.smol_decode_step_static.argtypes = [cfgp, ctypes.POINTER(smol_model_weights), vp, vp, i32, vp, vp, i32,
+                                              vp, vp]
         L.smol_block_backward_workspace_size.argtypes = [cfgp, i32, i32, ctypes.POINTER(sz)]
         L.smol_block_backward.argtypes = [cfgp, ctypes.POINTER(smol_layer_weights), i32, vp, vp, i32, i32, i32, vp,
                                           vp, ctypes.POINTER(smol_layer_grads), i32, vp, sz, vp]
@@ -257,6 +259,17 @@ def smol_decode_step(cfg: Config, w: ModelWeights, ids: torch.Tensor, cache_len:
     _check(lib().smol_decode_step(ctypes.byref(cfg.c()), ctypes.byref(w.c), _ptr(ids), _ptr(cache_len), B,
                                   _ptr(k_cache), _ptr(v_cache), cap, _ptr(logits), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+    return logits
+
+
+def smol_decode_step_static(cfg: Config, w: ModelWeights, ids: torch.Tensor, cache_len: torch.Tensor,
+                            k_cache: torch.Tensor, v_cache: torch.Tensor, logits: torch.Tensor,
+                            stream=None) -> torch.Tensor:
+    """As smol_decode_step, on the library's fixed scratch (no workspace, no allocation)."""
+    B = ids.shape[0]
+    cap = k_cache.shape[3]
+    _check(lib().smol_decode_step_static(ctypes.byref(cfg.c()), ctypes.byref(w.c), _ptr(ids), _ptr(cache_len), B,
+                                         _ptr(k_cache), _ptr(v_cache), cap, _ptr(logits), _stream(stream)))
     return logits
 
 

@@ -15,6 +15,7 @@
 // xs rescales its output rows. Five launches per block, no separate norm kernels.
 #include <algorithm>
 #include <cmath>
+#include <map>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -640,6 +641,37 @@ smol_status backward_impl(const Dims &D, const smol_layer_weights *w, int layer,
   return SMOL_OK;
 }
 
+// ------------------------------------------------------------------ fixed scratch
+// smol_decode_step_static runs the decode step on a file-scope device array instead
+// of a caller's workspace, for callers that cannot allocate. In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is taken once
+// per device with hipGetSymbolAddress (with that device current) and only that
+// address is ever handed to kernels.
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)SMOL_STATIC_SCRATCH_MIB << 20;
+__device__ __attribute__((aligned(256))) char scratch[STATIC_SCRATCH_BYTES];
+
+struct ScratchPtrs {
+  std::mutex mu;
+  std::map<int, char *> ptr;  // device -> address of that device's copy of `scratch`
+} g_scratch;
+
+smol_status static_scratch(char **out) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(SMOL_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch.mu);
+  auto it = g_scratch.ptr.find(device);
+  if (it == g_scratch.ptr.end()) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(SMOL_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    if ((uintptr_t)p % ALIGN) return fail(SMOL_ERR_HIP, "scratch is not 256-byte aligned");
+    it = g_scratch.ptr.emplace(device, (char *)p).first;
+  }
+  *out = it->second;
+  return SMOL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -738,6 +770,29 @@ smol_status smol_decode_step_ex(const smol_config *cfg, const smol_model_weights
                                     key_mask)
                 : decode_impl<float>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, (char *)ws, lay,
                                      s, key_mask);
+}
+
+smol_status smol_decode_step_static(const smol_config *cfg, const smol_model_weights *w, const int32_t *ids,
+                                    const int32_t *cache_len, int batch, void *k_cache, void *v_cache, int cache_cap,
+                                    void *logits, void *stream) {
+  g_err.clear();
+  Dims D;
+  smol_status st = check_config(cfg, &D);
+  if (st != SMOL_OK) return st;
+  if ((st = check_model(D, w)) != SMOL_OK) return st;
+  if (!ids || !cache_len || !logits) return fail(SMOL_ERR_INVALID_ARG, "ids / cache_len / logits is NULL");
+  if (!k_cache || !v_cache) return fail(SMOL_ERR_INVALID_ARG, "decode needs k_cache and v_cache");
+  if (batch < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d must be >= 1", batch);
+  if (cache_cap < 1) return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d must be >= 1", cache_cap);
+  const Ws lay = layout(D, SMOL_OP_DECODE, batch, cache_cap);
+  if (lay.total > STATIC_SCRATCH_BYTES)
+    return fail(SMOL_ERR_WORKSPACE, "decode step needs %zu bytes of scratch, more than the fixed %zu (%d MiB)",
+                lay.total, STATIC_SCRATCH_BYTES, SMOL_STATIC_SCRATCH_MIB);
+  char *ws = nullptr;
+  if ((st = static_scratch(&ws)) != SMOL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return D.bf16 ? decode_impl<bf16>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, ws, lay, s)
+                : decode_impl<float>(D, w, ids, cache_len, batch, k_cache, v_cache, cache_cap, logits, ws, lay, s);
 }
 
 smol_status smol_generate_workspace_size(const smol_config *cfg, int batch, int prompt_len, int max_new,

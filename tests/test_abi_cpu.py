@@ -156,6 +156,25 @@ def test_decode_step_rejects():
     assert call(ws_bytes=need - 256) == B.SMOL_ERR_WORKSPACE
 
 
+def test_decode_step_static_rejects():
+    """The no-workspace decode step checks its arguments like smol_decode_step and turns
+    a request larger than its fixed scratch into SMOL_ERR_WORKSPACE, before any GPU call."""
+    cfg = _cfg()
+    m, keep = _model_struct(cfg)
+    call = lambda **k: B.lib().smol_decode_step_static(  # noqa: E731
+        ctypes.byref(cfg.c()), ctypes.byref(m), k.get("ids", FAKE), k.get("cl", FAKE), k.get("b", 64),
+        k.get("kc", FAKE), k.get("vc", FAKE), k.get("cap", 2048), k.get("logits", FAKE), None)
+    assert call(ids=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(cl=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(logits=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(kc=None) == B.SMOL_ERR_INVALID_ARG
+    assert call(b=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(cap=0) == B.SMOL_ERR_INVALID_ARG
+    big = 1 << 14  # batch whose decode workspace passes the fixed scratch
+    assert _ws(cfg, B.SMOL_OP_DECODE, big, 2048)[1] > (32 << 20)
+    assert call(b=big) == B.SMOL_ERR_WORKSPACE and "scratch" in B.smol_last_error()
+
+
 def test_sample_rejects():
     L = B.lib()
     call = lambda **k: L.smol_sample(  # noqa: E731
