@@ -514,6 +514,11 @@ def main():
     model = S.model_weights(s, 0)
     md = B.upload_model(model, dev)
     if args.other_only:
+        if args.copy_check:  # the byte counters' calibration copy, outside the timed work
+            src = torch.ones(args.copy_check << 18, dtype=torch.float32, device=dev)
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+            del src
         print(json.dumps(other_prefills(B, torch, dev, md)), flush=True)
         return
     ids_np = S.token_ids(s, 0)

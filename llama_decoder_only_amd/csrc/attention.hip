@@ -244,14 +244,21 @@ attn_prefill_kernel(const AttnArgs a) {
             if (!((kb >> j) & 1ull) || k0 + j < kmin) s[i][e] = -INFINITY;
           }
       }
+      // The causal cut, on the tiles that cross the diagonal only (a branch on a wave-
+      // uniform condition: left as a select inside the max loop, the compiler evaluated
+      // the 32 compares on every tile, about a sixth of the loop's vector ALU work).
+      if (__builtin_expect(need_mask, 0)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (k0 + 32 * i + acc_row(rr, lane) > my_kmax) s[i][rr] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          if (need_mask && k0 + 32 * i + acc_row(rr, lane) > my_kmax) s[i][rr] = -INFINITY;
-          mx = fmaxf(mx, s[i][rr]);
-        }
+        for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[i][rr]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx * c_log2);
       const float m_use = ((KS > 1 || MASKED) && m_new == -INFINITY) ? 0.f : m_new;  // no key seen yet: p = 0

@@ -21,32 +21,61 @@ rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const f
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
+  // the loads that depend on nothing go out together: the row's id, its position and
+  // the norm weights of the operand pass (the embedding row waits only for the id)
+  const int id = ids ? ids[row] : 0;
+  const int pos = (rope.cs && rope.cache_len) ? rope.cache_len[row] : rope.pos0 + row % max(rope.seq, 1);
+  constexpr int R = 16;
+  const int nj = H / 64;
+  float wv[R];
+  if (w && nj <= R) {
+#pragma unroll
+    for (int e = 0; e < R; ++e) wv[e] = to_f32(w[min(e, nj - 1) * 64 + lane]);
+  }
   if (rope.cs && lane < rope.half) {
     // RoPE angle i of this row (abi96062 components.py, RotaryEmbedding: pos * omega_i)
-    const int pos = rope.cache_len ? rope.cache_len[row] : rope.pos0 + row % rope.seq;
     rope.cs[(size_t)row * rope.half + lane] = rope_cos_sin(pos, rope.inv_freq[lane]);
   }
   float *xr = x + (size_t)row * H;
-  const int id = ids ? ids[row] : 0;
   const bool bad = ids && (id < 0 || id >= V);
   const T *er = E + (size_t)(bad ? 0 : id) * H;
   const float *sr = src + (size_t)row * H;
+  // The row in rounds of 16 columns per lane, every load of a round issued before any
+  // is used (one memory round trip per round instead of one per 64 columns); rows up
+  // to 1024 wide stay in registers for the operand pass.
+  float keep[R];
   float tot = 0.f;
-  for (int j = 0; j < H / 64; ++j) {
-    const int i = j * 64 + lane;
-    const float v = bad ? __builtin_nanf("") : ids ? to_f32(er[i]) : sr[i];
-    if (ids || src != x) xr[i] = v;
-    const float q = wave_sum(v * v);
-    tot += q;
-    if (lane == 0) {
-      ss_new[(size_t)j * M + row] = q;
-      ss_old[(size_t)j * M + row] = q;
+  for (int j0 = 0; j0 < nj; j0 += R) {
+    float v[R];
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+      const int i = min(j0 + e, nj - 1) * 64 + lane;
+      v[e] = bad ? __builtin_nanf("") : ids ? to_f32(er[i]) : sr[i];
+    }
+#pragma unroll
+    for (int e = 0; e < R; ++e) {
+      if (j0 + e >= nj) break;
+      const int i = (j0 + e) * 64 + lane;
+      if (ids || src != x) xr[i] = v[e];
+      const float q = wave_sum(v[e] * v[e]);
+      tot += q;
+      if (lane == 0) {
+        ss_new[(size_t)(j0 + e) * M + row] = q;
+        ss_old[(size_t)(j0 + e) * M + row] = q;
+      }
+      keep[e] = v[e];
     }
   }
   if (!w) return;
   const float r = 1.0f / sqrtf(tot / (float)H + eps) * SMOL_XS_SCALE;  // xs is stored times 2^-8
   Act<T> *ur = xs + (size_t)row * H;
-  for (int i = lane; i < H; i += 64) ur[i] = from_f32<Act<T>>(to_f32(w[i]) * (xr[i] * r));
+  if (nj <= R) {
+#pragma unroll
+    for (int e = 0; e < R; ++e)
+      if (e < nj) ur[e * 64 + lane] = from_f32<Act<T>>(wv[e] * (keep[e] * r));
+  } else {
+    for (int i = lane; i < H; i += 64) ur[i] = from_f32<Act<T>>(to_f32(w[i]) * (xr[i] * r));
+  }
 }
 
 template <typename T>
