@@ -253,6 +253,34 @@ def test_long_block_bf16_sampled_rows():
     assert r <= TOL_BF16
 
 
+def test_block_long_sequences_f32_and_bf16():
+    """Long single blocks: float32 at 1 x 2100 (the two-key-group attention over 66 query
+    blocks; early, middle and last rows) at the float32 bar, and bf16 at 2 x 4100 (past
+    4096 keys: 64-query blocks with two key groups; both sequences) at the bf16 bar."""
+    s = S.workload("block_f32", batch=1, seq=2100, norm_jitter=0.1)
+    say("block f32 B=1 T=2100")
+    layer = S.layer_weights(s, 0, 0)
+    x = S.hidden_states(s, 0)
+    got = to_np(_run_block(s, B.upload_layer(layer), x.data))
+    rows = np.unique(np.concatenate([[0, 31, 32, 1055, 1056, 1057, 2047, 2048, 2099],
+                                     np.random.default_rng(3).integers(0, 2100, 23)]))
+    want = block_rows_oracle(x.f64[0], olayer(layer), ocfg(s), rows)
+    r = rel(got[0, rows], want)
+    say(f"rel = {r:.3e}")
+    assert r <= TOL_F32
+    s2 = S.workload("long_prefill_bf16", n_layers=1, batch=2, seq=4100, norm_jitter=0.1)
+    say("block bf16 B=2 T=4100")
+    layer2 = S.layer_weights(s2, 0, 0)
+    x2 = S.hidden_states(s2, 0)
+    got2 = to_np(_run_block(s2, B.upload_layer(layer2), x2.f64))
+    rows2 = np.unique(np.concatenate([[0, 2047, 2048, 4095, 4096, 4099], np.random.default_rng(4).integers(0, 4100, 10)]))
+    for b in range(2):
+        want2 = block_rows_oracle(x2.f64[b], olayer(layer2), ocfg(s2), rows2)
+        r2 = rel(got2[b, rows2], want2)
+        say(f"sequence {b}: rel = {r2:.3e}")
+        assert r2 <= TOL_BF16
+
+
 def test_block_bf16_many_rows_last_tiles():
     """A bf16 block over M = 26 x 500 = 13000 rows: gate/up runs 256 x 256 tiles with each XCD
     owning a range of whole tiles, the last one ragged (13000 = 50 x 256 + 200). The last rows of
