@@ -119,10 +119,35 @@ __device__ __forceinline__ int qkv_pos(const GemmParams &p, int row) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // 1 = column ownership per XCD, 2 = row ownership, 0 = plain order.
-__host__ __device__ inline int xcd_mode(int M, int N, int BN) {
-  if (N > M && N / BN >= SMOL_XCDS) return 1;
-  if (xcd_rows(M)) return 2;
-  return 0;
+//
+// The choice goes by an estimate of the bytes each mode fetches from beyond the
+// XCDs' L2 caches (4 MB each; an operand of up to 3 MB is taken to stay resident
+// while the XCD walks its tiles). Column ownership: every XCD reads its eighth of
+// the weights once and the whole activation A, once if A stays resident, else once
+// per column tile of its slice (its resident workgroups walk M fastest). Row
+// ownership: every XCD reads the whole weight matrix and its eighth of A, once if
+// that stays resident, else once per round of the columns its ~32 resident
+// workgroups cover together. At batch 4 x seq 512 the lm_head keeps column ownership
+// (A 2.4 MB: 75 MB against 455 MB); at 8192 rows it takes row ownership, as does
+// the SmolLM3-3B-shaped gate/up (1.1 GB against 3.0 GB). Measured against column
+// ownership for those three: lm_head at batch 1 x seq 8192 656 -> 605 us, the SmolLM3
+// shape's gate/up 853 -> 815 us and lm_head 4.77 -> 4.57 ms. Below 1024 rows every
+// XCD must get work: column ownership when N > M, else the plain order.
+__host__ __device__ inline int xcd_mode(int M, int N, int K, int BM, int BN, int esz) {
+  const bool col_ok = N / BN >= SMOL_XCDS;
+  if (!xcd_rows(M)) return N > M && col_ok ? 1 : 0;
+  if (!col_ok) return 2;
+  // integers only: the host sizes the grid and the kernel maps its tiles by this same
+  // decision, which must come out alike on both sides
+  constexpr long long RESIDENT = 3ll << 20;
+  const long long a = (long long)M * K * esz, w = (long long)N * K * esz;
+  const long long tiles_n = N / BN, ntx = (tiles_n + SMOL_XCDS - 1) / SMOL_XCDS;
+  const long long col = SMOL_XCDS * a * (a <= RESIDENT ? 1 : ntx) + w;
+  const long long mtx = rows_per_xcd(M, BM) / BM;
+  const long long cols_per_round = mtx >= 32 ? 1 : 32 / mtx;
+  const long long row = a * (a / SMOL_XCDS <= RESIDENT ? 1 : (tiles_n + cols_per_round - 1) / cols_per_round) +
+                        SMOL_XCDS * w;
+  return col < row ? 1 : 2;
 }
 
 // A store to global memory through a global-address-space pointer: the compiler
@@ -436,17 +461,17 @@ gemm_kernel(const GemmParams p) {
   const int wm = (wave % NWG) % WM, wn = (wave % NWG) / WM;
 
   // XCD-aware tile order (workgroup i runs on XCD i % 8; each XCD has its own L2
-  // and whatever misses it streams at roughly HBM rate). Column ownership when the
-  // weights outweigh the activations (N > M): XCD x takes a contiguous slice of N
-  // tiles, so every weight byte is fetched by one XCD only. Otherwise row
-  // ownership (see xcd_rows): XCD x takes the M tiles of its row range. Within an
-  // XCD, M runs fastest so that concurrent workgroups share a weight tile.
+  // and whatever misses it streams from MALL or HBM). Column ownership: XCD x takes
+  // a contiguous slice of N tiles, so every weight byte is fetched by one XCD only.
+  // Row ownership: XCD x takes the M tiles of its row range (see xcd_mode for the
+  // choice). Within an XCD, M runs fastest so that concurrent workgroups share a
+  // weight tile.
   int tm, tn, split = 0;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
   const int local = blockIdx.x / SMOL_XCDS, xcd = blockIdx.x % SMOL_XCDS;
   // K split (a grid of a few tiles): workgroup i takes tile i mod tiles, split
   // i / tiles, so the tiles of one split (which share A) run side by side.
-  switch (SPLIT ? 3 : xcd_mode(p.M, p.N, BN)) {
+  switch (SPLIT ? 3 : xcd_mode(p.M, p.N, p.K, BM, BN, (int)sizeof(W))) {
     case 1: {  // columns
       const int ntx = (tiles_n + SMOL_XCDS - 1) / SMOL_XCDS;
       tm = local % tiles_m;
@@ -458,7 +483,7 @@ gemm_kernel(const GemmParams p) {
       const int mtx = rows_per_xcd(p.M, BM) / BM;
       tm = xcd * mtx + local % mtx;
       tn = local / mtx;
-      if (tm >= tiles_m) return;  // whole workgroup
+      if (tm >= tiles_m || tn >= tiles_n) return;  // whole workgroup
       break;
     }
     case 3: {  // K split
@@ -722,7 +747,7 @@ static hipError_t launch_cfg(const GemmParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int tiles_m = (p.M + BM - 1) / BM, tiles_n = p.N / BN;
     int tiles;
-    switch (xcd_mode(p.M, p.N, BN)) {
+    switch (xcd_mode(p.M, p.N, p.K, BM, BN, (int)sizeof(W))) {
       case 1: tiles = SMOL_XCDS * ((tiles_n + SMOL_XCDS - 1) / SMOL_XCDS) * tiles_m; break;
       case 2: tiles = SMOL_XCDS * (rows_per_xcd(p.M, BM) / BM) * tiles_n; break;
       default: tiles = tiles_m * tiles_n;
