@@ -48,6 +48,10 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const char *p) {
 }
 
 
+// How far (log2 units) a tile's max may pass the running reference max before the
+// reference moves (p = exp2(s - m_ref) <= 2^8 meanwhile).
+constexpr float ATTN_REF_SLACK = 8.0f;
+
 // MASKED: the launch has a key mask or a sliding window (a query at key index i then
 // sees only indices > i - window; rounds wholly before the block's first window are
 // skipped). A separate instantiation: the mask's byte loads inside the ring loop make
@@ -223,9 +227,9 @@ attn_prefill_kernel(const AttnArgs a) {
           mma_32x32x16(s[i], kf, qf[st]);
         }
       }
-      // ---- online softmax. Scores stay unscaled; the running max m_run lives in the
-      // scaled (log2) domain, so p = exp2(s * c - m) is one FMA and one v_exp_f32 (its
-      // argument is <= 0, where the plain hardware exp2 needs no range fix-up). A key
+      // ---- online softmax. Scores stay unscaled; the running reference max m_run lives
+      // in the scaled (log2) domain, so p = exp2(s * c - m) is one FMA and one v_exp_f32
+      // (its argument is <= 8, where the plain hardware exp2 needs no range fix-up). A key
       // split may meet tiles where some of its queries see no key yet: their max stays
       // -inf and their probabilities 0.
       const bool need_mask = k0 + BKV - 1 > q0 + a.q_key_off;
@@ -260,32 +264,50 @@ attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[i][rr]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      const float m_use = ((KS > 1 || MASKED) && m_new == -INFINITY) ? 0.f : m_new;  // no key seen yet: p = 0
-      float ls = 0.f;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[i][rr], c_log2, -m_use));
-          s[i][rr] = p;
-          ls += p;
-        }
-      if (__any(m_new != m_run)) {  // rescale only when some running max moved
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // The reference max m_run moves only when a tile's max exceeds it by more than
+      // 2^8 (softmax is unchanged by the reference; p <= 256 stays far inside float16),
+      // so the O and l rescale runs on few tiles: the first, and the rare later jumps.
+      const float m_cand = mx * c_log2;
+      const bool grow = m_cand > m_run + ATTN_REF_SLACK;  // m_run = -inf: any visible key
+      if (__any(grow)) {
+        const float m_new = grow ? m_cand : m_run;
+        const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        m_run = m_new;
       }
-      l_run += ls;
-      m_run = m_new;
+      const float m_use = ((KS > 1 || MASKED) && m_run == -INFINITY) ? 0.f : m_run;  // no key seen yet: p = 0
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) s[i][rr] = __builtin_amdgcn_exp2f(fmaf(s[i][rr], c_log2, -m_use));
       // ---- O^T += V^T . P^T. Element e of a lane's 8 values in key step sg is key
       // 16 sg + 8 (e / 4) + 4 half + e % 4, for P (from the score registers) and V alike.
+      // With a 16-bit operand type the row sum l adds the rounded p the MFMAs take, two
+      // at a time (v_dot2_f32_f16 against (1, 1), float accumulation).
+      float ls = 0.f;
 #pragma unroll
       for (int sg = 0; sg < 4; ++sg) {
         Frag<T> pf;
+        if constexpr (sizeof(T) == 2) {
+          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+          typedef float f2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf.v[e] = from_f32<T>(s[sg >> 1][8 * (sg & 1) + e]);
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = s[sg >> 1][8 * (sg & 1) + e], p1 = s[sg >> 1][8 * (sg & 1) + e + 1];
+            const h2 pk = __builtin_convertvector((f2){p0, p1}, h2);
+            pf.v[e] = pk[0];
+            pf.v[e + 1] = pk[1];
+            ls = __builtin_amdgcn_fdot2(pk, (h2){(_Float16)1.0f, (_Float16)1.0f}, ls, false);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pf.v[e] = from_f32<T>(s[sg >> 1][8 * (sg & 1) + e]);
+            ls += s[sg >> 1][8 * (sg & 1) + e];
+          }
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           Frag<T> vf;
@@ -313,6 +335,7 @@ attn_prefill_kernel(const AttnArgs a) {
           mma_32x32x16(o[dt], vf, pf);
         }
       }
+      l_run += ls;
     }
   }
 
