@@ -816,6 +816,8 @@ static hipError_t launch_split(GemmParams p, int ks, hipStream_t s) {
 //   * >= 512 tiles of 128 x 128: 128 x 128 with the four waves side by side along N,
 //     so each converted weight fragment feeds four MFMAs;
 //   * >= 512 tiles of 64 x 128: the same 1 x 4 wave layout (gate/up);
+//   * N a multiple of 192 but not of 128 with >= 256 tiles of 64 x 192 (QKV, o_proj
+//     and down at 8192 rows): 64 x 192 in 2 x 2 waves, two K groups;
 //   * otherwise 64 x 64 in a 2 x 2 wave layout, for parallelism on small N (o_proj,
 //     down, QKV and every decode GEMM); 64 x 128 when a 128-wide head must stay in one
 //     tile for RoPE.
@@ -842,6 +844,14 @@ static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
     return launch_cfg<T, 256, 256, 4, 4, 128, EPI, 2, 1>(p, s);
   if (EPI != EPI_QKV_ROPE || p.head_dim == 64)
     if (tm64 * (p.N / 64) < 128 && p.N % 64 == 0) return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 4, 2>(p, s);
+  // Widths that 128 does not divide (576, 960) on grids of >= 256 tiles of 64 x 192: a
+  // third fewer bytes staged per FLOP than 64 x 64, which is what bounds these GEMMs
+  // (batch 1 x seq 8192: QKV 37 -> 32.5 us, o_proj 27 -> 23.5, down 46 -> 38.5; a
+  // 3-deep ring for the residual ones, 1 x 2 waves in four K groups and 128 x 192 QKV
+  // tiles were all slower).
+  if (sizeof(T) == 2 && p.N % 192 == 0 && p.N % 128 != 0 && tm64 * (p.N / 192) >= 256 &&
+      (EPI != EPI_QKV_ROPE || 192 % p.head_dim == 0))
+    return launch_cfg<T, 64, 192, 2, 2, 128, EPI, 2, 2>(p, s);
   if (p.N % 128 == 0 && tm128 * (p.N / 128) >= 512) return launch_cfg<T, 128, 128, 1, 4, 128, EPI, 2, 2>(p, s);
   if (EPI == EPI_QKV_ROPE && p.head_dim == 128) return launch_cfg<T, 64, 128, 2, 2, 128, EPI, 2, 2>(p, s);
   if (EPI != EPI_QKV_ROPE && p.N % 128 == 0 && tm64 * (p.N / 128) >= 512)
