@@ -281,6 +281,27 @@ def test_block_long_sequences_f32_and_bf16():
         assert r2 <= TOL_BF16
 
 
+def test_model_prefill_row_owned_head_ragged():
+    """One block and the tied head at batch 2 x seq 4100 (M = 8200 rows, vocab 49152): the
+    head's 9.4 MB of activations are more than one XCD's L2 keeps, so the lm_head runs
+    256 x 256 tiles under row ownership (XCD 6 owns tiles 30..34 of 33), the last one ragged
+    (8200 = 32 x 256 + 8). Every logit of sampled rows of both sequences, among them the eight
+    rows of the ragged tile (sequence 1, positions 4092..4099), against the oracle."""
+    s = S.workload("long_prefill_bf16", n_layers=1, batch=2, seq=4100, norm_jitter=0.1)
+    say("model bf16 L=1 B=2 T=4100 (head over M = 8200)")
+    model = S.model_weights(s, 0)
+    ids_np = S.token_ids(s, 0)
+    got = _prefill(s, B.upload_model(model), torch.from_numpy(ids_np).to(DEV))
+    assert torch.isfinite(got.float()).all()
+    rows = np.unique(np.concatenate([[0, 255, 256, 2047, 4091, 4092, 4095, 4096, 4099],
+                                     np.random.default_rng(5).integers(0, 4100, 7)]))
+    for b in range(2):
+        want = O.model_prefill(ids_np[b:b + 1], omodel(model), ocfg(s), logit_rows=rows)
+        r = rel(to_np(got[b, torch.from_numpy(rows).to(DEV)]), want)
+        say(f"sequence {b}: rel = {r:.3e}")
+        assert r <= TOL_BF16
+
+
 def test_block_bf16_many_rows_last_tiles():
     """A bf16 block over M = 26 x 500 = 13000 rows: gate/up runs 256 x 256 tiles with each XCD
     owning a range of whole tiles, the last one ragged (13000 = 50 x 256 + 200). The last rows of
