@@ -28,12 +28,20 @@
 
 namespace smol {
 
-// Byte offset of 16-bit element (row, col) in a swizzled LDS tile with RB-byte rows:
-// 16-byte chunk c of row r sits at slot c ^ (r & 7).
+// Slot permutation of the K/V tiles: 16-byte chunk c of key row r sits at slot
+// c ^ att_slot(r), att_slot(r) = 2 (r mod 4) + (r / 4 mod 2), a bijection of r mod 8.
+// K fragment reads (one chunk from each of 8 consecutive rows per LDS cycle) then hit 8
+// distinct slots, and so do the transposing V reads, whose 16-lane groups take two
+// adjacent chunks (c, c + 1; c even) of 4 consecutive rows: the rows' slots differ in
+// bits 1-2, the two chunks in bit 0. (With c ^ (r mod 8) those 8 blocks fell on 4
+// slots, a 2-way conflict on every V read.)
+__device__ __forceinline__ int att_slot(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Byte offset of element (row, col) of an ES-byte type in a swizzled LDS tile with RB-byte rows.
 template <int RB, int ES>
 __device__ __forceinline__ int swz(int row, int col) {
   constexpr int EPC = 16 / ES;
-  return row * RB + (((col / EPC) ^ (row & 7)) << 4) + (col % EPC) * ES;
+  return row * RB + (((col / EPC) ^ att_slot(row)) << 4) + (col % EPC) * ES;
 }
 
 typedef __fp16 half4 __attribute__((ext_vector_type(4)));
@@ -123,7 +131,7 @@ attn_prefill_kernel(const AttnArgs a) {
 
   // DMA: instruction q of a round fills LDS bytes [q*1024, q*1024 + 1024) of the stage:
   // chunk index q*64 + lane -> (tile of the round, K or V, key row, slot); the slot
-  // receives the row's chunk slot ^ (row & 7). Only the key moves from round to round.
+  // receives the row's chunk slot ^ att_slot(row). Only the key moves from round to round.
   const W *dma_base[IPW];
   int dma_row[IPW];
 #pragma unroll
@@ -132,7 +140,7 @@ attn_prefill_kernel(const AttnArgs a) {
     const int cidx = q * 64 + lane;
     const int part = cidx / (BKV * CPR);  // 2 * tile_in_round + (0 = K, 1 = V)
     const int row = (cidx % (BKV * CPR)) / CPR;
-    const int c = (cidx % CPR) ^ (row & 7);
+    const int c = (cidx % CPR) ^ att_slot(row);
     dma_base[j] = ((part & 1) == 0 ? kbase_ptr : vbase_ptr) + c * (16 / ES);
     dma_row[j] = (part >> 1) * BKV + row;  // key offset within the round
   }
@@ -335,7 +343,7 @@ attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int row = 16 * sg + 8 * pp + 4 * half + e;
-                vf.v[4 * pp + e] = *reinterpret_cast<const float *>(vs + row * RB + (((d >> 2) ^ (row & 7)) << 4) + (d & 3) * 4);
+                vf.v[4 * pp + e] = *reinterpret_cast<const float *>(vs + row * RB + (((d >> 2) ^ att_slot(row)) << 4) + (d & 3) * 4);
               }
           }
           mma_32x32x16(o[dt], vf, pf);
