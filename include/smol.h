@@ -34,6 +34,11 @@
  *   - Element types follow config.dtype: SMOL_F32 -> float, SMOL_BF16 -> bfloat16
  *     (weights, embedding, norm weights, caches, logits). The residual stream inside
  *     the library and the hidden states at the block interface are float32 for both.
+ *   - Buffers of rows (weights, embedding, norm weights, hidden states, caches and
+ *     the logits a forward call writes) must start on a 16-byte boundary: the
+ *     kernels move rows in 16-byte vectors. A misaligned one returns
+ *     SMOL_ERR_INVALID_ARG naming it. ids, cache_len and masks need only their
+ *     element's alignment; smol_sample reads logits rows at any alignment.
  *   - Matrices are row-major. Linear weights are [out, in] (as nn.Linear stores them):
  *     wq [n_heads*d, H], wk/wv [n_kv*d, H], wo [H, n_heads*d], w_gate/w_up [I, H],
  *     w_down [H, I]; norm weights [H]; embedding [vocab, H].

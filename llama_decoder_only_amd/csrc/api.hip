@@ -19,6 +19,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -87,12 +88,27 @@ smol_status check_config(const smol_config *c, Dims *o) {
   return SMOL_OK;
 }
 
+// The kernels move rows in 16-byte vectors and 16-byte copies into LDS, so every
+// buffer of rows (weights, embedding, hidden states, caches, logits) starts on a
+// 16-byte boundary; a null pointer passes here (the callers check those).
+struct Named {
+  const void *p;
+  const char *name;
+};
+smol_status check_aligned(std::initializer_list<Named> bufs) {
+  for (const Named &b : bufs)
+    if ((uintptr_t)b.p % 16) return fail(SMOL_ERR_INVALID_ARG, "%s must be 16-byte aligned", b.name);
+  return SMOL_OK;
+}
+
 smol_status check_layer(const smol_layer_weights *w, int idx) {
   if (!w) return fail(SMOL_ERR_INVALID_ARG, "layer weights %d: NULL", idx);
   const void *p[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
   static const char *names[9] = {"attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"};
-  for (int i = 0; i < 9; ++i)
+  for (int i = 0; i < 9; ++i) {
     if (!p[i]) return fail(SMOL_ERR_INVALID_ARG, "layer %d: %s is NULL", idx, names[i]);
+    if ((uintptr_t)p[i] % 16) return fail(SMOL_ERR_INVALID_ARG, "layer %d: %s must be 16-byte aligned", idx, names[i]);
+  }
   return SMOL_OK;
 }
 
@@ -440,6 +456,7 @@ smol_status check_model(const Dims &D, const smol_model_weights *w) {
   if (!w->embed) return fail(SMOL_ERR_INVALID_ARG, "embed is NULL");
   if (!w->final_norm) return fail(SMOL_ERR_INVALID_ARG, "final_norm is NULL");
   if (!w->layers) return fail(SMOL_ERR_INVALID_ARG, "layers is NULL");
+  if (smol_status st = check_aligned({{w->embed, "embed"}, {w->final_norm, "final_norm"}}); st != SMOL_OK) return st;
   for (int l = 0; l < D.L; ++l) {
     smol_status st = check_layer(&w->layers[l], l);
     if (st != SMOL_OK) return st;
@@ -697,6 +714,8 @@ smol_status smol_block_forward(const smol_config *cfg, const smol_layer_weights 
   if (st != SMOL_OK) return st;
   if ((st = check_layer(w, 0)) != SMOL_OK) return st;
   if (!x_in || !x_out) return fail(SMOL_ERR_INVALID_ARG, "x_in / x_out is NULL");
+  if ((st = check_aligned({{x_in, "x_in"}, {x_out, "x_out"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}})) != SMOL_OK)
+    return st;
   if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d, seq %d must be >= 1", batch, seq);
   if (pos0 < 0) return fail(SMOL_ERR_INVALID_ARG, "pos0 %d < 0", pos0);
   if ((long)pos0 + seq > D.max_pos)
@@ -720,6 +739,7 @@ smol_status smol_model_prefill_ex(const smol_config *cfg, const smol_model_weigh
   if (st != SMOL_OK) return st;
   if ((st = check_model(D, w)) != SMOL_OK) return st;
   if (!ids || !logits) return fail(SMOL_ERR_INVALID_ARG, "ids / logits is NULL");
+  if ((st = check_aligned({{logits, "logits"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}})) != SMOL_OK) return st;
   if (batch < 1 || seq < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d, seq %d must be >= 1", batch, seq);
   if (pos0 < 0) return fail(SMOL_ERR_INVALID_ARG, "pos0 %d < 0", pos0);
   if ((long)pos0 + seq > D.max_pos)
@@ -761,6 +781,7 @@ smol_status smol_decode_step_ex(const smol_config *cfg, const smol_model_weights
   if ((st = check_model(D, w)) != SMOL_OK) return st;
   if (!ids || !cache_len || !logits) return fail(SMOL_ERR_INVALID_ARG, "ids / cache_len / logits is NULL");
   if (!k_cache || !v_cache) return fail(SMOL_ERR_INVALID_ARG, "decode needs k_cache and v_cache");
+  if ((st = check_aligned({{logits, "logits"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}})) != SMOL_OK) return st;
   if (batch < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d must be >= 1", batch);
   if (cache_cap < 1) return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d must be >= 1", cache_cap);
   Ws lay;
@@ -782,6 +803,7 @@ smol_status smol_decode_step_static(const smol_config *cfg, const smol_model_wei
   if ((st = check_model(D, w)) != SMOL_OK) return st;
   if (!ids || !cache_len || !logits) return fail(SMOL_ERR_INVALID_ARG, "ids / cache_len / logits is NULL");
   if (!k_cache || !v_cache) return fail(SMOL_ERR_INVALID_ARG, "decode needs k_cache and v_cache");
+  if ((st = check_aligned({{logits, "logits"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}})) != SMOL_OK) return st;
   if (batch < 1) return fail(SMOL_ERR_INVALID_ARG, "batch %d must be >= 1", batch);
   if (cache_cap < 1) return fail(SMOL_ERR_INVALID_ARG, "cache_cap %d must be >= 1", cache_cap);
   const Ws lay = layout(D, SMOL_OP_DECODE, batch, cache_cap);
@@ -820,6 +842,7 @@ smol_status smol_generate(const smol_config *cfg, const smol_model_weights *w, c
   if ((st = check_model(D, w)) != SMOL_OK) return st;
   if (!prompt_ids || !out_ids) return fail(SMOL_ERR_INVALID_ARG, "prompt_ids / out_ids is NULL");
   if (!k_cache || !v_cache) return fail(SMOL_ERR_INVALID_ARG, "generation needs k_cache and v_cache");
+  if ((st = check_aligned({{k_cache, "k_cache"}, {v_cache, "v_cache"}})) != SMOL_OK) return st;
   if (batch < 1 || prompt_len < 1 || max_new < 1)
     return fail(SMOL_ERR_INVALID_ARG, "batch %d, prompt_len %d, max_new %d must be >= 1", batch, prompt_len, max_new);
   const long last = (long)prompt_len + max_new - 1;  // positions fed: 0 .. last - 1
@@ -910,11 +933,6 @@ smol_status smol_block_backward(const smol_config *cfg, const smol_layer_weights
   if ((uintptr_t)ws % ALIGN) return fail(SMOL_ERR_INVALID_ARG, "ws must be 256-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   smol_layer_weights wf = *w;
-  if (D.bf16) {
-    const void *pw[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
-    for (const void *p : pw)
-      if ((uintptr_t)p % 16) return fail(SMOL_ERR_INVALID_ARG, "bf16 weights must be 16-byte aligned");
-  }
   if (D.bf16) {  // widen the weights to float32 once (exact) and differentiate in float32
     const void *src[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->mlp_norm, w->w_gate, w->w_up, w->w_down};
     const void **dst[9] = {&wf.attn_norm, &wf.wq, &wf.wk, &wf.wv, &wf.wo, &wf.mlp_norm, &wf.w_gate, &wf.w_up, &wf.w_down};

@@ -8,11 +8,42 @@
 
 namespace smol {
 
+// Four consecutive elements of a row as float (bf16 widens exactly), and back.
+__device__ __forceinline__ void load4(const float *p, float v[4]) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+}
+__device__ __forceinline__ void load4(const bf16 *p, float v[4]) {
+  const uint2 a = *reinterpret_cast<const uint2 *>(p);
+  v[0] = __uint_as_float(a.x << 16); v[1] = __uint_as_float(a.x & 0xffff0000u);
+  v[2] = __uint_as_float(a.y << 16); v[3] = __uint_as_float(a.y & 0xffff0000u);
+}
+__device__ __forceinline__ void store4(float *p, const float v[4]) {
+  *reinterpret_cast<f32x4 *>(p) = (f32x4){v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ void store4(f16 *p, const float v[4]) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  *reinterpret_cast<h4 *>(p) = (h4){(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+}
+
+// Sum over each row of 16 lanes, in every lane of the row: neighbours, pairs, then
+// the mirrored half-rows and the mirrored row (DPP moves, no LDS round trip). Every
+// lane adds the same two operands at each step, so all 16 hold the same bits.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
 // One wavefront per row: x[row] = E[ids[row]] (ids != nullptr) or x[row] = src[row];
 // the row's sums of squares per 64 columns into ss_new and ss_old ([H/64, M]); and,
 // when w != nullptr, xs[row] = w * x * r * 2^-8 with the row's r -- the input of the
-// first deferred RMSNorm (stored at SMOL_XS_SCALE, as every xs); and the row's RoPE (cos, sin) table (RopeIn). An id outside
-// [0, V) makes the row (and its sums) NaN.
+// first deferred RMSNorm (stored at SMOL_XS_SCALE, as every xs); and the row's RoPE
+// (cos, sin) table (RopeIn). An id outside [0, V) makes the row (and its sums) NaN.
+// A lane handles 4-column units: unit u (columns 4u .. 4u + 3) is lane u % 64 in round
+// u / 64, so each 64-column group is one DPP row of 16 lanes, summed without LDS.
 template <typename T>
 __global__ void __launch_bounds__(256)
 rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const float *src, float *x,
@@ -21,16 +52,17 @@ rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const f
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
+  constexpr int R = 8;            // rounds kept in registers: rows up to 2048 wide
+  const int nu = H / 4, nr = (nu + 63) / 64;
   // the loads that depend on nothing go out together: the row's id, its position and
   // the norm weights of the operand pass (the embedding row waits only for the id)
   const int id = ids ? ids[row] : 0;
   const int pos = (rope.cs && rope.cache_len) ? rope.cache_len[row] : rope.pos0 + row % max(rope.seq, 1);
-  constexpr int R = 16;
-  const int nj = H / 64;
-  float wv[R];
-  if (w && nj <= R) {
+  float wv[R][4];
+  if (w && nr <= R) {
 #pragma unroll
-    for (int e = 0; e < R; ++e) wv[e] = to_f32(w[min(e, nj - 1) * 64 + lane]);
+    for (int t = 0; t < R; ++t)
+      if (t < nr) load4(w + 4 * min(lane + 64 * t, nu - 1), wv[t]);
   }
   if (rope.cs && lane < rope.half) {
     // RoPE angle i of this row (abi96062 components.py, RotaryEmbedding: pos * omega_i)
@@ -40,41 +72,69 @@ rows_ss_kernel(const int32_t *__restrict__ ids, const T *__restrict__ E, const f
   const bool bad = ids && (id < 0 || id >= V);
   const T *er = E + (size_t)(bad ? 0 : id) * H;
   const float *sr = src + (size_t)row * H;
-  // The row in rounds of 16 columns per lane, every load of a round issued before any
-  // is used (one memory round trip per round instead of one per 64 columns); rows up
-  // to 1024 wide stay in registers for the operand pass.
-  float keep[R];
-  float tot = 0.f;
-  for (int j0 = 0; j0 < nj; j0 += R) {
-    float v[R];
-#pragma unroll
-    for (int e = 0; e < R; ++e) {
-      const int i = min(j0 + e, nj - 1) * 64 + lane;
-      v[e] = bad ? __builtin_nanf("") : ids ? to_f32(er[i]) : sr[i];
+  auto load_unit = [&](int u, float v[4]) {
+    if (bad) {
+      v[0] = v[1] = v[2] = v[3] = __builtin_nanf("");
+    } else if (ids) {
+      load4(er + 4 * u, v);
+    } else {
+      load4(sr + 4 * u, v);
     }
+  };
+  float keep[R][4];
+  float tot = 0.f;  // lanes 0, 16, 32, 48: the sums of their groups, in round order
+  for (int t0 = 0; t0 < nr; t0 += R) {
+    float v[R][4];
 #pragma unroll
-    for (int e = 0; e < R; ++e) {
-      if (j0 + e >= nj) break;
-      const int i = (j0 + e) * 64 + lane;
-      if (ids || src != x) xr[i] = v[e];
-      const float q = wave_sum(v[e] * v[e]);
-      tot += q;
-      if (lane == 0) {
-        ss_new[(size_t)(j0 + e) * M + row] = q;
-        ss_old[(size_t)(j0 + e) * M + row] = q;
+    for (int t = 0; t < R; ++t)
+      if (t0 + t < nr) load_unit(min(lane + 64 * (t0 + t), nu - 1), v[t]);
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      if (t0 + t >= nr) break;
+      const int u = lane + 64 * (t0 + t);
+      const bool ok = u < nu;  // a whole 16-lane group is in or out (nu % 16 == 0)
+      if (ok && (ids || src != x)) store4(xr + 4 * u, v[t]);
+      float q = v[t][0] * v[t][0];
+      q = fmaf(v[t][1], v[t][1], q);
+      q = fmaf(v[t][2], v[t][2], q);
+      q = fmaf(v[t][3], v[t][3], q);
+      q = row16_sum(ok ? q : 0.f);
+      if (ok && (lane & 15) == 0) {
+        const int g = u >> 4;
+        ss_new[(size_t)g * M + row] = q;
+        ss_old[(size_t)g * M + row] = q;
+        tot += q;
       }
-      keep[e] = v[e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keep[t][e] = v[t][e];
     }
   }
   if (!w) return;
-  const float r = 1.0f / sqrtf(tot / (float)H + eps) * SMOL_XS_SCALE;  // xs is stored times 2^-8
+  auto lane_val = [&](int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), l)); };
+  const float sum = (lane_val(0) + lane_val(16)) + (lane_val(32) + lane_val(48));
+  const float r = 1.0f / sqrtf(sum / (float)H + eps) * SMOL_XS_SCALE;  // xs is stored times 2^-8
   Act<T> *ur = xs + (size_t)row * H;
-  if (nj <= R) {
+  if (nr <= R) {
 #pragma unroll
-    for (int e = 0; e < R; ++e)
-      if (e < nj) ur[e * 64 + lane] = from_f32<Act<T>>(wv[e] * (keep[e] * r));
+    for (int t = 0; t < R; ++t) {
+      const int u = lane + 64 * t;
+      if (t >= nr || u >= nu) continue;
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = wv[t][e] * (keep[t][e] * r);
+      store4(ur + 4 * u, o);
+    }
   } else {
-    for (int i = lane; i < H; i += 64) ur[i] = from_f32<Act<T>>(to_f32(w[i]) * (xr[i] * r));
+    // wider rows: the source again (read-only here; x itself only when src == x,
+    // which this kernel then leaves unwritten)
+    for (int u = lane; u < nu; u += 64) {
+      float v[4], wu[4], o[4];
+      load_unit(u, v);
+      load4(w + 4 * u, wu);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = wu[e] * (v[e] * r);
+      store4(ur + 4 * u, o);
+    }
   }
 }
 

@@ -112,6 +112,13 @@ def test_block_forward_rejects():
     assert _block(cfg, w, ws_bytes=need - 1) == B.SMOL_ERR_WORKSPACE
     assert _block(cfg, w, ws=FAKE + 8) == B.SMOL_ERR_INVALID_ARG and "aligned" in B.smol_last_error()
     assert _block(cfg, w, ws=None) == B.SMOL_ERR_INVALID_ARG
+    # rows move in 16-byte vectors: every buffer of rows must be 16-byte aligned
+    assert _block(cfg, w, x_in=FAKE + 8) == B.SMOL_ERR_INVALID_ARG and "x_in" in B.smol_last_error()
+    assert _block(cfg, w, x_out=FAKE + 4) == B.SMOL_ERR_INVALID_ARG and "x_out" in B.smol_last_error()
+    assert _block(cfg, w, kc=FAKE + 2, vc=FAKE, cap=16) == B.SMOL_ERR_INVALID_ARG
+    assert "k_cache" in B.smol_last_error() and "aligned" in B.smol_last_error()
+    odd = B.smol_layer_weights(*[FAKE + 8 if n == "w_up" else FAKE for n in B.LAYER_FIELDS])
+    assert _block(cfg, odd) == B.SMOL_ERR_INVALID_ARG and "w_up must be 16-byte aligned" in B.smol_last_error()
     assert B.lib().smol_block_forward(None, ctypes.byref(w), FAKE, FAKE, 1, 8, 0, None, None, 0, FAKE, need,
                                       None) == B.SMOL_ERR_INVALID_ARG
 
@@ -140,6 +147,12 @@ def test_model_prefill_rejects():
     assert call(m=m2) == B.SMOL_ERR_INVALID_ARG and "layer 17" in B.smol_last_error()
     m3 = B.smol_model_weights(None, keep, FAKE)
     assert call(m=m3) == B.SMOL_ERR_INVALID_ARG and "embed" in B.smol_last_error()
+    m4 = B.smol_model_weights(FAKE + 8, keep, FAKE)
+    assert call(m=m4) == B.SMOL_ERR_INVALID_ARG and "embed must be 16-byte aligned" in B.smol_last_error()
+    m5 = B.smol_model_weights(FAKE, keep, FAKE + 2)
+    assert call(m=m5) == B.SMOL_ERR_INVALID_ARG and "final_norm" in B.smol_last_error()
+    assert call(logits=FAKE + 2) == B.SMOL_ERR_INVALID_ARG and "logits" in B.smol_last_error()
+    assert call(kc=FAKE, vc=FAKE + 8, cap=64) == B.SMOL_ERR_INVALID_ARG and "v_cache" in B.smol_last_error()
 
 
 def test_decode_step_rejects():
@@ -154,6 +167,7 @@ def test_decode_step_rejects():
     assert call(b=0) == B.SMOL_ERR_INVALID_ARG
     assert call(cap=0) == B.SMOL_ERR_INVALID_ARG
     assert call(ws_bytes=need - 256) == B.SMOL_ERR_WORKSPACE
+    assert call(kc=FAKE + 8) == B.SMOL_ERR_INVALID_ARG and "k_cache" in B.smol_last_error()
 
 
 def test_decode_step_static_rejects():
@@ -170,6 +184,7 @@ def test_decode_step_static_rejects():
     assert call(kc=None) == B.SMOL_ERR_INVALID_ARG
     assert call(b=0) == B.SMOL_ERR_INVALID_ARG
     assert call(cap=0) == B.SMOL_ERR_INVALID_ARG
+    assert call(logits=FAKE + 2) == B.SMOL_ERR_INVALID_ARG and "logits" in B.smol_last_error()
     big = 1 << 14  # batch whose decode workspace passes the fixed scratch
     assert _ws(cfg, B.SMOL_OP_DECODE, big, 2048)[1] > (32 << 20)
     assert call(b=big) == B.SMOL_ERR_WORKSPACE and "scratch" in B.smol_last_error()
@@ -214,6 +229,7 @@ def test_generate_rejects():
     assert call(t=60, n=6) == B.SMOL_ERR_INVALID_ARG and "cache_cap" in B.smol_last_error()  # 60 + 6 - 1 > 64
     assert call(temp=0.7) == B.SMOL_ERR_INVALID_ARG and "uniforms" in B.smol_last_error()
     assert call(ws_bytes=need - 256) == B.SMOL_ERR_WORKSPACE
+    assert call(kc=FAKE + 4) == B.SMOL_ERR_INVALID_ARG and "k_cache" in B.smol_last_error()
     cfg8 = _cfg(max_pos=20)
     assert L.smol_generate(ctypes.byref(cfg8.c()), ctypes.byref(m), FAKE, None, 4, 16, 8, 0.0, 0, 1.0, None, FAKE,
                            FAKE, FAKE, 64, FAKE, need, None) == B.SMOL_ERR_INVALID_ARG
