@@ -826,13 +826,16 @@ static hipError_t launch_split(GemmParams p, int ks, hipStream_t s) {
 //   * N a multiple of 192 but not of 128 with >= 256 tiles of 64 x 192 (QKV, o_proj
 //     and down at 8192 rows): 64 x 192 in 2 x 2 waves, two K groups;
 //   * otherwise 64 x 64 in a 2 x 2 wave layout, for parallelism on small N (o_proj,
-//     down, QKV and every decode GEMM); 64 x 128 when a 128-wide head must stay in one
-//     tile for RoPE.
+//     down and QKV); 64 x 128 when a 128-wide head must stay in one tile for RoPE;
+//     32 x 64 (1 x 2 waves, two K groups) on grids of fewer than 128 64 x 64 tiles.
 // Grids of a few hundred tiles leave one wave per SIMD, whose LDS -> convert -> MFMA
 // chain then runs exposed: those split each stage's K steps over two wave groups.
 // Grids under 128 tiles (a decode step: M = batch) stream weights that are cold in
-// L2 and MALL through few workgroups; there a 4-deep ring keeps three stages of HBM
-// reads in flight (measured 25-30% faster than 2 stages with cold weights). In the
+// L2 and MALL through few workgroups, each bounded by the bytes it stages (about
+// 30 GB/s per CU); there a 4-deep ring keeps three stages of HBM reads in flight
+// (measured 25-30% faster than 2 stages with cold weights), and 32-row tiles double
+// the workgroups while each stages a quarter fewer bytes (batch-64 decode step 1.785
+// -> 1.754 ms; with one K group, 1.866; rings of 6 or 8 stages, 1.86-1.87). In the
 // prefill each layer's weights are also cold in L2 (they come from MALL or HBM): the
 // residual GEMMs (o_proj, and down with its 24 stages) run a 3-deep ring (down
 // 22.2 -> 18.8 us at batch 4 x seq 512; 4 stages or 4 wave groups gain nothing
@@ -850,7 +853,7 @@ static hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
   if (((EPI == EPI_STORE || EPI == EPI_SWIGLU) && t256 >= 512) || (EPI == EPI_RESIDUAL && t256 >= 256))
     return launch_cfg<T, 256, 256, 4, 4, 128, EPI, 2, 1>(p, s);
   if (EPI != EPI_QKV_ROPE || p.head_dim == 64)
-    if (tm64 * (p.N / 64) < 128 && p.N % 64 == 0) return launch_cfg<T, 64, 64, 2, 2, 128, EPI, 4, 2>(p, s);
+    if (tm64 * (p.N / 64) < 128 && p.N % 64 == 0) return launch_cfg<T, 32, 64, 1, 2, 128, EPI, 4, 2>(p, s);
   // Widths that 128 does not divide (576, 960) on grids of >= 256 tiles of 64 x 192: a
   // third fewer bytes staged per FLOP than 64 x 64, which is what bounds these GEMMs
   // (batch 1 x seq 8192: QKV 37 -> 32.5 us, o_proj 27 -> 23.5, down 46 -> 38.5; a
