@@ -145,7 +145,7 @@ smol_status smol_decode_step(const smol_config *cfg, const smol_model_weights *w
  * call on it until the process ends. A call whose decode workspace
  * (smol_workspace_size with SMOL_OP_DECODE and cache_cap) would exceed it returns
  * SMOL_ERR_WORKSPACE (batch 64 over a 2048-key cache of the SmolLM2-135M shape needs
- * about 2.4 MiB). Every call on a GPU shares that GPU's array and leaves its contents
+ * about 3.7 MiB). Every call on a GPU shares that GPU's array and leaves its contents
  * behind; nothing in it needs to start at zero (each call writes every value it reads
  * before reading it), but calls that overlap on one GPU (different streams or host
  * threads without ordering) race on it: the caller must serialise them. */
@@ -292,7 +292,10 @@ typedef enum {
   SMOL_K_DECODE_ATTENTION = 8, SMOL_K_DECODE_COMBINE = 9, SMOL_K_SAMPLE = 10,
   /* smol_block_backward: its GEMMs, attention forward / dQ / dK-dV, row kernels */
   SMOL_K_BW_GEMM = 11, SMOL_K_BW_ATTN_FWD = 12, SMOL_K_BW_ATTN_DQ = 13, SMOL_K_BW_ATTN_DKDV = 14,
-  SMOL_K_BW_ROWS = 15, SMOL_K_COUNT = 16
+  SMOL_K_BW_ROWS = 15,
+  /* the one-launch decode step of a bf16 model at head_dim 64 (every layer, up to the
+   * final norm; smol_decode_step and the decode steps of smol_generate) */
+  SMOL_K_DECODE_STEP = 16, SMOL_K_COUNT = 17
 } smol_kernel;
 smol_status smol_timing_begin(int kernel, int max_launches);
 smol_status smol_timing_end(float *total_ms, int *launches);

@@ -26,7 +26,7 @@ SMOL_F32, SMOL_BF16 = 0, 1
 SMOL_OP_BLOCK, SMOL_OP_PREFILL, SMOL_OP_DECODE = 0, 1, 2
 KERNELS = ["embed", "rmsnorm", "qkv_rope", "attention", "o_proj", "gate_up", "down", "lm_head",
            "decode_attention", "decode_combine", "sample",
-           "bw_gemm", "bw_attn_fwd", "bw_attn_dq", "bw_attn_dkdv", "bw_rows"]
+           "bw_gemm", "bw_attn_fwd", "bw_attn_dq", "bw_attn_dkdv", "bw_rows", "decode_step"]
 EXPORTED = ["smol_workspace_size", "smol_block_forward", "smol_model_prefill", "smol_decode_step",
             "smol_model_prefill_ex", "smol_decode_step_ex", "smol_decode_step_static",
             "smol_sample", "smol_generate_workspace_size", "smol_generate",

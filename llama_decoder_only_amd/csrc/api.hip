@@ -22,6 +22,7 @@
 #include <initializer_list>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "common.h"
@@ -117,7 +118,7 @@ size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 // Workspace carve-up. Offsets in bytes from ws.
 struct Ws {
-  size_t x, xs, q, k, v, o, y, ss_p, ss_q, rope, part, gpart, total;
+  size_t x, xs, q, k, v, o, y, ss_p, ss_q, rope, part, gpart, dxpart, dxctrl, total;
 };
 
 Ws layout(const Dims &D, int op, int B, int T) {
@@ -145,6 +146,9 @@ Ws layout(const Dims &D, int op, int B, int T) {
     const int cap = std::min(T, D.max_pos);
     const int splits = smol::decode_splits(cap, D.d, D.esz, &chunk);
     w.part = take((size_t)B * D.nq * splits * (D.d + 2) * 4);
+    // the one-launch step (decode_xcd): its attention partials and barrier flags
+    w.dxpart = take(smol::decode_xcd_part_floats(B, D.nq, D.nkv) * 4);
+    w.dxctrl = take(smol::decode_xcd_ctrl_words(64) * 4);
   } else {
     w.k = take((size_t)B * D.nkv * T * D.d * D.esz);
     w.v = take((size_t)B * D.nkv * T * D.d * D.esz);
@@ -365,6 +369,34 @@ smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_
                         int B, void *kc, void *vc, int cap, void *logits, char *ws, const Ws &lay, hipStream_t s,
                         const uint8_t *key_mask = nullptr) {
   float *x = (float *)(ws + lay.x);
+  if constexpr (std::is_same<T, bf16>::value) {
+    // the whole step but the head in one persistent launch, where the shape fits it
+    const int nwx = smol::decode_xcd_groups_per_xcd();
+    if (smol::decode_xcd_fits(B, D.H, D.nq, D.nkv, D.d, D.I, D.L, cap, nwx)) {
+      smol::DecodeXcdArgs a{};
+      a.B = B; a.H = D.H; a.nq = D.nq; a.nkv = D.nkv; a.I = D.I; a.L = D.L; a.V = D.V;
+      a.cap = cap; a.max_pos = D.max_pos; a.nope_every = D.nope_every; a.window = D.window;
+      a.nwx = nwx; a.sp = smol::decode_xcd_splits(B, D.nkv, nwx); a.mask_ld = cap; a.eps = D.eps;
+      a.ids = ids; a.cache_len = cache_len; a.key_mask = key_mask;
+      a.embed = (const bf16 *)w->embed; a.final_norm = (const bf16 *)w->final_norm;
+      a.kc = (bf16 *)kc; a.vc = (bf16 *)vc;
+      a.x = x; a.q = (f16 *)(ws + lay.q); a.o = (f16 *)(ws + lay.o); a.y = (f16 *)(ws + lay.y);
+      a.part = (float *)(ws + lay.dxpart); a.xs = (f16 *)(ws + lay.xs);
+      a.ss_p = (float *)(ws + lay.ss_p); a.ss_q = (float *)(ws + lay.ss_q);
+      a.ctrl = (uint32_t *)(ws + lay.dxctrl);
+      double f[64];
+      fill_inv_freq(D, f);
+      for (int i = 0; i < D.d / 2; ++i) a.inv_freq[i] = f[i];
+      for (int l = 0; l < D.L; ++l) {
+        const smol_layer_weights &Lw = w->layers[l];
+        a.layer[l] = smol::DxLayer{(const bf16 *)Lw.wq, (const bf16 *)Lw.wk, (const bf16 *)Lw.wv,
+                                   (const bf16 *)Lw.wo, (const bf16 *)Lw.w_gate, (const bf16 *)Lw.w_up,
+                                   (const bf16 *)Lw.w_down, (const bf16 *)Lw.attn_norm, (const bf16 *)Lw.mlp_norm};
+      }
+      SMOL_LAUNCH(SMOL_K_DECODE_STEP, smol::decode_xcd(a, s));
+      return head<T>(D, w, B, logits, ws, lay, s);
+    }
+  }
   LayerCtx c{};
   c.D = &D;
   c.ws = ws;

@@ -30,7 +30,7 @@ LIB = os.path.join(PKG, "libsmol.so")
 SAN_BUILD = os.path.join(BUILD, "sanitize")
 SAN_LIB = os.path.join(SAN_BUILD, "libsmol.so")
 
-SOURCES = ["api.hip", "gemm.hip", "attention.hip", "decode_attention.hip", "norm_embed.hip", "sample.hip", "backward.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attention.hip", "decode_attention.hip", "decode_xcd.hip", "norm_embed.hip", "sample.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 

@@ -45,6 +45,10 @@ def test_decode_bytes_match_the_stated_total():
     assert abs(b["total"] - 3.295e9) <= 2e6
     assert abs(b["kv_read"] - 3.018e9) <= 2e6
     assert b["decode_attention_per_launch"] * s.n_layers == b["kv_read"]
+    # the one-launch step is everything but the head: the embedding matrix it reads and
+    # the logits it writes, less the embedding rows the step gathers itself
+    head_only = 2 * s.vocab * s.hidden + b["logits"] - 2 * s.batch * s.hidden
+    assert b["decode_step_per_launch"] == b["total"] - head_only
 
 
 def test_backward_flops():
