@@ -259,37 +259,46 @@ __device__ __forceinline__ void dx_split4(bf16 *h, bf16 *l, const float (&u)[4])
 }
 
 // Stage u = RMSNorm(x rows; w) of the group's rows (hi into Ah, lo into Al). Thread t
-// serves row t / TPR (16 rows x TPR threads), columns 4 (t % TPR) + 4 TPR i; the norm
-// weights and the rows are requested together.
-template <int HMAX, int LDA>
-__device__ __forceinline__ void dx_stage_norm(bf16 *Ah, bf16 *Al, __amdgpu_buffer_rsrc_t xr, const bf16 *w, int H,
-                                              float eps, int g, int R) {
-  constexpr int TPR = DX_THREADS / DX_ROWS, IT = (HMAX + 4 * TPR - 1) / (4 * TPR);
-  const int t = threadIdx.x, j = t / TPR, c = t % TPR;
-  const int b = g + 8 * j;
-  f32x4 v[IT];
-  uint2 wb[IT];
+// serves row t / TPR (16 rows x TPR threads), columns 4 (t % TPR) + 4 TPR i. The norm
+// weights of those columns arrive in wb (dx_norm_prefetch, issued just before, so that
+// both round trips overlap; requesting them before the phase's barrier instead, with
+// the weight fragments, measured slower).
+constexpr int DX_TPR = DX_THREADS / DX_ROWS, DX_NIT = (DX_HMAX + 4 * DX_TPR - 1) / (4 * DX_TPR);
+__device__ __forceinline__ void dx_norm_prefetch(uint2 (&wb)[DX_NIT], const bf16 *w, int H, int R) {
+  const int t = threadIdx.x, j = t / DX_TPR, c = t % DX_TPR;
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int col = 4 * c + 4 * TPR * i;
-    v[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < DX_NIT; ++i) {
+    const int col = 4 * c + 4 * DX_TPR * i;
     wb[i] = make_uint2(0u, 0u);
+    if (j < R && col < H) wb[i] = *reinterpret_cast<const uint2 *>(w + col);
+  }
+}
+
+template <int LDA>
+__device__ __forceinline__ void dx_stage_norm(bf16 *Ah, bf16 *Al, __amdgpu_buffer_rsrc_t xr, const uint2 (&wb)[DX_NIT],
+                                              int H, float eps, int g, int R) {
+  const int t = threadIdx.x, j = t / DX_TPR, c = t % DX_TPR;
+  const int b = g + 8 * j;
+  f32x4 v[DX_NIT];
+#pragma unroll
+  for (int i = 0; i < DX_NIT; ++i) {
+    const int col = 4 * c + 4 * DX_TPR * i;
+    v[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (j < R && col < H) {
-      wb[i] = *reinterpret_cast<const uint2 *>(w + col);
       const Chunk16 ch = ld_sc1(xr, (uint32_t)((b * H + col) * 4));
       v[i] = (f32x4){__uint_as_float(ch[0]), __uint_as_float(ch[1]), __uint_as_float(ch[2]), __uint_as_float(ch[3])};
     }
   }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < IT; ++i) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+  for (int i = 0; i < DX_NIT; ++i) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
 #pragma unroll
-  for (int o = TPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  for (int o = DX_TPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
   const float r = 1.0f / sqrtf(ss / (float)H + eps);
   if (j < R) {
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int col = 4 * c + 4 * TPR * i;
+    for (int i = 0; i < DX_NIT; ++i) {
+      const int col = 4 * c + 4 * DX_TPR * i;
       if (col < H) {
         const float u[4] = {v[i][0] * r * __uint_as_float(wb[i].x << 16), v[i][1] * r * __uint_as_float(wb[i].x & 0xffff0000u),
                             v[i][2] * r * __uint_as_float(wb[i].y << 16), v[i][3] * r * __uint_as_float(wb[i].y & 0xffff0000u)};
@@ -349,6 +358,7 @@ namespace {
 constexpr int DX_BLK = 32;                 // keys per block
 constexpr int DX_SLOT = 2 * DX_BLK * DX_D * 2;  // LDS bytes of one block: its keys, then its values
 constexpr int DX_NSLOT = 4;                // blocks in flight per wavefront
+constexpr float DX_REF_SLACK = 8.0f;       // log2 units a score may pass the softmax reference
 constexpr int DX_CPB = DX_BLK * DX_D * 2 / 1024;  // 1 KB copies per block and matrix (4)
 
 typedef __fp16 dx_half4 __attribute__((ext_vector_type(4)));
@@ -430,10 +440,17 @@ __device__ __forceinline__ void dx_kv_block_mfma(const char *slot, int kb, int k
   float bm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
   bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
   bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-  const float mn = fmaxf(mx, bm);
-  const float mu = mn == -INFINITY ? 0.f : mn;  // nothing kept yet: weights 0
-  const float alpha = __builtin_amdgcn_exp2f(mx - mu);  // exp2(-inf) = 0
-  mx = mn;
+  // mx is a reference, not the running max: it moves (and the state is rescaled) only
+  // when a score passes it by more than 2^8, so p = exp2(s - mx) stays <= 256
+  if (__any(bm > mx + DX_REF_SLACK)) {
+    const float mn = fmaxf(mx, bm);
+    const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mx - mn);  // exp2(-inf) = 0
+    lsum *= alpha;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] *= alpha;
+    mx = mn;
+  }
+  const float mu = mx == -INFINITY ? 0.f : mx;  // nothing kept yet: weights 0
   bf16x8 ph, pl;
   float ps = 0.f;
 #pragma unroll
@@ -444,10 +461,9 @@ __device__ __forceinline__ void dx_kv_block_mfma(const char *slot, int kb, int k
     pl[e] = (bf16)(pv - (float)hi);
     ps += pv;
   }
-  lsum = lsum * alpha + ps;
+  lsum += ps;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    o[t] *= alpha;
     uint32_t raw[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -532,6 +548,7 @@ __global__ void __launch_bounds__(DX_THREADS, 1) decode_xcd_kernel(const DecodeX
   // the barrier before it; every phase writes all the slots it uses (zero where idle)
   constexpr int NFR = UR * (IM_I > IM_H3 ? IM_I : IM_H3);
   Chunk16 fr[NFR];
+  uint2 nw[DX_NIT];  // the next norm stage's weights
   f32x4 res[2];
 
   // ---- embedding rows: workgroup m < R gathers row j = m
@@ -568,7 +585,8 @@ __global__ void __launch_bounds__(DX_THREADS, 1) decode_xcd_kernel(const DecodeX
     bf16 *vc = a.vc + (size_t)l * B * nkv * a.cap * DX_D;
 
     // ---- QKV + RoPE; k, v into the cache at P
-    dx_stage_norm<DX_HMAX, DX_KPAD_H>(Ah, Al, xr, Ly.an, H, a.eps, g, R);
+    dx_norm_prefetch(nw, Ly.an, H, R);
+    dx_stage_norm<DX_KPAD_H>(Ah, Al, xr, nw, H, a.eps, g, R);
     dx_mma<UR, IM_H, 1, NFR, DX_WAVES, DX_KPAD_H, false>(fr, nullptr, nu_qkv, KS_H, Ah, Al, red, res);
     if (w < nu_qkv) {
       const int u = m + w * nwx, hsl = u >> 2, c = u & 3, slot = lane & 15;
@@ -609,32 +627,54 @@ __global__ void __launch_bounds__(DX_THREADS, 1) decode_xcd_kernel(const DecodeX
 
     // ---- attention: item it = (pair, split), pair = (row j, kv head h); wavefront w * nwx + m.
     // Keys and values stream through the wavefront's LDS ring, DX_NSLOT blocks in
-    // flight; blocks that lie wholly below P (not written in this step) are requested
-    // before the barrier.
+    // flight. The first blocks that lie wholly below P (not written in this step) are
+    // requested before the barrier, except by wavefront 0, which polls the barrier (the
+    // poll's loads would wait for its copies: loads complete in order). Handing wavefront
+    // 0's first blocks to wavefront 1, with a sync after the barrier, measured slower.
     {
-      const int npair = R * nkv, sp = a.sp;
-      const int it = w * nwx + m;
-      const bool has = it < npair * sp;
-      const int pair = has ? it / sp : 0, s = has ? it % sp : 0;
-      const int j = pair / nkv, h = pair % nkv;
-      const int b = g + 8 * j;
-      const int P = has ? pos[j] : -1;
-      const bool valid = P >= 0 && P < a.cap && P < a.max_pos;
-      const int k_lo = valid ? (window > 0 ? max(0, P - window + 1) : 0) : 0;
-      const int n = valid ? P + 1 - k_lo : 0;
-      const int k0 = k_lo + (int)((long)s * n / sp), k1 = k_lo + (int)((long)(s + 1) * n / sp);
+      const int sp = a.sp;
+      struct Item {
+        bool has;
+        int b, h, s, P, k0, k1;
+      };
+      auto item = [&](int wv) {
+        Item t;
+        const int it = wv * nwx + m;
+        t.has = it < R * nkv * sp;
+        const int pair = t.has ? it / sp : 0;
+        t.s = t.has ? it % sp : 0;
+        const int j = pair / nkv;
+        t.h = pair % nkv;
+        t.b = g + 8 * j;
+        t.P = t.has ? pos[j] : -1;
+        const bool valid = t.P >= 0 && t.P < a.cap && t.P < a.max_pos;
+        const int k_lo = valid ? (window > 0 ? max(0, t.P - window + 1) : 0) : 0;
+        const int n = valid ? t.P + 1 - k_lo : 0;
+        t.k0 = k_lo + (int)((long)t.s * n / sp);
+        t.k1 = k_lo + (int)((long)(t.s + 1) * n / sp);
+        return t;
+      };
+      // the first blocks of an item that can be requested before the barrier
+      auto early_blocks = [&](const Item &t) {
+        const int nb = t.k1 > t.k0 ? (t.k1 - t.k0 + DX_BLK - 1) / DX_BLK : 0;
+        int e = 0;
+        while (e < nb && e < DX_NSLOT && t.k0 + (e + 1) * DX_BLK <= t.P) ++e;
+        return e;
+      };
+      const Item me = item(w);
+      const bool has = me.has;
+      const int b = me.b, h = me.h, s = me.s, P = me.P, k0 = me.k0, k1 = me.k1;
       const int nblk = k1 > k0 ? (k1 - k0 + DX_BLK - 1) / DX_BLK : 0;
       const size_t kvbase = ((size_t)b * nkv + h) * a.cap * DX_D;
       const bf16 *kb_ = kc + kvbase, *vb_ = vc + kvbase;
       const uint32_t wring_off = (uint32_t)(w * DX_NSLOT * DX_SLOT);
       const uint32_t wring = lds_addr(smem) + wring_off;
       const int first = nblk < DX_NSLOT ? nblk : DX_NSLOT;
-      int issued = 0;
-      while (w != 0 && issued < first && k0 + (issued + 1) * DX_BLK <= P) {  // wave 0 polls the barrier
-        dx_kv_issue(kb_, vb_, wring, k0, issued, k1, lane);
-        ++issued;
-      }
+      const int early = early_blocks(me);
+      if (w != 0)
+        for (int e = 0; e < early; ++e) dx_kv_issue(kb_, vb_, wring, k0, e, k1, lane);
       if (!dx_wait(sy, &bad)) goto aborted;
+      int issued = w != 0 ? early : 0;
       if (has) {
         // q of the G heads into rows 0 .. G-1 of the wave's zero-padded tile, then the
         // remaining first blocks
@@ -685,8 +725,6 @@ __global__ void __launch_bounds__(DX_THREADS, 1) decode_xcd_kernel(const DecodeX
 #pragma unroll
           for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4 *>(pp + 2 + 16 * t + 4 * gq) = o[t];
         }
-      } else {
-        wait_vmcnt<0>();
       }
     }
     {
@@ -763,7 +801,8 @@ __global__ void __launch_bounds__(DX_THREADS, 1) decode_xcd_kernel(const DecodeX
 
     // ---- gate/up + SwiGLU
     wait_vmcnt<0>();  // the weight copies have landed (the barrier in the staging publishes them)
-    dx_stage_norm<DX_HMAX, DX_KPAD_H>(Ah, Al, xr, Ly.mn, H, a.eps, g, R);
+    dx_norm_prefetch(nw, Ly.mn, H, R);
+    dx_stage_norm<DX_KPAD_H>(Ah, Al, xr, nw, H, a.eps, g, R);
     dx_mma<2 * DX_UMAX, IM_H, 2, NFR, DX_WAVES, DX_KPAD_H, true>(fr, GW, nu_i, KS_H, Ah, Al, red, res);
     if (w < nu_i) {
       const int col = (m + w * nwx) * 16 + (lane & 15);
