@@ -161,7 +161,7 @@ def _kernel_time(B, kernel, run_once, torch, max_launches=4096):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_prefill_b4s512_gemms.md")
-TRAFFIC_DECODE_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b64.md")
+TRAFFIC_DECODE_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_step_b64.md")
 TRAFFIC_BACKWARD_PROFILE = os.path.join(ROOT, "profiles", "traffic_block_backward_b4s512.md")
 TRAFFIC_OTHER_PROFILE = os.path.join(ROOT, "profiles", "traffic_prefill_smollm3_b2s4096.md")
 
