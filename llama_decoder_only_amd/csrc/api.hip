@@ -27,6 +27,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "decode_xcd.h"
 #include "smol.h"
 
 namespace {

@@ -46,6 +46,7 @@
 // operand rows are set to NaN, so that the step's logits come out NaN.
 #include "common.h"
 #include "kernels.h"
+#include "decode_xcd.h"
 
 namespace smol {
 
