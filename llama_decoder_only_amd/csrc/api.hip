@@ -385,6 +385,7 @@ smol_status decode_impl(const Dims &D, const smol_model_weights *w, const int32_
       a.part = (float *)(ws + lay.dxpart); a.xs = (f16 *)(ws + lay.xs);
       a.ss_p = (float *)(ws + lay.ss_p); a.ss_q = (float *)(ws + lay.ss_q);
       a.ctrl = (uint32_t *)(ws + lay.dxctrl);
+      a.deadline = smol::decode_xcd_deadline_ticks();
       double f[64];
       fill_inv_freq(D, f);
       for (int i = 0; i < D.d / 2; ++i) a.inv_freq[i] = f[i];

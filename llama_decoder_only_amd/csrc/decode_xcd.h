@@ -33,9 +33,11 @@ struct DecodeXcdArgs {
   f16 *xs;                  // [B, H] head operand
   float *ss_p, *ss_q;       // [H / 64, B]
   uint32_t *ctrl;           // decode_xcd_ctrl_words(nwx), zeroed by decode_xcd before the step
+  unsigned long long deadline;  // barrier wait limit after the step starts, shader-clock ticks
   double inv_freq[32];
   DxLayer layer[DX_LMAX];
 };
+unsigned long long decode_xcd_deadline_ticks();
 int decode_xcd_groups_per_xcd();  // workgroups per XCD group on the current device (CUs / 8)
 bool decode_xcd_fits(int B, int H, int nq, int nkv, int d, int I, int L, int cap, int nwx);
 int decode_xcd_splits(int B, int nkv, int nwx);

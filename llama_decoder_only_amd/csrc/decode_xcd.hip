@@ -41,12 +41,16 @@
 // phase, so their memory latency overlaps the wait. The contraction of each tile is
 // split over the workgroup's eight wavefronts by K step and summed through LDS.
 //
-// Failure: a step whose barriers are still waiting ~1 s after it started (a workgroup that never became
-// resident) sets the abort word; every workgroup then leaves, and the group's head
-// operand rows are set to NaN, so that the step's logits come out NaN.
+// Failure: a step whose barriers are still waiting ~1 s after it started (a workgroup that
+// never became resident) sets the abort word; every workgroup then leaves, and the
+// group's head operand rows are set to NaN, so that the step's logits come out NaN. The
+// limit is a kernel argument (decode_xcd_deadline_ticks), which lets a test force the
+// path from the host.
 #include "common.h"
 #include "kernels.h"
 #include "decode_xcd.h"
+
+#include <cstdlib>
 
 namespace smol {
 
@@ -59,7 +63,6 @@ constexpr int DX_KPAD = DX_KMAX + 8;        // LDS row of the staged A operand o
 constexpr int DX_KPAD_H = DX_HMAX + 8;      // the same for the contractions over the hidden size
 constexpr int DX_TMAX = 2 * DX_UMAX;        // tiles per workgroup and phase
 constexpr int SC1 = 16;                     // buffer-op cache policy: agent-coherent
-constexpr unsigned long long DX_DEADLINE = 100000000ull;  // 1 s of the 100 MHz clock
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -527,7 +530,7 @@ __global__ void __launch_bounds__(DX_THREADS, 1) decode_xcd_kernel(const DecodeX
     rope[j][i] = j < R ? rope_cos_sin(pos[j], a.inv_freq[i]) : make_float2(1.f, 0.f);
   }
 
-  DxSync sy{a.ctrl + DX_CTRL_WORDS + g * nwx * 16, a.ctrl + DX_CTRL_ABORT, nwx, m, 0u, wall_clock64() + DX_DEADLINE};
+  DxSync sy{a.ctrl + DX_CTRL_WORDS + g * nwx * 16, a.ctrl + DX_CTRL_ABORT, nwx, m, 0u, wall_clock64() + a.deadline};
   const __amdgpu_buffer_rsrc_t xr = dx_rsrc(a.x, (uint32_t)((size_t)B * H * 4));
   const __amdgpu_buffer_rsrc_t qr = dx_rsrc(a.q, (uint32_t)((size_t)B * H * 2));
   const __amdgpu_buffer_rsrc_t orr = dx_rsrc(a.o, (uint32_t)((size_t)B * H * 2));
@@ -898,6 +901,17 @@ aborted:
 
 __global__ void dx_clear_kernel(uint32_t *ctrl, int words) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < words; i += gridDim.x * blockDim.x) ctrl[i] = 0u;
+}
+
+// Barrier deadline in ticks of the 100 MHz shader clock: 1 s, or SMOL_DECODE_DEADLINE_TICKS
+// (read at every call: a test sets a tiny value to drive the abort path).
+unsigned long long decode_xcd_deadline_ticks() {
+  const char *e = getenv("SMOL_DECODE_DEADLINE_TICKS");
+  if (e && *e) {
+    const unsigned long long v = strtoull(e, nullptr, 10);
+    if (v > 0) return v;
+  }
+  return 100000000ull;
 }
 
 int decode_xcd_groups_per_xcd() {
