@@ -15,10 +15,8 @@
 // (lane % 32) and half of that query's keys in registers: the row max / sum of
 // the online softmax needs only in-register reductions plus one exchange with
 // lane ^ 32. P then feeds O^T = V^T . P^T straight from those registers; the V^T
-// fragments come from transposing LDS reads (ds_read_b64_tr_b16). A bf16 cache is
-// converted to the fp16 operand type once per staged round, in LDS, when waves walk
-// many rounds; with a 4-way key split (short key ranges, one or two rounds) each wave
-// converts the fragments it reads instead, which spares the extra barrier per round.
+// fragments come from transposing LDS reads (ds_read_b64_tr_b16). K and V of a bf16
+// cache enter bf16 MFMAs as they were copied, with no conversion pass.
 // Keys come in tiles in increasing order, so without a key mask tile 0 (always
 // visible) fixes a finite running max before any fully masked tile can occur; with
 // one, a row may see no key yet (or ever): its max stays -inf, its probabilities 0,
@@ -55,6 +53,19 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const char *p) {
   return __builtin_bit_cast(u16x4, v);
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// A lane's LDS address for this round, opaque to the optimiser: the reads at fixed
+// offsets from it then use the instructions' immediate offsets, where left alone the
+// compiler hoisted every (lane offset + immediate) sum out of the loop into a register
+// of its own and added the round's base to each one (16 more VGPRs and 32 more VALU
+// instructions per round).
+__device__ __forceinline__ const lds_char *lds_base(const char *p) {
+  const lds_char *q = (const lds_char *)p;
+  asm volatile("" : "+v"(q));
+  return q;
+}
+
 
 // How far (log2 units) a tile's max may pass the running reference max before the
 // reference moves (p = exp2(s - m_ref) <= 2^8 meanwhile).
@@ -65,10 +76,20 @@ constexpr float ATTN_REF_SLACK = 8.0f;
 // skipped). A separate instantiation: the mask's byte loads inside the ring loop make
 // the compiler drain every outstanding load (it cannot see the ring's direct-to-LDS
 // copies), which the unmasked kernel must not pay.
+//
+// Operands: a bf16 cache feeds bf16 MFMAs straight from LDS (no conversion); q, stored
+// float16, is scaled by log2(e)/sqrt(d) once and rounded to bf16, and p is rounded to
+// bf16 for the P.V product, its row sum adding exactly the rounded values
+// (v_dot2_f32_bf16): the operand precision of a bf16 attention. A float cache keeps
+// float operands throughout.
+// bf16 cache: the running reference max m (kept bf16-exact) enters the score MFMAs as one
+// more K step, a column of ones in K against -m in q's place, so they return
+// s*log2(e)/sqrt(d) - m and p is one v_exp_f32. float cache: one FMA per score.
 template <typename W, int D, int G, int QW, int KS, int S, bool MASKED>
 __global__ void __launch_bounds__(64 * G * QW * KS)
 attn_prefill_kernel(const AttnArgs a) {
-  using T = Act<W>;  // operand type of q, p and o; cached k, v (type W) convert as they leave LDS
+  using QT = Act<W>;  // how q and o are stored (float16 for a bf16 model)
+  using T = W;        // MFMA operand type: bf16 or float, as the cache
   constexpr int NW = G * QW * KS, BQ = 32 * QW, BKV = 64;
   constexpr int ES = sizeof(W);
   constexpr int RB = D * ES;                       // bytes per key row
@@ -80,7 +101,6 @@ attn_prefill_kernel(const AttnArgs a) {
   constexpr int DS = D / 16;                       // MFMA K-steps over the head dim
   constexpr int DT = D / 32;                       // 32-row tiles of O^T
   constexpr int PSTATE = DT * 16 + 2;              // floats per lane of a partial state
-  constexpr bool LCONV = ES == 2 && KS < 4;        // convert each round in LDS on arrival
   static_assert(S >= 2, "ring depth");
   static_assert(KS == 1 || (KS - 1) * G * QW * PSTATE * 64 * 4 <= S * STAGE_BYTES, "partials fit the ring");
 
@@ -100,23 +120,23 @@ attn_prefill_kernel(const AttnArgs a) {
   const int qt = min(q0 + ql, a.T - 1);
   const bool wave_live = q0 < a.T;
   const int ldq = a.n_heads * D;
+  const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
 
+  // q fragments, scaled into the log2 domain (using the loads here also makes the
+  // compiler wait for them now: left to the key loop, its vmcnt waits, which count the
+  // ring's DMAs too, would stall every round on the copies just issued)
   Frag<T> qf[DS];
   {
-    const T *qp = (const T *)a.q + (size_t)(b * a.T + qt) * ldq + h * D + half * 8;
+    Frag<QT> raw[DS];
+    const QT *qp = (const QT *)a.q + (size_t)(b * a.T + qt) * ldq + h * D + half * 8;
 #pragma unroll
-    for (int st = 0; st < DS; ++st) load_frag(qf[st], qp + 16 * st);
-    // Use the fragments once here, before the ring starts: the compiler then waits for
-    // these loads now. Left to their first use inside the key loop, its vmcnt waits
-    // (which also count the ring's DMAs, invisible to it) would stall every round on
-    // the loads just issued for a later round.
-    typedef uint32_t QWords __attribute__((ext_vector_type(sizeof(qf[0].v) / 4)));
+    for (int st = 0; st < DS; ++st) load_frag(raw[st], qp + 16 * st);
 #pragma unroll
-    for (int st = 0; st < DS; ++st) {
-      const QWords u = __builtin_bit_cast(QWords, qf[st].v);
+    for (int st = 0; st < DS; ++st)
 #pragma unroll
-      for (int i = 0; i < (int)(sizeof(QWords) / 4); ++i) asm volatile("" ::"v"(u[i]));
-    }
+      for (int e = 0; e < 8; ++e) {
+        qf[st].v[e] = from_f32<T>((float)raw[st].v[e] * (ES == 2 ? c_log2 : 1.f));
+      }
   }
 
   const int last_q = min(a.T - 1, qb * BQ + BQ - 1);
@@ -154,35 +174,36 @@ attn_prefill_kernel(const AttnArgs a) {
   };
 
   // Per-lane LDS offsets of the K fragments (S^T = K Q^T) and of the V^T fragment
-  // sources for the transposed reads, fixed for the whole loop.
-  int koff[2][DS];
+  // sources for the transposed reads, fixed for the whole loop. att_slot depends on the
+  // row modulo 8 only, so rows 8 apart sit exactly 8 row lengths apart: one offset per K
+  // step (K) or per 32-dim tile (V) serves every row group, the rest is an immediate.
+  int koff[DS];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int st = 0; st < DS; ++st) koff[st] = swz<RB, ES>(ql, 16 * st + half * 8);
+  int voff[DT];
 #pragma unroll
-    for (int st = 0; st < DS; ++st) koff[i][st] = swz<RB, ES>(32 * i + ql, 16 * st + half * 8);
-  int voff[4][DT][2];
-#pragma unroll
-  for (int sg = 0; sg < 4; ++sg)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        if constexpr (ES == 2) {
-          // lane l supplies 4 dims starting at 16*((l/16)%2) + 4*(l%4) of key row
-          // 16 sg + 8 pp + 4*(l/32) + (l%16)/4; the transposed read then returns dim
-          // (l % 32) of the 4 keys 16 sg + 8 pp + 4 half + (0..3).
-          const int sl = lane & 15;
-          voff[sg][dt][pp] = swz<RB, ES>(16 * sg + 8 * pp + 4 * half + (sl >> 2), 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (sl & 3));
-        } else {
-          voff[sg][dt][pp] = 0;
-        }
-      }
+  for (int dt = 0; dt < DT; ++dt) {
+    // lane l supplies 4 dims starting at 16*((l/16)%2) + 4*(l%4) of key row
+    // 16 sg + 8 pp + 4*(l/32) + (l%16)/4; the transposed read then returns dim
+    // (l % 32) of the 4 keys 16 sg + 8 pp + 4 half + (0..3).
+    const int sl = lane & 15;
+    voff[dt] = ES == 2 ? swz<RB, ES>(4 * half + (sl >> 2), 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (sl & 3)) : 0;
+  }
 
-  const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
   f32x16 o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = (f32x16){};
+  // m_run: the reference max (log2 domain; -inf until the lane's query has seen a key).
+  // bf16: kx / qx, the extra K step of the scores: k index 0 (lanes of half 0, element 0)
+  // holds 1 in K and -m_run in q (0 while m_run is -inf), every other index 0.
   float m_run = -INFINITY, l_run = 0.f;
+  Frag<T> kx, qx;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kx.v[e] = from_f32<T>((e == 0 && half == 0) ? 1.f : 0.f);
+    qx.v[e] = from_f32<T>(0.f);
+  }
+  constexpr bool XSTEP = ES == 2;
 
   // first round that holds a key some query of the block may see (0 without a window)
   const int rf = (MASKED && a.window > 0) ? max(0, qb * BQ + a.q_key_off - a.window + 1) / (KS * BKV) : 0;
@@ -198,38 +219,30 @@ attn_prefill_kernel(const AttnArgs a) {
     else
       wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // round r landed for every wave; slot of round r-1 is free
-    if constexpr (LCONV) {
-      // bf16 cache: convert the round's K and V tiles to the operand type once, in
-      // place (same width, same swizzled layout), instead of in every wave that reads
-      // them. The barrier waits for the LDS writes only: the DMA of a later round may
-      // still be in flight.
-      Chunk16 *t = reinterpret_cast<Chunk16 *>(smem + (step % S) * STAGE_BYTES);
-      for (int i = tid; i < STAGE_BYTES / 16; i += NW * 64) t[i] = to_operand<W>(t[i]);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-    }
     if (step + S - 1 < nr) issue(r + S - 1, (step + S - 1) % S);
     const int kt = r * KS + ks;  // this wave's tile
     const char *ks_ptr = smem + (step % S) * STAGE_BYTES + ks * 2 * TILE_BYTES;
     const char *vs = ks_ptr + TILE_BYTES;
     const int k0 = kt * BKV;
     if (wave_live && kt < ntiles && k0 <= wave_kmax) {
-      // ---- S^T = K . Q^T (lane: one query, 32 of its keys in two 32-key tiles)
+      // ---- S^T = K . Q^T - m (lane: one query, 32 of its keys in two 32-key tiles)
       f32x16 s[2] = {(f32x16){}, (f32x16){}};
+      if constexpr (XSTEP) {
+        mma_32x32x16(s[0], kx, qx);
+        mma_32x32x16(s[1], kx, qx);
+      }
       // With four key groups (short sequences: 16 waves per workgroup) a wave raises its
-      // issue priority over its MFMA loops, so others' softmax fills the gaps (batch 4 x
-      // seq 512: 13.1 -> 12.7 us; the long configurations gained nothing or lost).
+      // issue priority over its MFMA loops, so others' softmax fills the gaps.
       if constexpr (KS == 4) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
+        const lds_char *kp = lds_base(ks_ptr + koff[st]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int row = 32 * i + ql;
           Frag<T> kf;
           if constexpr (ES == 2) {
-            Chunk16 c = *reinterpret_cast<const Chunk16 *>(ks_ptr + koff[i][st]);
-            if constexpr (!LCONV) c = to_operand<W>(c);
-            kf.v = __builtin_bit_cast(decltype(kf.v), c);
+            kf.v = __builtin_bit_cast(decltype(kf.v), *(const __attribute__((address_space(3))) Chunk16 *)(kp + 32 * i * RB));
           } else {
             const Chunk16 lo = *reinterpret_cast<const Chunk16 *>(ks_ptr + swz<RB, ES>(row, 16 * st + half * 8));
             const Chunk16 hi = *reinterpret_cast<const Chunk16 *>(ks_ptr + swz<RB, ES>(row, 16 * st + half * 8 + 4));
@@ -240,11 +253,8 @@ attn_prefill_kernel(const AttnArgs a) {
         }
       }
       if constexpr (KS == 4) __builtin_amdgcn_s_setprio(0);
-      // ---- online softmax. Scores stay unscaled; the running reference max m_run lives
-      // in the scaled (log2) domain, so p = exp2(s * c - m) is one FMA and one v_exp_f32
-      // (its argument is <= 8, where the plain hardware exp2 needs no range fix-up). A key
-      // split may meet tiles where some of its queries see no key yet: their max stays
-      // -inf and their probabilities 0.
+      // ---- online softmax. A key split may meet tiles where some of its queries see no
+      // key yet: their max stays -inf and their probabilities 0.
       const bool need_mask = k0 + BKV - 1 > q0 + a.q_key_off;
       if constexpr (MASKED) {
         unsigned long long kb = ~0ull;  // bit j: key k0 + j may be attended (lane j loads its byte)
@@ -263,7 +273,7 @@ attn_prefill_kernel(const AttnArgs a) {
       }
       // The causal cut, on the tiles that cross the diagonal only (a branch on a wave-
       // uniform condition: left as a select inside the max loop, the compiler evaluated
-      // the 32 compares on every tile, about a sixth of the loop's vector ALU work).
+      // the 32 compares on every tile).
       if (__builtin_expect(need_mask, 0)) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -271,54 +281,69 @@ attn_prefill_kernel(const AttnArgs a) {
           for (int rr = 0; rr < 16; ++rr)
             if (k0 + 32 * i + acc_row(rr, lane) > my_kmax) s[i][rr] = -INFINITY;
       }
-      float mx = -INFINITY;
+      if constexpr (!XSTEP) {
+        const float mb = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) s[i][rr] = fmaf(s[i][rr], c_log2, -mb);
+      }
+      float mx = -INFINITY;  // the tile's max of s * c - m (s * c while m_run is -inf)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[i][rr]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // The reference max m_run moves only when a tile's max exceeds it by more than
-      // 2^8 (softmax is unchanged by the reference; p <= 256 stays far inside float16),
-      // so the O and l rescale runs on few tiles: the first, and the rare later jumps.
-      const float m_cand = mx * c_log2;
-      const bool grow = m_cand > m_run + ATTN_REF_SLACK;  // m_run = -inf: any visible key
+      // The reference moves only when a tile's max passes it by more than 2^8 (softmax is
+      // unchanged by the reference; p <= 256 stays far inside bf16's and float's range), so
+      // the rescale of O, l and the tile's scores runs on few tiles: the first, and the
+      // rare later jumps.
+      const bool grow = mx > (m_run == -INFINITY ? -INFINITY : ATTN_REF_SLACK);
       if (__any(grow)) {
-        const float m_new = grow ? m_cand : m_run;
+        const float mb = m_run == -INFINITY ? 0.f : m_run;
+        // the new reference: the tile's max, rounded to bf16 where it enters an MFMA
+        const float m_new = grow ? (XSTEP ? (float)from_f32<T>(mb + mx) : mb + mx) : m_run;
+        const float sh = grow ? m_new - mb : 0.f;  // the scores' reference moves up by sh
         const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) s[i] -= sh;
         m_run = m_new;
+        if constexpr (XSTEP) qx.v[0] = from_f32<T>(half == 0 && m_run != -INFINITY ? -m_run : 0.f);
       }
-      const float m_use = ((KS > 1 || MASKED) && m_run == -INFINITY) ? 0.f : m_run;  // no key seen yet: p = 0
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) s[i][rr] = __builtin_amdgcn_exp2f(fmaf(s[i][rr], c_log2, -m_use));
+        for (int rr = 0; rr < 16; ++rr) s[i][rr] = __builtin_amdgcn_exp2f(s[i][rr]);
       // ---- O^T += V^T . P^T. Element e of a lane's 8 values in key step sg is key
       // 16 sg + 8 (e / 4) + 4 half + e % 4, for P (from the score registers) and V alike.
-      // With a 16-bit operand type the row sum l adds the rounded p the MFMAs take, two
-      // at a time (v_dot2_f32_f16 against (1, 1), float accumulation).
+      // With bf16 operands the row sum l adds the rounded p the MFMAs take, two at a time
+      // (v_dot2_f32_bf16 against (1, 1), float accumulation).
       float ls = 0.f;
       if constexpr (KS == 4) __builtin_amdgcn_s_setprio(1);
+      const lds_char *vp[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vp[dt] = lds_base(vs + voff[dt]);
 #pragma unroll
       for (int sg = 0; sg < 4; ++sg) {
         Frag<T> pf;
-        if constexpr (sizeof(T) == 2) {
-          typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        if constexpr (ES == 2) {
+          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
           typedef float f2 __attribute__((ext_vector_type(2)));
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             const float p0 = s[sg >> 1][8 * (sg & 1) + e], p1 = s[sg >> 1][8 * (sg & 1) + e + 1];
-            const h2 pk = __builtin_convertvector((f2){p0, p1}, h2);
+            const b2 pk = __builtin_convertvector((f2){p0, p1}, b2);
             pf.v[e] = pk[0];
             pf.v[e + 1] = pk[1];
-            ls = __builtin_amdgcn_fdot2(pk, (h2){(_Float16)1.0f, (_Float16)1.0f}, ls, false);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pk, (b2){(__bf16)1.0f, (__bf16)1.0f}, ls, false);
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pf.v[e] = from_f32<T>(s[sg >> 1][8 * (sg & 1) + e]);
+            pf.v[e] = s[sg >> 1][8 * (sg & 1) + e];
             ls += s[sg >> 1][8 * (sg & 1) + e];
           }
         }
@@ -330,10 +355,10 @@ attn_prefill_kernel(const AttnArgs a) {
             u32x4v raw;
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-              const u16x4 t = lds_read_tr16(vs + voff[sg][dt][pp]);
-              const uint32_t lo = (uint32_t)t[0] | ((uint32_t)t[1] << 16), hi = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
-              raw[2 * pp] = LCONV ? lo : bf16x2_to_f16x2(lo);
-              raw[2 * pp + 1] = LCONV ? hi : bf16x2_to_f16x2(hi);
+              const u16x4 t = __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                  (__attribute__((address_space(3))) half4 *)(vp[dt] + (16 * sg + 8 * pp) * RB)));
+              raw[2 * pp] = (uint32_t)t[0] | ((uint32_t)t[1] << 16);
+              raw[2 * pp + 1] = (uint32_t)t[2] | ((uint32_t)t[3] << 16);
             }
             vf.v = __builtin_bit_cast(decltype(vf.v), raw);
           } else {
@@ -394,11 +419,11 @@ attn_prefill_kernel(const AttnArgs a) {
   if (!wave_live || q0 + ql >= a.T) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
-  T *op = (T *)a.o + (size_t)(b * a.T + q0 + ql) * ldq + h * D;
+  QT *op = (QT *)a.o + (size_t)(b * a.T + q0 + ql) * ldq + h * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) op[32 * dt + acc_row(rr, lane)] = from_f32<T>(o[dt][rr] * inv);
+    for (int rr = 0; rr < 16; ++rr) op[32 * dt + acc_row(rr, lane)] = from_f32<QT>(o[dt][rr] * inv);
 }
 
 template <typename T, int D, int G, int QW, int KS>
