@@ -107,7 +107,7 @@ attn_prefill_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[S * STAGE_BYTES];
   const uint32_t smem_base = lds_addr(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, ql = lane & 31;
   const int hq = w % (G * QW), ks = w / (G * QW);  // (head, query sub-block) and key split
   const int nqb = (a.T + BQ - 1) / BQ;
@@ -151,25 +151,44 @@ attn_prefill_kernel(const AttnArgs a) {
 
   // DMA: instruction q of a round fills LDS bytes [q*1024, q*1024 + 1024) of the stage:
   // chunk index q*64 + lane -> (tile of the round, K or V, key row, slot); the slot
-  // receives the row's chunk slot ^ att_slot(row). Only the key moves from round to round.
-  const W *dma_base[IPW];
-  int dma_row[IPW];
+  // receives the row's chunk slot ^ att_slot(row). An instruction's 64 lanes stay inside
+  // one tile of K or of V (a tile is 64 * CPR chunks), so its source is a wave-uniform
+  // base, which moves with the round, plus a fixed 32-bit byte offset per lane: the
+  // copies of a full round take the global_load_lds form with an SGPR base. Only a round
+  // that reaches past the last key (the final one) clamps each lane's key instead.
+  static_assert((BKV * CPR) % 64 == 0, "an instruction covers one tile");
+  const W *dma_tile[IPW];    // K or V base of the instruction's tile within a round (uniform)
+  int dma_t0[IPW];           // that tile's first key within the round (uniform)
+  uint32_t dma_lane[IPW];    // the lane's byte offset from the tile's first key row
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int q = min(w * IPW + j, NINS - 1);
+    const int part = q * 64 / (BKV * CPR);  // 2 * tile_in_round + (0 = K, 1 = V)
     const int cidx = q * 64 + lane;
-    const int part = cidx / (BKV * CPR);  // 2 * tile_in_round + (0 = K, 1 = V)
     const int row = (cidx % (BKV * CPR)) / CPR;
     const int c = (cidx % CPR) ^ att_slot(row);
-    dma_base[j] = ((part & 1) == 0 ? kbase_ptr : vbase_ptr) + c * (16 / ES);
-    dma_row[j] = (part >> 1) * BKV + row;  // key offset within the round
+    dma_tile[j] = ((part & 1) == 0 ? kbase_ptr : vbase_ptr) + (size_t)(part >> 1) * BKV * D;
+    dma_t0[j] = (part >> 1) * BKV;
+    dma_lane[j] = (uint32_t)(row * RB + c * 16);
   }
   auto issue = [&](int r, int slot) {
+    const int key0 = r * KS * BKV;
+    if (key0 + KS * BKV <= nkeys) {
 #pragma unroll
-    for (int j = 0; j < IPW; ++j) {
-      const int q = min(w * IPW + j, NINS - 1);
-      const int key = min(r * KS * BKV + dma_row[j], nkeys - 1);
-      lds_dma16(dma_base[j] + (size_t)key * D, smem_base + slot * STAGE_BYTES + q * 1024);
+      for (int j = 0; j < IPW; ++j) {
+        const int q = min(w * IPW + j, NINS - 1);
+        const W *base = dma_tile[j] + (size_t)key0 * D;
+        asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(dma_lane[j]), "s"(base),
+                     "{m0}"(smem_base + slot * STAGE_BYTES + q * 1024) : "memory");
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const int q = min(w * IPW + j, NINS - 1);
+        const int key = min(key0 + dma_t0[j] + (int)(dma_lane[j] / RB), nkeys - 1);
+        lds_dma16((const char *)dma_tile[j] + (size_t)(key - dma_t0[j]) * RB + dma_lane[j] % RB,
+                  smem_base + slot * STAGE_BYTES + q * 1024);
+      }
     }
   };
 
