@@ -55,6 +55,13 @@ __device__ __forceinline__ u16x4 lds_read_tr16(const char *p) {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
+// Max of x over lanes l and l ^ 32 (gfx950 v_permlane32_swap: one VALU exchange of the
+// two halves instead of an LDS permute and its address arithmetic).
+__device__ __forceinline__ float max_lane32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // A lane's LDS address for this round, opaque to the optimiser: the reads at fixed
 // offsets from it then use the instructions' immediate offsets, where left alone the
 // compiler hoisted every (lane offset + immediate) sum out of the loop into a register
@@ -240,7 +247,9 @@ attn_prefill_kernel(const AttnArgs a) {
     __builtin_amdgcn_s_barrier();  // round r landed for every wave; slot of round r-1 is free
     if (step + S - 1 < nr) issue(r + S - 1, (step + S - 1) % S);
     const int kt = r * KS + ks;  // this wave's tile
-    const char *ks_ptr = smem + (step % S) * STAGE_BYTES + ks * 2 * TILE_BYTES;
+    // this wave's K tile of the round in LDS (a scalar: the per-lane offsets add to it)
+    const int kt_off = __builtin_amdgcn_readfirstlane((step % S) * STAGE_BYTES + ks * 2 * TILE_BYTES);
+    const char *ks_ptr = smem + kt_off;
     const char *vs = ks_ptr + TILE_BYTES;
     const int k0 = kt * BKV;
     if (wave_live && kt < ntiles && k0 <= wave_kmax) {
@@ -312,7 +321,7 @@ attn_prefill_kernel(const AttnArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[i][rr]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_lane32(mx);
       // The reference moves only when a tile's max passes it by more than 2^8 (softmax is
       // unchanged by the reference; p <= 256 stays far inside bf16's and float's range), so
       // the rescale of O, l and the tile's scores runs on few tiles: the first, and the
