@@ -252,14 +252,21 @@ def prefill_rooflines(kern, flops):
     return out
 
 
+def _note(msg):
+    """A progress line on stderr (stdout carries the one JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def other_prefills(B, torch, dev, md):
     """The long-context prefill (the same model as the headline, md) and the SmolLM3-3B
     shape (weights drawn on the GPU)."""
     from llama_decoder_only_amd import synthetic as S
 
     out = {"long_prefill": other_prefill(B, torch, dev, "long_prefill_bf16", md, reps=10, warmup=2)}
+    _note("long prefill done")
     m5 = random_model(B, torch, dev, S.workload("smollm3_prefill_bf16"))
     out["smollm3_prefill"] = other_prefill(B, torch, dev, "smollm3_prefill_bf16", m5, reps=5, warmup=1)
+    _note("SmolLM3-shaped prefill done")
     out["smollm3_prefill"]["data"] = "weights N(0, 0.02^2) drawn on the GPU (torch generator), norm weights 1"
     del m5
     torch.cuda.empty_cache()
@@ -625,6 +632,7 @@ def main():
         "rooflines": rooflines,
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kern.items()},
     }
+    _note("headline prefill done")
 
     if not args.no_other:
         out.update(other_prefills(B, torch, dev, md))
@@ -743,14 +751,17 @@ def main():
             "sample_us": samp,
         }
         del kc, vc
+        _note("decode done")
 
     if not args.no_backward:
         out["backward"] = backward_section(B, S, torch, dev, stream, args)
+        _note("backward done")
 
     if not args.no_decode:
         out["ceilings"] = ceilings(torch, dev)
 
     if not args.no_cpu:
+        _note("CPU oracle baseline (about 10-30 s)")
         out["cpu_baseline"] = cpu_baseline(s, model, ids_np)
 
     print(json.dumps(out), flush=True)
