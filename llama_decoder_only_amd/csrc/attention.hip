@@ -89,9 +89,10 @@ constexpr float ATTN_REF_SLACK = 8.0f;
 // bf16 for the P.V product, its row sum adding exactly the rounded values
 // (v_dot2_f32_bf16): the operand precision of a bf16 attention. A float cache keeps
 // float operands throughout.
-// bf16 cache: the running reference max m (kept bf16-exact) enters the score MFMAs as one
-// more K step, a column of ones in K against -m in q's place, so they return
-// s*log2(e)/sqrt(d) - m and p is one v_exp_f32. float cache: one FMA per score.
+// bf16 cache: the running reference max m enters the score MFMAs as one more K step,
+// ones in K against -m split into three bf16 parts (hi + mid + lo: exact for a float)
+// in q's place, so they return s*log2(e)/sqrt(d) - m and p is one v_exp_f32. float
+// cache: one FMA per score.
 template <typename W, int D, int G, int QW, int KS, int S, bool MASKED>
 __global__ void __launch_bounds__(64 * G * QW * KS)
 attn_prefill_kernel(const AttnArgs a) {
@@ -220,13 +221,14 @@ attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) o[i] = (f32x16){};
   // m_run: the reference max (log2 domain; -inf until the lane's query has seen a key).
-  // bf16: kx / qx, the extra K step of the scores: k index 0 (lanes of half 0, element 0)
-  // holds 1 in K and -m_run in q (0 while m_run is -inf), every other index 0.
+  // bf16: kx / qx, the extra K step of the scores: k indices 0-2 (lanes of half 0,
+  // elements 0-2) hold 1 in K and the three bf16 parts of -m_run in q (0 while m_run is
+  // -inf), every other index 0.
   float m_run = -INFINITY, l_run = 0.f;
   Frag<T> kx, qx;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    kx.v[e] = from_f32<T>((e == 0 && half == 0) ? 1.f : 0.f);
+    kx.v[e] = from_f32<T>((e < 3 && half == 0) ? 1.f : 0.f);
     qx.v[e] = from_f32<T>(0.f);
   }
   constexpr bool XSTEP = ES == 2;
@@ -329,8 +331,7 @@ attn_prefill_kernel(const AttnArgs a) {
       const bool grow = mx > (m_run == -INFINITY ? -INFINITY : ATTN_REF_SLACK);
       if (__any(grow)) {
         const float mb = m_run == -INFINITY ? 0.f : m_run;
-        // the new reference: the tile's max, rounded to bf16 where it enters an MFMA
-        const float m_new = grow ? (XSTEP ? (float)from_f32<T>(mb + mx) : mb + mx) : m_run;
+        const float m_new = grow ? mb + mx : m_run;  // the new reference: the tile's max
         const float sh = grow ? m_new - mb : 0.f;  // the scores' reference moves up by sh
         const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
@@ -339,7 +340,18 @@ attn_prefill_kernel(const AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) s[i] -= sh;
         m_run = m_new;
-        if constexpr (XSTEP) qx.v[0] = from_f32<T>(half == 0 && m_run != -INFINITY ? -m_run : 0.f);
+        if constexpr (XSTEP) {
+          // -m_run as hi + mid + lo, each the bf16 rounding of what the parts before
+          // leave: 3 x 8 significant bits hold the float exactly, and the MFMA's float
+          // sum of the three is exact too
+          const float nm = (half == 0 && m_run != -INFINITY) ? -m_run : 0.f;
+          const T hi = from_f32<T>(nm);
+          const float r1 = nm - (float)hi;
+          const T mid = from_f32<T>(r1);
+          qx.v[0] = hi;
+          qx.v[1] = mid;
+          qx.v[2] = from_f32<T>(r1 - (float)mid);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)

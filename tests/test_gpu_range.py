@@ -102,3 +102,26 @@ def test_prefill_bf16_norm_jump_and_large_embedding_rows():
     r_other = rel(got[..., other], want[..., other])
     say(f"rel: large-row columns {r_big:.3e}, other columns {r_other:.3e}")
     assert r_big <= TOL_BF16 and r_other <= TOL_BF16
+
+
+def test_block_bf16_huge_attention_scores_stay_finite():
+    """W_q and W_k scaled 1024 times: q and k stay inside float16 / bf16, but the scores
+    reach ~10^5 in log2 units, where a bf16 rounding of the softmax's running reference
+    max could miss the true max by ~10^3 and overflow exp2. The reference enters the
+    score MFMAs as an exact three-part bf16 split, so every output stays finite; the
+    float64 oracle's answer is reported (near-tied keys may pick differently under bf16
+    q at this scale, so it is not held to the bar)."""
+    s = S.workload("prefill_bf16", n_layers=1, batch=1, seq=192)
+    say("block bf16 B=1 T=192 with W_q, W_k x 1024")
+    layer = S.layer_weights(s, 0, 0)
+    layer.wq = S.stored(layer.wq.f64 * 1024.0, s.dtype)
+    layer.wk = S.stored(layer.wk.f64 * 1024.0, s.dtype)
+    x = S.stored(S.hidden_states(s, 0).f64, "f32").f64
+    xd = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(DEV)
+    out = torch.empty_like(xd)
+    B.smol_block_forward(B.Config.from_shape(s), B.upload_layer(layer), xd, out)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    assert np.isfinite(got).all()
+    want = O.block_forward(x, olayer(layer), ocfg(s))
+    say(f"finite; rel against the oracle {rel(got, want):.3e} (reported only)")
