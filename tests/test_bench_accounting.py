@@ -63,3 +63,17 @@ def test_more_than_one_gpu_is_refused(n):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", n], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_dominant_class_breaks_near_ties_conservatively():
+    """Within 5% of the largest summed time the class furthest below its roofline is
+    reported; a clear leader is reported whatever its fraction."""
+    import bench
+
+    flops = {"per_launch": {"gate_up": 7.2e9, "down": 3.6e9, "attention": 1.2e9}}
+    kern = {"gate_up": {"total_ms": 0.560, "launches": 30, "avg_us": 18.7},
+            "down": {"total_ms": 0.549, "launches": 30, "avg_us": 18.3},
+            "attention": {"total_ms": 0.340, "launches": 30, "avg_us": 11.3}}
+    assert bench.dominant_class(kern, flops) == "down"
+    kern["down"]["total_ms"] = 0.40
+    assert bench.dominant_class(kern, flops) == "gate_up"
